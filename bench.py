@@ -1,0 +1,335 @@
+"""Benchmark of the DDTree tree-verify step on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input:
+  plan -> 16 x [3 x (tree conv + tree gated delta-net), tree attention]
+       -> verify argmax + greedy walk -> commit of the accepted path (replay)
+on the hybrid stack of 48 gated delta-net layers and 16 attention layers at
+131,072 committed tokens and a 22-node draft tree (the pages' budget 22:
+lucebox-hub README, "02 · DFlash DDtree", "Implemented here"; 128K context:
+same section, first list).
+
+    python bench.py [--steps K] [--warmup W] [--no-graph] [--no-cpu-baseline]
+
+Prints ONE JSON line.  ``value`` is verify steps per second with every input
+already resident in HBM; the step is captured once in a HIP graph and
+replayed.  ``roofline`` is for the dominant kernel (tree attention: context
+split kernel + split combine, timed per call with HIP events on the launch
+stream); ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the
+same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "tree-verify steps/sec (budget 22) + achieved HBM GB/s vs peak, 1 GPU"
+
+
+def _dev(a, device):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+class Stack:
+    """Device-resident inputs, outputs and descriptors of one verify step."""
+
+    def __init__(self, device, seed=0, cfg=None, headroom_steps=256):
+        import torch
+        import tree_verification_ddtree_amd as ddt
+        self.ddt = ddt
+        c = dict(synth.STACK if cfg is None else cfg)
+        self.c = c
+        self.device = device
+        N, T = c["N"], c["T"]
+        self.parent = synth.random_tree(synth.rng_for(seed, 3, 18), N, c["levels"])
+        self.tb = ddt.TreeBatch(self.parent, [0, N], c["W"], device)
+        self.T0 = T
+        # room for the accepted tokens of every step the benchmark runs
+        self.T_max = T + headroom_steps * N
+        npages = (self.T_max + N + 15) // 16
+        g = torch.Generator(device=device)
+        n_gdn, n_attn = c["n_gdn"], c["n_attn"]
+        self.gdn, self.conv, self.gdn_out, self.conv_out = [], [], [], []
+        for l in range(n_gdn):
+            gi = synth.gdn_inputs(seed, (3, l), N, c["Hk"], c["Hv"], c["dk"], c["dv"], "bf16")
+            self.gdn.append({k: _dev(v, device) for k, v in gi.items()})
+            ci = synth.conv_inputs(seed, (3, 1000 + l), N, c["C"], c["W"], "bf16")
+            self.conv.append({k: _dev(v, device) for k, v in ci.items()})
+            self.gdn_out.append(torch.empty(N, c["Hv"], c["dv"], dtype=torch.float32, device=device))
+            self.conv_out.append(torch.empty(N, c["C"], dtype=torch.float32, device=device))
+        self.attn, self.kv, self.attn_out = [], [], []
+        for l in range(n_attn):
+            ai = synth.attn_inputs(seed, (3, 2000 + l), N, c["Hq"], c["Hkv"], c["D"], "f16")
+            self.attn.append({k: _dev(v, device) for k, v in ai.items()})
+            g.manual_seed(int(seed) * 1000003 + 3 * 10007 + l)
+            K = torch.randn((npages, c["Hkv"], 16, c["D"]), generator=g, device=device,
+                            dtype=torch.float16)
+            V = torch.randn((npages, c["Hkv"], c["D"], 16), generator=g, device=device,
+                            dtype=torch.float16)
+            self.kv.append((K, V))
+            self.attn_out.append(torch.empty(N, c["Hq"], c["D"], dtype=torch.float32, device=device))
+        self.T = torch.tensor([T], dtype=torch.int32, device=device)
+        self.attn_ws = torch.empty(
+            ddt.ddt_tree_attn_workspace(self.tb, c["Hq"], c["Hkv"], c["D"], self.T_max),
+            dtype=torch.uint8, device=device)
+        V = synth.VOCAB
+        lg, tok = synth.logits_and_draft(seed, (3, 3000), self.parent, V, "bf16", p_match=0.8)
+        self.logits, self.tok = _dev(lg, device), _dev(tok, device)
+        self.walk_ws = torch.empty(ddt.ddt_accept_walk_workspace(self.tb, V), dtype=torch.uint8,
+                                   device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.amax = torch.empty(N, **i32)
+        self.path = torch.empty(1, self.tb.n_max, **i32)
+        self.L = torch.empty(1, **i32)
+        self.bonus = torch.empty(1, **i32)
+        gl = [ddt.GdnLayer(a["q"].data_ptr(), a["k"].data_ptr(), a["v"].data_ptr(),
+                           a["alpha"].data_ptr(), a["beta"].data_ptr(), a["S_c"].data_ptr(), None,
+                           x["x"].data_ptr(), x["prefix"].data_ptr())
+              for a, x in zip(self.gdn, self.conv)]
+        al = [ddt.AttnLayer(a["Kt"].data_ptr(), a["Vt"].data_ptr(), K.data_ptr(), Vv.data_ptr())
+              for a, (K, Vv) in zip(self.attn, self.kv)]
+        self.gdn_table, self.attn_table = ddt.layer_table(gl, device), ddt.layer_table(al, device)
+        self.attn_events = None
+
+    def step(self, stream=None):
+        ddt, c = self.ddt, self.c
+        ddt.ddt_tree_plan(self.tb, c["levels"], stream)
+        gi = 0
+        for a in range(c["n_attn"]):
+            for _ in range(c["n_gdn"] // c["n_attn"]):
+                x, g = self.conv[gi], self.gdn[gi]
+                ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0, self.conv_out[gi], stream)
+                ddt.ddt_tree_gdn(self.tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"],
+                                 1.0, self.gdn_out[gi], None, stream)
+                gi += 1
+            at, (K, V) = self.attn[a], self.kv[a]
+            ev = self.attn_events
+            if ev is not None:
+                ev[a][0].record()
+            ddt.ddt_tree_attn(self.tb, at["q"], K, V, None, self.T, self.T_max, at["Kt"], at["Vt"],
+                              self.attn_out[a], self.attn_ws, stream=stream)
+            if ev is not None:
+                ev[a][1].record()
+        ddt.ddt_accept_walk(self.tb, self.logits, self.tok, self.amax, self.path, self.L,
+                            self.bonus, self.walk_ws, stream)
+        ddt.ddt_commit_state(self.tb, self.path, self.L, ddt.DDT_COMMIT_REPLAY, self.gdn_table,
+                             c["n_gdn"], c["Hk"], c["Hv"], c["dk"], c["dv"], ddt.DDT_BF16, c["C"],
+                             ddt.DDT_BF16, self.attn_table, c["n_attn"], c["Hkv"], c["D"],
+                             ddt.DDT_F16, None, self.T, stream)
+
+    # ---------------------------------------------------------------- bytes
+    def attn_bytes(self, T):
+        c = self.c
+        N = c["N"]
+        kv = T * c["Hkv"] * c["D"] * 2 * 2
+        return kv + N * c["Hq"] * c["D"] * 2 + N * c["Hkv"] * c["D"] * 2 * 2 + N * c["Hq"] * c["D"] * 4
+
+    def step_bytes(self, T, L):
+        """Algorithmic HBM bytes of one step: every input read once, every
+        output written once, plus the commit's state / prefix / K-V writes."""
+        c = self.c
+        N = c["N"]
+        gdn = (c["Hv"] * c["dv"] * c["dk"] * 4 * 2 + N * c["Hk"] * c["dk"] * 2 * 2
+               + N * c["Hv"] * c["dv"] * 2 + N * c["Hv"] * 2 * 2 + N * c["Hv"] * c["dv"] * 4)
+        W1 = c["W"] - 1
+        conv = (N * c["C"] * 2 + W1 * c["C"] * 2 * 2 + c["C"] * c["W"] * 2 + N * c["C"] * 4)
+        logits = N * synth.VOCAB * 2 + N * 4
+        append = L * c["Hkv"] * c["D"] * 2 * 2 * c["n_attn"]
+        return (c["n_attn"] * self.attn_bytes(T) + c["n_gdn"] * (gdn + conv) + logits + append)
+
+
+def _traffic(kernel_src_sha):
+    """HBM traffic of the attention call from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "tree_attn_t128k_n22_traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != kernel_src_sha:
+        return None
+    return d.get("bytes_per_call")
+
+
+def cpu_baseline(st, seed, budget_s=30.0):
+    """The CPU oracle on a bounded sample of the same step, scaled to a
+    whole step: one gated delta-net + conv layer (of 48), one KV head of one
+    attention layer (of 16 x 4), and the full verify walk."""
+    import torch
+    import oracle
+    c = st.c
+    N = c["N"]
+    nthreads = len(os.sched_getaffinity(0))
+    torch.set_num_threads(nthreads)
+    par = st.parent
+    host = lambda t: t.detach().cpu()
+    # sample inputs (copied from the device; generation is not timed)
+    g0 = {k: (host(v).view(torch.int16).numpy().view(np.uint16) if v.dtype == torch.bfloat16
+              else host(v).numpy()) for k, v in st.gdn[0].items()}
+    x0 = {k: host(v).view(torch.int16).numpy().view(np.uint16) for k, v in st.conv[0].items()}
+    K, V = st.kv[0]
+    a0 = {k: host(v).numpy() for k, v in st.attn[0].items()}
+    T = st.T0
+    npg = (T + 15) // 16
+    Kh = host(K[:npg, :1]).numpy()
+    Vh = host(V[:npg, :1]).numpy()
+    lg = host(st.logits).view(torch.int16).numpy().view(np.uint16)
+    tok = host(st.tok).numpy()
+    q1, kt1, vt1 = a0["q"][:, :c["Hq"] // c["Hkv"]], a0["Kt"][:, :1], a0["Vt"][:, :1]
+    t0 = time.perf_counter()
+    oracle.tree_conv(par, x0["x"], x0["prefix"], x0["w"])
+    oracle.tree_gdn(par, g0["q"], g0["k"], g0["v"], g0["alpha"], g0["beta"], g0["S_c"])
+    t1 = time.perf_counter()
+    oracle.tree_attn(par, q1, Kh, Vh, [T], kt1, vt1)
+    t2 = time.perf_counter()
+    am = oracle.argmax_rows(lg)
+    paths, L, bonus = oracle.accept_walk(par, tok, am)
+    t3 = time.perf_counter()
+    step_s = c["n_gdn"] * (t1 - t0) + c["n_attn"] * c["Hkv"] * (t2 - t1) + (t3 - t2)
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": nthreads, "kind": "oracle",
+            "sample": (f"numpy fp64 oracle: 1 of {c['n_gdn']} gated delta-net+conv layers, 1 KV "
+                       f"head (6 q-heads x {N} nodes) of 1 of {c['n_attn']} attention layers at "
+                       f"T={T}, full argmax+walk over {N}x{synth.VOCAB}; scaled to one step "
+                       f"(x{c['n_gdn']} and x{c['n_attn'] * c['Hkv']}); sample took "
+                       f"{t3 - t0:.1f} s"),
+            "seconds_per_step": step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=5, help="eager steps timed per attention call")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the verify step of one batch runs on a single MI355X; "
+              "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tree_verification_ddtree_amd as ddt
+    ddt.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] building the 128K stack (seed {args.seed})", file=sys.stderr, flush=True)
+    st = Stack(dev, seed=args.seed, headroom_steps=args.warmup + args.steps + args.kernel_reps + 8)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    status = st.tb.status.cpu().numpy()
+    if status.any():
+        raise RuntimeError(f"device status {status}")
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                st.step()
+            torch.cuda.synchronize()
+        except Exception as e:  # noqa: BLE001 - report and time eagerly instead
+            print(f"[bench] graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph, use_graph = None, False
+    T_start = int(st.T.item())
+    print(f"[bench] timing {args.steps} steps (graph={use_graph})", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            st.step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    T_end = int(st.T.item())
+    L_mean = (T_end - T_start) / args.steps
+    status = st.tb.status.cpu().numpy()
+    if status.any():
+        raise RuntimeError(f"device status {status}")
+
+    # dominant kernel: time every attention call of a few eager steps with
+    # HIP events on the launch stream
+    st.attn_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(st.c["n_attn"])]
+    durs = []
+    for _ in range(args.kernel_reps):
+        st.step()
+        torch.cuda.synchronize()
+        durs += [a.elapsed_time(b) for a, b in st.attn_events]
+    st.attn_events = None
+    attn_ms = float(np.mean(durs))
+    T_mid = (T_start + T_end) / 2
+    attn_bytes = st.attn_bytes(T_mid)
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    src = open(os.path.join(ROOT, "tree_verification_ddtree_amd", "csrc", "attn.hip"), "rb").read()
+    traffic = _traffic(hashlib.sha256(src).hexdigest())
+    step_bytes = st.step_bytes(T_mid, L_mean)
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": synth.STACK["name"],
+            "budget": st.c["N"], "context": st.T0, "gdn_layers": st.c["n_gdn"],
+            "attn_layers": st.c["n_attn"], "kv_heads": st.c["Hkv"], "q_heads": st.c["Hq"],
+            "head_dim": st.c["D"], "gdn_heads": [st.c["Hk"], st.c["Hv"]], "state": [st.c["dv"], st.c["dk"]],
+            "conv_channels": st.c["C"], "vocab": synth.VOCAB, "graph": use_graph,
+            "inputs": "fp16 KV cache and attention, bf16 delta-net/conv/logits, fp32 state and accumulation",
+            "mean_accepted_L": L_mean,
+        },
+        "achieved_GBps_step": step_bytes / (ms * 1e-3) / 1e9,
+        "roofline_frac_step": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "wall_s_timed": wall,
+        "roofline": {
+            "kernel": "ddt_tree_attn (attn_mfma_kernel + attn_combine_kernel)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "bytes_per_call": attn_bytes, "ms_per_call": attn_ms,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(st, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+/*
+ * ddtree.h -- C ABI of libddtree.so, the DDTree tree-verify step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step verifies a budget-sized draft token tree against the committed
+ * state of a hybrid linear-attention target in one pass, then accepts the
+ * longest draft path that agrees with the target's greedy choice and rolls
+ * the linear-attention state forward to it.  Sources:
+ *   [P1] Luce-Org/lucebox-hub README (bittide copy), section
+ *        "02 · DFlash DDtree Qwen3.5 & Qwen3.6 27B GGUF on RTX 3090":
+ *        "Algorithms used" (DDTree tree-structured verify beats chain verify
+ *        at the same budget), "Implemented here" (tree-aware SSM state
+ *        rollback kernels ssm_conv_tree, gated_delta_net_tree and
+ *        gated_delta_net_tree_persist; budget 22), "Retune per GPU".
+ *   [P2] codehub view of lucebox-hub@main: "Run the Server" / "Making
+ *        requests" (greedy decoding), "Server flags" (--ddtree,
+ *        --ddtree-budget 22, --fa-window 0 = full attention),
+ *        "GPU draft top-K & verify-argmax (DFlash)" (verify argmax read in
+ *        place from device logits, result validated).
+ *   [P3] Luce-Org/lucebox README, "Inference Engine Optimizations" (paged
+ *        attention, concurrent serving).
+ * The recurrence of the linear-attention layers is the gated delta rule
+ * (Yang, Kautz, Hatamizadeh, "Gated Delta Networks", 2024).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers named "device" are HIP device pointers owned by the caller;
+ *   the library never allocates, frees or keeps a pointer past the call.
+ * - Every call that takes `stream` validates its host-visible arguments,
+ *   then enqueues kernels on that hipStream_t (passed as void*, NULL = the
+ *   null stream) and returns without synchronising.  On any validation
+ *   error it returns a negative DDT_E_* code and enqueues nothing.
+ * - Problems that only the device can see (a malformed parent array, a draft
+ *   token outside the vocabulary, ...) are reported as DDT_ST_* bits in the
+ *   per-sequence device status word plan->status[b]; kernels never read
+ *   outside their buffers on such input.  The caller reads the status words
+ *   (a few bytes) after the step and discards results of flagged sequences.
+ *   There is no silent CPU fallback.
+ * - Several sequences are verified together (continuous batching, [P3]):
+ *   their trees are concatenated; node ids inside a tree are local
+ *   (0 = root), and "global" node g = tree_off[b] + local id indexes the
+ *   per-node arrays.
+ * - Calls on different streams are thread-safe; calls that share output
+ *   buffers must be ordered by the caller.
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDT_VERSION 1
+
+/* return codes */
+#define DDT_OK 0
+#define DDT_E_ARG (-1)    /* null pointer or bad enum / flag               */
+#define DDT_E_TREE (-2)   /* malformed tree (host-side plan only)           */
+#define DDT_E_SHAPE (-3)  /* unsupported or inconsistent sizes              */
+#define DDT_E_DTYPE (-4)  /* unsupported storage type                       */
+#define DDT_E_RANGE (-5)  /* value out of range (host-side checks)          */
+#define DDT_E_WS (-6)     /* workspace too small                            */
+#define DDT_E_HIP (-7)    /* a HIP launch failed; see ddt_status_str        */
+
+/* device status bits, OR-ed into plan->status[b] */
+#define DDT_ST_TREE 1u    /* parent array of sequence b malformed           */
+#define DDT_ST_LEVELS 2u  /* tree deeper than the level cap                 */
+#define DDT_ST_TOKEN 4u   /* a draft token is outside [0, V)                */
+#define DDT_ST_ARGMAX 8u  /* verify argmax failed validation                */
+#define DDT_ST_CTX 16u    /* context length / page table cannot hold it     */
+#define DDT_ST_COMMIT 32u /* commit descriptor incomplete                   */
+
+/* storage types */
+#define DDT_F32 0
+#define DDT_F16 1
+#define DDT_BF16 2
+
+#define DDT_MAX_NODES 64 /* nodes per tree, root included                  */
+#define DDT_MAX_W 8      /* conv width                                      */
+#define DDT_PAGE 16      /* tokens per KV page                              */
+
+/*
+ * Plan of a batch of draft trees.  Host struct holding device pointers
+ * (host pointers for ddt_tree_plan_host).  The caller allocates every array
+ * with the stated size; ddt_tree_plan fills the outputs.
+ *
+ * Tree encoding ([P1] "Algorithms used"; [P2] --ddtree-budget): parent
+ * pointers, parent[root] = -1, 0 <= parent[i] < i, so index order is
+ * topological.  The root is the last committed token (the previous step's
+ * bonus), not yet in the cache or the state; the budget counts it.
+ */
+typedef struct ddt_plan {
+  int32_t B;       /* sequences, >= 1                                      */
+  int32_t n_total; /* nodes over all sequences = tree_off[B]               */
+  int32_t n_max;   /* largest tree, 1..DDT_MAX_NODES                       */
+  int32_t W;       /* conv width the windows are built for, 1..DDT_MAX_W   */
+  const int32_t *tree_off; /* [B+1] node offsets, tree_off[0] = 0           */
+  const int32_t *parent;   /* [n_total] local parent ids                    */
+  int32_t *depth;  /* out [n_total] edge depth (root 0)                    */
+  uint64_t *anc;   /* out [n_total] bit j = local node j on the root path  */
+  int32_t *win;    /* out [n_total][max(W-1,1)]: entry j-1 = j-th previous
+                      token on prefix ++ root path: local node id >= 0, or
+                      -(s+1) for committed prefix slot s (0 = oldest)     */
+  int32_t *order;  /* out [n_total] per tree: local ids in the order the
+                      linear-attention kernels visit them (a depth-first
+                      preorder that visits each node's largest subtree
+                      last; parents precede children)                     */
+  int32_t *slot;   /* out [n_total] state slot of each node for that visit
+                      order; slots <= floor(log2(n_max))                  */
+  int32_t *status; /* out [B] device status word, DDT_ST_* bits          */
+} ddt_plan;
+
+int ddt_version(void);
+const char *ddt_status_str(int code);
+
+/* Number of state slots the visit order needs for trees of n_max nodes. */
+int ddt_plan_slots(int32_t n_max);
+
+/*
+ * a1. Tree plan on the host: same outputs as ddt_tree_plan, all pointers in
+ * `plan` are host pointers.  Returns DDT_E_TREE on a malformed tree (any
+ * parent[0] != -1, parent[i] outside [0, i), tree size outside
+ * [1, DDT_MAX_NODES] or above n_max) and DDT_E_RANGE when a tree has more
+ * than max_levels levels (levels count the nodes on a root path).  Outputs
+ * are written only on DDT_OK.
+ */
+int ddt_tree_plan_host(const ddt_plan *plan, int32_t max_levels);
+
+/*
+ * a1. Tree plan on the device (one wavefront per sequence).  Reads
+ * plan->tree_off and plan->parent, writes depth, anc, win, order, slot and
+ * resets status[b] to the sequence's DDT_ST_TREE / DDT_ST_LEVELS bits.  A
+ * malformed tree is flagged and replaced by a safe plan (invalid parents
+ * read as the root) so later kernels stay in bounds.  Must run before the
+ * other calls of a step.
+ */
+int ddt_tree_plan(const ddt_plan *plan, int32_t max_levels, void *stream);
+
+/*
+ * a2. Tree-aware causal depthwise conv1d ([P1] "Implemented here",
+ * ssm_conv_tree).  For every node i and channel c:
+ *   y[i][c] = act( sum_{t=0}^{W-1} w[c][W-1-t] * tok_t(i)[c] )
+ * where tok_0 = x[i] and tok_j (j >= 1) is window entry j-1 of the plan
+ * (an ancestor's x, or a committed prefix token).  No bias.
+ *   x      device [n_total][C]        dtype
+ *   prefix device [B][W-1][C]         dtype, oldest first (read only)
+ *   w      device [C][W]              dtype, tap W-1 = current token
+ *   y      device [n_total][C]        fp32
+ *   act    0 = identity, 1 = SiLU;  dtype DDT_F32 or DDT_BF16;  C % 8 == 0.
+ */
+int ddt_tree_conv(const ddt_plan *plan, const void *x, const void *prefix, const void *w,
+                  int32_t C, int32_t act, int32_t dtype, float *y, void *stream);
+
+/*
+ * a3. Tree gated delta-net ([P1] "Implemented here", gated_delta_net_tree
+ * and its _persist variant).  For value head h (key head g = h / (Hv/Hk)),
+ * every node n starts from its parent's state (the root from S_c[b][h]):
+ *   S_n = alpha_n S_p (I - beta_n k_n k_n^T) + beta_n v_n k_n^T
+ *   out_n = scale * S_n q_n
+ * S is dv x dk (row r of S maps keys to value channel r).
+ *   q, k        device [n_total][Hk][dk]   dtype
+ *   v           device [n_total][Hv][dv]   dtype
+ *   alpha, beta device [n_total][Hv]       dtype
+ *   S_c         device [B][Hv][dv][dk]     fp32, read only
+ *   out         device [n_total][Hv][dv]   fp32
+ *   node_states device [n_total][Hv][dv][dk] fp32 or NULL: when given, every
+ *               node's state is stored ("persist"), so the commit can
+ *               select the accepted node's state instead of replaying.
+ * Requires Hv % Hk == 0, dk in {16, 32, 64, 128}, dv % 16 == 0 (dv <= 128
+ * or a multiple of the row tile), dtype DDT_F32 or DDT_BF16.
+ */
+int ddt_tree_gdn(const ddt_plan *plan, const void *q, const void *k, const void *v,
+                 const void *alpha, const void *beta, const float *S_c, int32_t Hk, int32_t Hv,
+                 int32_t dk, int32_t dv, float scale, int32_t dtype, float *out,
+                 float *node_states, void *stream);
+
+/*
+ * a4. Tree-masked attention over the committed KV cache.  Node i, query
+ * head h (KV head g = h / (Hq/Hkv)) attends to all T[b] committed tokens of
+ * its sequence plus the draft tokens on its own root path, itself included
+ * (plan->anc); full attention, no window ([P2] --fa-window 0):
+ *   out[i][h] = softmax(scale * K q_ih)^T V
+ * The cache is paged ([P3]); a page holds DDT_PAGE tokens of every KV head:
+ *   Kc device [P][Hkv][DDT_PAGE][D]   token t at page_table[b][t/16], row t%16
+ *   Vc device [P][Hkv][D][DDT_PAGE]   same page, column t%16 (channel-major
+ *                                     inside a page)
+ *   page_table device [B][max_pages] int32, or NULL for B == 1 with page
+ *              t/16 (a contiguous cache).
+ *   T          device [B] committed lengths; each must be <= T_max (host).
+ *   q          device [n_total][Hq][D];  Kt, Vt device [n_total][Hkv][D]
+ *              (the tree's draft keys/values, not yet in the cache)
+ *   out        device [n_total][Hq][D] fp32
+ *   ws         device workspace of ddt_tree_attn_workspace() bytes.
+ * dtype: DDT_F16 (D in {64, 128, 256} use matrix cores; D <= 64 also
+ * accepted) or DDT_F32 (D <= 64).  Hq % Hkv == 0.  n_splits: number of
+ * context splits per (sequence, KV head), 0 = automatic.  A sequence whose
+ * T[b] exceeds T_max or its page table is flagged DDT_ST_CTX and only its
+ * first T_max tokens are read.
+ */
+size_t ddt_tree_attn_workspace(const ddt_plan *plan, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t T_max, int32_t n_splits);
+int ddt_tree_attn(const ddt_plan *plan, const void *q, const void *Kc, const void *Vc,
+                  const int32_t *page_table, int32_t max_pages, const int32_t *T, int32_t T_max,
+                  const void *Kt, const void *Vt, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                  int32_t dtype, int32_t n_splits, float *out, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/*
+ * a5. Verify argmax and greedy acceptance walk ([P2] "Making requests":
+ * greedy decoding; "GPU draft top-K & verify-argmax": the argmax is read in
+ * place from the device logits and validated).
+ *   argmax[i] = smallest v maximising logits[i][v] (NaN never wins)
+ *   path: start at the root; while some child c of the last node has
+ *   draft_tok[c] == argmax[last], append the smallest such c.
+ *   logits    device [n_total][V]  DDT_F32 or DDT_BF16
+ *   draft_tok device [n_total] int32 (the root's entry is not compared)
+ *   argmax    device out [n_total] int32
+ *   path      device out [B][n_max] int32 local ids, padded with -1
+ *   L         device out [B] path length (tokens emitted = L: L-1 drafts
+ *             plus the bonus token)
+ *   bonus     device out [B] argmax of the last path node
+ *   ws        device workspace of ddt_accept_walk_workspace() bytes.
+ * A draft token outside [0, V) sets DDT_ST_TOKEN (it can never match).
+ */
+size_t ddt_accept_walk_workspace(const ddt_plan *plan, int32_t V);
+int ddt_accept_walk(const ddt_plan *plan, const void *logits, int32_t dtype, int32_t V,
+                    const int32_t *draft_tok, int32_t *argmax, int32_t *path, int32_t *L,
+                    int32_t *bonus, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * a6. Commit of the accepted path ([P1] "Implemented here": tree-aware SSM
+ * state rollback; "Why GGUF": the DDTree verify state).  In one launch, for
+ * every sequence b with accepted local path p_0 = 0, ..., p_{L-1}:
+ *  - each gated delta-net layer: S_c[b] <- state of node p_{L-1}.
+ *    mode DDT_COMMIT_REPLAY re-runs the rule along the path from S_c;
+ *    mode DDT_COMMIT_SELECT copies the persisted node state (node_states of
+ *    that layer must be non-NULL).
+ *  - each conv: prefix[b] <- last W-1 rows of prefix[b] ++ x[path].
+ *  - each attention layer: the path's Kt/Vt are written to cache positions
+ *    T[b] .. T[b]+L-1 (the page table must already map them), and finally
+ *    T[b] += L.
+ * The layer descriptor arrays live in DEVICE memory (the caller builds them
+ * once); their shapes are given here.  Per-layer fields may be NULL where
+ * noted.
+ */
+#define DDT_COMMIT_REPLAY 0
+#define DDT_COMMIT_SELECT 1
+
+typedef struct ddt_gdn_layer {
+  const void *q, *k, *v, *alpha, *beta; /* this step's tree inputs (ddt_tree_gdn) */
+  float *S_c;                           /* [B][Hv][dv][dk], updated in place */
+  const float *node_states;             /* SELECT source, or NULL            */
+  const void *x;                        /* conv input [n_total][C], NULL = no conv */
+  void *prefix;                         /* [B][W-1][C], updated in place     */
+} ddt_gdn_layer;
+
+typedef struct ddt_attn_layer {
+  const void *Kt, *Vt; /* [n_total][Hkv][D] draft keys / values */
+  void *Kc, *Vc;       /* the layer's page pools                */
+} ddt_attn_layer;
+
+int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L, int32_t mode,
+                     const ddt_gdn_layer *gdn_layers, int32_t n_gdn, int32_t Hk, int32_t Hv,
+                     int32_t dk, int32_t dv, int32_t gdn_dtype, int32_t C, int32_t conv_dtype,
+                     const ddt_attn_layer *attn_layers, int32_t n_attn, int32_t Hkv, int32_t D,
+                     int32_t kv_dtype, const int32_t *page_table, int32_t max_pages, int32_t *T,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DDTREE_H */

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: exports, the host-side plan, and argument
+validation (every call below returns before any kernel is enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import tree_verification_ddtree_amd as ddt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "ddtree.h")).read()
+    names = set(re.findall(r"\b(ddt_\w+)\s*\(", hdr))
+    assert len(names) >= 12
+    L = ddt.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert ddt.ddt_version() == 1
+
+
+def host_plan(trees, W=4, max_levels=64, n_max=None):
+    par, off = synth.concat_trees(trees)
+    n = len(par)
+    out = dict(depth=np.zeros(n, np.int32), anc=np.zeros(n, np.uint64),
+               win=np.zeros(n * max(W - 1, 1), np.int32), order=np.zeros(n, np.int32),
+               slot=np.zeros(n, np.int32), status=np.zeros(len(trees), np.int32))
+    nm = n_max or max(len(t) for t in trees)
+    st = ddt.plan_struct(len(trees), n, nm, W, off, par, out["depth"], out["anc"], out["win"],
+                         out["order"], out["slot"], out["status"])
+    rc = ddt.ddt_tree_plan_host(st, max_levels)
+    return rc, par, off, out
+
+
+def check_schedule(par, order, slot, n):
+    """Replay the visit order with per-slot contents: every parent state must
+    still be in its slot when a child reads it; slots stay within the bound."""
+    assert sorted(order) == list(range(n))
+    pos = {v: i for i, v in enumerate(order)}
+    assert all(pos[int(par[i])] < pos[i] for i in range(1, n))      # parents first
+    # preorder: each subtree is a contiguous run starting at its root
+    for u in range(n):
+        sub = [v for v in range(n) if u in oracle.root_path(par, v)]
+        ps = sorted(pos[v] for v in sub)
+        assert ps == list(range(pos[u], pos[u] + len(sub)))
+    nslot = ddt.ddt_plan_slots(n)
+    held = {}
+    for v in order:
+        p = int(par[v])
+        if p >= 0:
+            assert held.get(int(slot[p])) == p, "parent state overwritten"
+        assert 0 <= slot[v] < nslot
+        held[int(slot[v])] = v
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_host_plan_matches_oracle_and_schedules(seed):
+    sizes = [22, 64, 1, 7, 33, 2]
+    trees = [synth.random_tree(synth.rng_for(seed, 20, b), s, 10 if s > 22 else 8)
+             for b, s in enumerate(sizes)]
+    trees.append(synth.chain(40))
+    trees.append(synth.binary_tree(5))   # 31 nodes
+    rc, par, off, out = host_plan(trees, W=4)
+    assert rc == 0
+    W1 = 3
+    for b, t in enumerate(trees):
+        o, e = off[b], off[b + 1]
+        n = e - o
+        assert list(out["depth"][o:e]) == list(oracle.depth(t))
+        assert [int(x) for x in out["anc"][o:e]] == oracle.ancestor_mask(t)
+        np.testing.assert_array_equal(out["win"][o * W1:e * W1].reshape(n, W1), oracle.conv_window(t, 4))
+        check_schedule(t, list(out["order"][o:e]), out["slot"][o:e], n)
+        assert out["status"][b] == 0
+
+
+def test_host_plan_all_small_trees():
+    import itertools
+    for n in range(1, 7):
+        for ps in itertools.product(*[range(i) for i in range(1, n)]):
+            t = np.array([-1, *ps], dtype=np.int32)
+            rc, par, off, out = host_plan([t], W=3)
+            assert rc == 0
+            assert [int(x) for x in out["anc"]] == oracle.ancestor_mask(t)
+            check_schedule(t, list(out["order"]), out["slot"], n)
+
+
+def test_slot_bound_is_tight_for_complete_binary_trees():
+    for lv in range(1, 7):
+        t = synth.binary_tree(lv)
+        rc, par, off, out = host_plan([t], W=2)
+        assert rc == 0 and int(out["slot"].max()) + 1 <= ddt.ddt_plan_slots(len(t))
+
+
+def test_host_plan_rejects_malformed_trees():
+    assert host_plan([np.array([0, 0], np.int32)])[0] == -2
+    assert host_plan([np.array([-1, 1], np.int32)])[0] == -2
+    assert host_plan([np.array([-1, 0, 5], np.int32)])[0] == -2
+    assert host_plan([synth.chain(10)], max_levels=9)[0] == -5       # 10 levels > 9
+    assert host_plan([synth.chain(10)], max_levels=10)[0] == 0
+    assert host_plan([synth.chain(8)], n_max=7)[0] in (-2, -3)         # tree larger than n_max
+    assert host_plan([synth.chain(3)], W=9)[0] == -3                    # W > DDT_MAX_W
+
+
+def _dummy_plan(B=1, n=4, n_max=4, W=4):
+    z = np.zeros(64, np.int64)
+    return ddt.plan_struct(B, n, n_max, W, z, z, z, z, z, z, z, z)
+
+
+def test_device_entry_points_validate_before_launch():
+    L = ddt.lib()
+    P = _dummy_plan()
+    bp = ctypes.byref(P)
+    one = ctypes.c_void_p(16)
+    # gated delta-net: Hv not a multiple of Hk; unsupported dk; dtype
+    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 3, 4, 128, 128, 1.0, 2, one, None, None) == -3
+    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 2, 4, 96, 128, 1.0, 2, one, None, None) == -3
+    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 2, 4, 128, 128, 1.0, 1, one, None, None) == -4
+    assert L.ddt_tree_gdn(bp, None, one, one, one, one, one, 2, 4, 128, 128, 1.0, 2, one, None, None) == -1
+    # conv: channels not a multiple of 8, bad activation
+    assert L.ddt_tree_conv(bp, one, one, one, 12, 0, 2, one, None) == -3
+    assert L.ddt_tree_conv(bp, one, one, one, 16, 2, 2, one, None) == -1
+    # attention: GQA mismatch, small workspace, paged without table for B > 1
+    assert L.ddt_tree_attn(bp, one, one, one, None, 0, one, 100, one, one, 6, 4, 256, 0.1, 1, 0,
+                           one, one, 0, None) == -3
+    assert L.ddt_tree_attn(bp, one, one, one, None, 0, one, 100, one, one, 24, 4, 256, 0.1, 1, 0,
+                           one, one, 16, None) == -6
+    P2 = _dummy_plan(B=2)
+    assert L.ddt_tree_attn(ctypes.byref(P2), one, one, one, None, 0, one, 100, one, one, 24, 4, 256,
+                           0.1, 1, 0, one, one, 1 << 30, None) == -1
+    assert ddt.ddt_tree_attn_workspace(P, 24, 4, 256, 131072) > 0
+    # walk: workspace, dtype
+    assert L.ddt_accept_walk(bp, one, 2, 1000, one, one, one, one, one, one, 0, None) == -6
+    assert L.ddt_accept_walk(bp, one, 1, 1000, one, one, one, one, one, one, 1 << 20, None) == -4
+    # plan struct itself
+    assert L.ddt_tree_plan(ctypes.byref(_dummy_plan(n_max=65)), 8, None) == -3
+    assert L.ddt_tree_plan(ctypes.byref(_dummy_plan(W=0)), 8, None) == -3
+    # commit: bad mode, SELECT/REPLAY shapes
+    assert L.ddt_commit_state(bp, one, one, 7, one, 1, 16, 32, 128, 128, 2, 8192, 2, None, 0, 4,
+                              256, 1, None, 0, None, None) == -1
+    assert L.ddt_commit_state(bp, one, one, 0, one, 1, 16, 30, 128, 128, 2, 8192, 2, None, 0, 4,
+                              256, 1, None, 0, None, None) == -3
+    for c in (-1, -2, -3, -4, -5, -6, -7, 0):
+        assert ddt.status_str(c)

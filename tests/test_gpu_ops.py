@@ -1,0 +1,317 @@
+"""GPU parity of each entry point against the CPU oracle, through the C ABI.
+
+Sizes span several tiles and ragged tails while the oracle still finishes in
+seconds; integer outputs are compared bit for bit, floating-point outputs to
+max relative error 2e-3 per slice."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tree_verification_ddtree_amd as ddt
+from gpu_util import TOL, banner, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def make_batch(trees, W, gpu, max_levels=64):
+    par, off = synth.concat_trees(trees)
+    tb = ddt.TreeBatch(par, off, W, gpu)
+    ddt.ddt_tree_plan(tb, max_levels)
+    return tb, par, off
+
+
+# ------------------------------------------------------------------ plan
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_plan_device_matches_host_and_oracle(gpu, seed):
+    banner(f"plan seed={seed}")
+    sizes = [22, 64, 1, 7, 33, 2, 16]
+    trees = [synth.random_tree(synth.rng_for(seed, 30, b), s, 10) for b, s in enumerate(sizes)]
+    trees += [synth.chain(64), synth.binary_tree(6)]
+    for W in (4, 1, 8):
+        tb, par, off = make_batch(trees, W, gpu)
+        torch.cuda.synchronize()
+        n = len(par)
+        W1 = max(W - 1, 1)
+        h = dict(depth=np.zeros(n, np.int32), anc=np.zeros(n, np.uint64),
+                 win=np.zeros(n * W1, np.int32), order=np.zeros(n, np.int32),
+                 slot=np.zeros(n, np.int32), status=np.zeros(len(trees), np.int32))
+        st = ddt.plan_struct(len(trees), n, tb.n_max, W, off, par, h["depth"], h["anc"], h["win"],
+                             h["order"], h["slot"], h["status"])
+        assert ddt.ddt_tree_plan_host(st, 64) == 0
+        assert np.array_equal(host(tb.depth), h["depth"])
+        assert np.array_equal(host(tb.anc).view(np.uint64), h["anc"])
+        assert np.array_equal(host(tb.win), h["win"])
+        assert np.array_equal(host(tb.order), h["order"])
+        assert np.array_equal(host(tb.slot), h["slot"])
+        assert not host(tb.status).any()
+        for b, t in enumerate(trees):
+            o, e = off[b], off[b + 1]
+            assert list(host(tb.depth)[o:e]) == list(oracle.depth(t))
+            assert [int(x) for x in host(tb.anc).view(np.uint64)[o:e]] == oracle.ancestor_mask(t)
+            if W > 1:
+                np.testing.assert_array_equal(host(tb.win)[o * (W - 1):e * (W - 1)].reshape(e - o, W - 1),
+                                              oracle.conv_window(t, W))
+
+
+def test_plan_flags_malformed_trees(gpu):
+    banner("plan malformed")
+    good = synth.random_tree(synth.rng_for(0, 31), 22, 8)
+    bad1 = good.copy(); bad1[5] = 9          # parent after child
+    bad2 = good.copy(); bad2[0] = 0          # root with a parent
+    deep = synth.chain(12)                   # 12 levels > cap 8
+    par, off = synth.concat_trees([good, bad1, bad2, deep])
+    tb = ddt.TreeBatch(par, off, 4, gpu)
+    ddt.ddt_tree_plan(tb, 8)
+    st = host(tb.status)
+    assert st[0] == 0
+    assert st[1] & ddt.DDT_ST_TREE and st[2] & ddt.DDT_ST_TREE
+    assert st[3] == ddt.DDT_ST_LEVELS
+    slot = host(tb.slot)
+    order = host(tb.order)
+    for b in range(4):
+        o, e = off[b], off[b + 1]
+        assert sorted(order[o:e]) == list(range(e - o))       # still a permutation
+        assert (slot[o:e] >= 0).all() and (slot[o:e] < ddt.ddt_plan_slots(tb.n_max)).all()
+
+
+# ------------------------------------------------------------------ conv
+@pytest.mark.parametrize("case", ["tiny_f32", "layer_bf16", "batch_silu_bf16"])
+def test_conv(gpu, case):
+    banner(f"conv {case}")
+    if case == "tiny_f32":
+        trees, C, W, dt, act = [synth.binary_tree(3)], 64, 4, "f32", 0
+    elif case == "layer_bf16":
+        trees, C, W, dt, act = [synth.random_tree(synth.rng_for(1, 40), 22, 8)], 8192, 4, "bf16", 0
+    else:
+        trees = [synth.random_tree(synth.rng_for(2, 41, b), s, 10) for b, s in enumerate([8, 64, 22])]
+        C, W, dt, act = 1024, 4, "bf16", 1
+    tb, par, off = make_batch(trees, W, gpu)
+    inp = synth.conv_inputs(3, (42,), len(par), C, W, dt, B=len(trees))
+    y = torch.empty(len(par), C, dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_conv(tb, dev(inp["x"]), dev(inp["prefix"]), dev(inp["w"]), act, y)
+    ref = oracle.tree_conv(par, inp["x"], inp["prefix"], inp["w"], act=act, tree_off=off)
+    assert rel_err(host(y), ref, (0,)) < TOL
+
+
+# ------------------------------------------------------------------ gated delta-net
+GDN_CASES = {
+    "tiny_f32": dict(sizes=[7], Hk=2, Hv=2, d=16, dt="f32", binary=True),
+    "layer_bf16": dict(sizes=[22], Hk=16, Hv=32, d=128, dt="bf16"),
+    "batch_bf16": dict(sizes=[8, 64, 22, 1], Hk=2, Hv=4, d=128, dt="bf16"),
+    "gqa_d64_f32": dict(sizes=[13, 5], Hk=1, Hv=4, d=64, dt="f32"),
+}
+
+
+@pytest.mark.parametrize("case", list(GDN_CASES))
+def test_gdn(gpu, case):
+    banner(f"gdn {case}")
+    c = GDN_CASES[case]
+    if c.get("binary"):
+        trees = [synth.binary_tree(3)]
+    else:
+        trees = [synth.random_tree(synth.rng_for(4, 50, b), s, 10) for b, s in enumerate(c["sizes"])]
+    tb, par, off = make_batch(trees, 4, gpu)
+    n, B = len(par), len(trees)
+    inp = synth.gdn_inputs(5, (51,), n, c["Hk"], c["Hv"], c["d"], c["d"], c["dt"], B=B)
+    d = {k: dev(v) for k, v in inp.items()}
+    out = torch.empty(n, c["Hv"], c["d"], dtype=torch.float32, device=gpu)
+    out2 = torch.empty_like(out)
+    ns = torch.empty(n, c["Hv"], c["d"], c["d"], dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_gdn(tb, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_c"], 1.0, out)
+    ddt.ddt_tree_gdn(tb, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_c"], 1.0, out2, ns)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)  # persisting states does not change the outputs
+    if c["Hv"] * c["d"] ** 2 * n <= 32 * 128 * 128 * 22:
+        ref, states = oracle.tree_gdn(par, **inp, tree_off=off, want_states=True)
+        assert rel_err(host(ns), states, (0, 1)) < TOL
+    else:
+        ref = oracle.tree_gdn(par, **inp, tree_off=off)
+    assert rel_err(host(out), ref, (0, 1)) < TOL
+
+
+def test_gdn_scale(gpu):
+    banner("gdn scale")
+    trees = [synth.random_tree(synth.rng_for(6, 52), 10, 5)]
+    tb, par, off = make_batch(trees, 4, gpu)
+    inp = synth.gdn_inputs(6, (52,), len(par), 2, 4, 32, 32, "bf16")
+    d = {k: dev(v) for k, v in inp.items()}
+    out = torch.empty(len(par), 4, 32, dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_gdn(tb, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_c"], 0.125, out)
+    ref = oracle.tree_gdn(par, **inp, scale=0.125)
+    assert rel_err(host(out), ref, (0, 1)) < TOL
+
+
+# ------------------------------------------------------------------ attention
+def attn_case(gpu, trees, T, Hq, Hkv, D, dt, seed, paged=True, nan_fill=False, n_splits=0,
+              rows=None):
+    tb, par, off = make_batch(trees, 4, gpu)
+    n, B = len(par), len(trees)
+    T = np.asarray(T)
+    pt, P = synth.page_layout(seed, (60,), T, [len(t) for t in trees], shuffle=paged)
+    K, V = synth.kv_pool(seed, (60,), P, Hkv, D, dt)
+    if nan_fill:  # slots past T must never influence the result
+        for b in range(B):
+            for t in range(int(T[b]), int(np.ceil((T[b] + len(trees[b])) / 16)) * 16):
+                K[pt[b][t // 16], :, t % 16, :] = np.nan
+                V[pt[b][t // 16], :, :, t % 16] = np.nan
+    a = synth.attn_inputs(seed, (61,), n, Hq, Hkv, D, dt)
+    use_pt = paged or B > 1
+    ptd = dev(pt) if use_pt else None
+    Td = dev(T.astype(np.int32))
+    T_max = int(T.max())
+    ws_bytes = ddt.ddt_tree_attn_workspace(tb, Hq, Hkv, D, T_max, n_splits)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=gpu)
+    out = torch.full((n, Hq, D), np.nan, dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_attn(tb, dev(a["q"]), dev(K), dev(V), ptd, Td, T_max, dev(a["Kt"]), dev(a["Vt"]),
+                      out, ws, n_splits=n_splits)
+    torch.cuda.synchronize()
+    ref = oracle.tree_attn(par, a["q"], K, V, T, a["Kt"], a["Vt"],
+                           page_table=pt if use_pt else None, tree_off=off, rows=rows)
+    got = host(out)
+    if rows is not None:
+        idx = tuple(np.array(rows).T)
+        return rel_err(got[idx], ref[idx], (0,)), tb
+    assert np.isfinite(got).all()
+    return rel_err(got, ref, (0, 1)), tb
+
+
+def test_attn_tiny_f32(gpu):
+    banner("attn tiny f32 D=16")
+    err, _ = attn_case(gpu, [synth.binary_tree(3)], [64], 2, 1, 16, "f32", 0, paged=False)
+    assert err < TOL
+
+
+@pytest.mark.parametrize("T", [0, 5, 32, 100, 1000, 4133])
+def test_attn_mfma_contiguous(gpu, T):
+    banner(f"attn mfma D=256 N=22 T={T}")
+    tree = synth.random_tree(synth.rng_for(7, 62), 22, 8)
+    err, _ = attn_case(gpu, [tree], [T], 24, 4, 256, "f16", 7, paged=False)
+    assert err < TOL
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 0])
+def test_attn_mfma_paged_nan_tail(gpu, n_splits):
+    banner(f"attn mfma paged nan-tail splits={n_splits}")
+    trees = [synth.random_tree(synth.rng_for(8, 63, b), s, 10) for b, s in enumerate([22, 8, 64])]
+    err, _ = attn_case(gpu, trees, [1500, 37, 3001], 24, 4, 256, "f16", 8, paged=True,
+                       nan_fill=True, n_splits=n_splits)
+    assert err < TOL
+
+
+def test_attn_mfma_d128_and_chain(gpu):
+    banner("attn mfma D=128")
+    trees = [synth.chain(16), synth.random_tree(synth.rng_for(9, 64), 32, 10)]
+    err, _ = attn_case(gpu, trees, [777, 2048], 16, 2, 128, "f16", 9)
+    assert err < TOL
+
+
+def test_attn_full_context_32k_sampled(gpu):
+    banner("attn mfma T=32768 N=22 sampled rows")
+    tree = synth.random_tree(synth.rng_for(10, 65), 22, 8)
+    rng = np.random.default_rng(10)
+    rows = [(int(i), int(h)) for i, h in zip(rng.integers(0, 22, 12), rng.integers(0, 24, 12))]
+    rows += [(21, 23), (0, 0)]
+    err, _ = attn_case(gpu, [tree], [32768], 24, 4, 256, "f16", 10, paged=False, rows=rows)
+    assert err < TOL
+
+
+def test_attn_deterministic(gpu):
+    banner("attn determinism")
+    tree = synth.random_tree(synth.rng_for(11, 66), 22, 8)
+    tb, par, off = make_batch([tree], 4, gpu)
+    pt, P = synth.page_layout(11, (67,), [3000], [22])
+    K, V = synth.kv_pool(11, (67,), P, 4, 256, "f16")
+    a = synth.attn_inputs(11, (67,), 22, 24, 4, 256, "f16")
+    args = [dev(a["q"]), dev(K), dev(V), dev(pt), dev(np.array([3000], np.int32)), 3000,
+            dev(a["Kt"]), dev(a["Vt"])]
+    ws = torch.empty(ddt.ddt_tree_attn_workspace(tb, 24, 4, 256, 3000), dtype=torch.uint8, device=gpu)
+    o1 = torch.empty(22, 24, 256, dtype=torch.float32, device=gpu)
+    o2 = torch.empty_like(o1)
+    ddt.ddt_tree_attn(tb, *args, o1, ws)
+    ddt.ddt_tree_attn(tb, *args, o2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ accept walk
+@pytest.mark.parametrize("case", ["planted_bf16", "ties_bf16", "f32_ragged_vocab", "batch"])
+def test_accept_walk(gpu, case):
+    banner(f"walk {case}")
+    V = 151936
+    if case == "planted_bf16":
+        trees, dt, plant, pm = [synth.random_tree(synth.rng_for(12, 70), 22, 8)], "bf16", True, 0.8
+    elif case == "ties_bf16":
+        trees, dt, plant, pm = [synth.random_tree(synth.rng_for(13, 71), 22, 8)], "bf16", False, 0
+    elif case == "f32_ragged_vocab":
+        trees, dt, plant, pm, V = [synth.binary_tree(3)], "f32", True, 0.9, 1001
+    else:
+        trees = [synth.random_tree(synth.rng_for(14, 72, b), s, 10) for b, s in enumerate([8, 64, 22, 1, 32])]
+        dt, plant, pm = "bf16", True, 0.9
+    logits, toks = [], []
+    for b, t in enumerate(trees):
+        lg, tk = synth.logits_and_draft(15, (73, b), t, V, dt, p_match=pm, plant=plant)
+        logits.append(lg)
+        toks.append(tk)
+    lg = np.concatenate(logits)
+    tok = np.concatenate(toks).astype(np.int32)
+    if case == "ties_bf16":
+        # unplanted bf16 rows tie at their maximum; force one more explicit
+        # tie, then let every other node carry its parent's argmax so the walk
+        # runs deep through tie-decided choices
+        X = oracle.num.f64(lg)
+        lg[5, 100:110] = lg[5, int(np.argmax(X[5]))]
+        am = oracle.argmax_rows(lg)
+        par0 = trees[0]
+        for i in range(1, len(par0)):
+            if i % 3:
+                tok[i] = am[par0[i]]
+    tb, par, off = make_batch(trees, 4, gpu)
+    n, B = len(par), len(trees)
+    ws = torch.empty(ddt.ddt_accept_walk_workspace(tb, V), dtype=torch.uint8, device=gpu)
+    am = torch.empty(n, dtype=torch.int32, device=gpu)
+    path = torch.empty(B, tb.n_max, dtype=torch.int32, device=gpu)
+    L = torch.empty(B, dtype=torch.int32, device=gpu)
+    bonus = torch.empty(B, dtype=torch.int32, device=gpu)
+    ddt.ddt_accept_walk(tb, dev(lg), dev(tok), am, path, L, bonus, ws)
+    torch.cuda.synchronize()
+    ref_am = oracle.argmax_rows(lg)
+    assert np.array_equal(host(am), ref_am)
+    paths, rL, rb = oracle.accept_walk(par, tok, ref_am, tree_off=off)
+    assert np.array_equal(host(L), rL) and np.array_equal(host(bonus), rb)
+    hp = host(path)
+    for b in range(B):
+        assert list(hp[b, :rL[b]]) == paths[b] and (hp[b, rL[b]:] == -1).all()
+    assert not host(tb.status).any()
+    if case == "planted_bf16":
+        assert rL[0] >= 1
+
+
+def test_accept_walk_nan_and_bad_tokens(gpu):
+    banner("walk NaN + bad tokens")
+    V = 4096
+    tree = synth.chain(6)
+    lg = np.random.default_rng(0).standard_normal((6, V)).astype(np.float32)
+    lg[0, :] = np.nan
+    lg[1, 7] = np.nan
+    lg[1, 9] = 50.0
+    lg[2, :] = -np.inf
+    lg[3, [4, 8]] = [0.0, -0.0]
+    lg[3, :4] = -1
+    lg[3, 5:8] = -1
+    lg[3, 9:] = -1
+    tok = np.array([0, 0, 9, 0, V + 5, -3], dtype=np.int32)
+    tb, par, off = make_batch([tree], 4, gpu)
+    ws = torch.empty(ddt.ddt_accept_walk_workspace(tb, V), dtype=torch.uint8, device=gpu)
+    am = torch.empty(6, dtype=torch.int32, device=gpu)
+    path = torch.empty(1, 6, dtype=torch.int32, device=gpu)
+    L = torch.empty(1, dtype=torch.int32, device=gpu)
+    bonus = torch.empty(1, dtype=torch.int32, device=gpu)
+    ddt.ddt_accept_walk(tb, dev(lg), dev(tok), am, path, L, bonus, ws)
+    torch.cuda.synchronize()
+    ref = oracle.argmax_rows(lg)
+    assert np.array_equal(host(am), ref)
+    assert host(tb.status)[0] == ddt.DDT_ST_TOKEN
+    paths, rL, rb = oracle.accept_walk(par, tok, ref)
+    assert host(L)[0] == rL[0] and host(bonus)[0] == rb[0]

@@ -1,0 +1,172 @@
+"""A whole verify step on the GPU through the C ABI -- plan, conv, gated
+delta-net, attention, accept walk, commit -- checked against the oracle,
+including REPLAY == SELECT bitwise and commit-then-next-step semantics."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tree_verification_ddtree_amd as ddt
+from gpu_util import TOL, banner, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+Hk, Hv, dk, C, W = 2, 4, 128, 256, 4
+Hq, Hkv, D = 12, 2, 256
+V = 5000
+
+
+def build_step(gpu, seed, sizes, T, n_gdn=2, n_attn=1):
+    trees = [synth.random_tree(synth.rng_for(seed, 80, b), s, 10) for b, s in enumerate(sizes)]
+    par, off = synth.concat_trees(trees)
+    n, B = len(par), len(trees)
+    tb = ddt.TreeBatch(par, off, W, gpu)
+    st = dict(trees=trees, par=par, off=off, tb=tb, n=n, B=B, T=np.asarray(T, np.int64))
+    st["gdn"] = [synth.gdn_inputs(seed, (81, l), n, Hk, Hv, dk, dk, "bf16", B=B) for l in range(n_gdn)]
+    st["conv"] = [synth.conv_inputs(seed, (82, l), n, C, W, "bf16", B=B) for l in range(n_gdn)]
+    pt, P = synth.page_layout(seed, (83,), T, sizes)
+    st["pt"] = pt
+    st["kv"] = [synth.kv_pool(seed, (84, l), P, Hkv, D, "f16") for l in range(n_attn)]
+    st["attn"] = [synth.attn_inputs(seed, (85, l), n, Hq, Hkv, D, "f16") for l in range(n_attn)]
+    lg, tok = [], []
+    for b, t in enumerate(trees):
+        l_, t_ = synth.logits_and_draft(seed, (86, b), t, V, "bf16", p_match=0.9)
+        lg.append(l_)
+        tok.append(t_)
+    st["logits"], st["tok"] = np.concatenate(lg), np.concatenate(tok).astype(np.int32)
+    return st
+
+
+def run_step(gpu, st, mode):
+    tb, n, B = st["tb"], st["n"], st["B"]
+    d = {}
+    d["gdn"] = [{k: dev(v) for k, v in g.items()} for g in st["gdn"]]
+    d["conv"] = [{k: dev(v) for k, v in c.items()} for c in st["conv"]]
+    d["kv"] = [(dev(K), dev(Vv)) for K, Vv in st["kv"]]
+    d["attn"] = [{k: dev(v) for k, v in a.items()} for a in st["attn"]]
+    pt = dev(st["pt"])
+    T = dev(st["T"].astype(np.int32))
+    T_max = int(st["T"].max())
+    ddt.ddt_tree_plan(tb, 10)
+    outs = dict(conv=[], gdn=[], attn=[])
+    ns = []
+    for l, (g, c) in enumerate(zip(d["gdn"], d["conv"])):
+        y = torch.empty(n, C, dtype=torch.float32, device=gpu)
+        ddt.ddt_tree_conv(tb, c["x"], c["prefix"], c["w"], 0, y)
+        o = torch.empty(n, Hv, dk, dtype=torch.float32, device=gpu)
+        nsl = torch.empty(n, Hv, dk, dk, dtype=torch.float32, device=gpu) if mode == 1 else None
+        ddt.ddt_tree_gdn(tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"], 1.0, o, nsl)
+        outs["conv"].append(y)
+        outs["gdn"].append(o)
+        ns.append(nsl)
+    ws = torch.empty(ddt.ddt_tree_attn_workspace(tb, Hq, Hkv, D, T_max), dtype=torch.uint8, device=gpu)
+    for (K, Vv), a in zip(d["kv"], d["attn"]):
+        o = torch.empty(n, Hq, D, dtype=torch.float32, device=gpu)
+        ddt.ddt_tree_attn(tb, a["q"], K, Vv, pt, T, T_max, a["Kt"], a["Vt"], o, ws)
+        outs["attn"].append(o)
+    wws = torch.empty(ddt.ddt_accept_walk_workspace(tb, V), dtype=torch.uint8, device=gpu)
+    am = torch.empty(n, dtype=torch.int32, device=gpu)
+    path = torch.empty(B, tb.n_max, dtype=torch.int32, device=gpu)
+    L = torch.empty(B, dtype=torch.int32, device=gpu)
+    bonus = torch.empty(B, dtype=torch.int32, device=gpu)
+    ddt.ddt_accept_walk(tb, dev(st["logits"]), dev(st["tok"]), am, path, L, bonus, wws)
+    gl = [ddt.GdnLayer(g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["alpha"].data_ptr(),
+                       g["beta"].data_ptr(), g["S_c"].data_ptr(),
+                       ns[l].data_ptr() if ns[l] is not None else None,
+                       c["x"].data_ptr(), c["prefix"].data_ptr())
+          for l, (g, c) in enumerate(zip(d["gdn"], d["conv"]))]
+    al = [ddt.AttnLayer(a["Kt"].data_ptr(), a["Vt"].data_ptr(), K.data_ptr(), Vv.data_ptr())
+          for (K, Vv), a in zip(d["kv"], d["attn"])]
+    gt, at = ddt.layer_table(gl, gpu), ddt.layer_table(al, gpu)
+    ddt.ddt_commit_state(tb, path, L, mode, gt, len(gl), Hk, Hv, dk, dk, ddt.DDT_BF16, C, ddt.DDT_BF16,
+                         at, len(al), Hkv, D, ddt.DDT_F16, pt, T)
+    torch.cuda.synchronize()
+    return d, outs, dict(am=host(am), path=host(path), L=host(L), bonus=host(bonus), T=host(T),
+                         status=host(tb.status))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_step_against_oracle(gpu, seed):
+    banner(f"step seed={seed}")
+    sizes = [22, 8, 33]
+    T = [700, 1000, 64]
+    st = build_step(gpu, seed, sizes, T)
+    d, outs, res = run_step(gpu, st, ddt.DDT_COMMIT_REPLAY)
+    par, off = st["par"], st["off"]
+    assert not res["status"].any()
+    for l in range(len(st["gdn"])):
+        c = st["conv"][l]
+        assert rel_err(host(outs["conv"][l]), oracle.tree_conv(par, c["x"], c["prefix"], c["w"], tree_off=off), (0,)) < TOL
+        assert rel_err(host(outs["gdn"][l]), oracle.tree_gdn(par, **st["gdn"][l], tree_off=off), (0, 1)) < TOL
+    for l, ((K, Vv), a) in enumerate(zip(st["kv"], st["attn"])):
+        ref = oracle.tree_attn(par, a["q"], K, Vv, st["T"], a["Kt"], a["Vt"], page_table=st["pt"], tree_off=off)
+        assert rel_err(host(outs["attn"][l]), ref, (0, 1)) < TOL
+    am = oracle.argmax_rows(st["logits"])
+    assert np.array_equal(res["am"], am)
+    paths, L, bonus = oracle.accept_walk(par, st["tok"], am, tree_off=off)
+    assert np.array_equal(res["L"], L) and np.array_equal(res["bonus"], bonus)
+    assert np.array_equal(res["T"], st["T"] + L)
+    # committed state, prefix and cache of every sequence
+    for b in range(st["B"]):
+        pg = [off[b] + j for j in paths[b]]
+        for l in range(len(st["gdn"])):
+            g = st["gdn"][l]
+            S_ref = oracle.commit_gdn_state(g["S_c"], g["q"], g["k"], g["v"], g["alpha"], g["beta"], pg, b)
+            assert rel_err(host(d["gdn"][l]["S_c"])[b], S_ref, (0,)) < TOL
+            c = st["conv"][l]
+            pre = oracle.commit_conv_prefix(c["prefix"], c["x"], pg, b)
+            assert np.array_equal(oracle.num.f64(host(d["conv"][l]["prefix"].view(torch.int16)).view(np.uint16))[b], pre)
+        for l, ((K, Vv), a) in enumerate(zip(st["kv"], st["attn"])):
+            K2, V2, _ = oracle.commit_kv(K, Vv, st["pt"], st["T"], a["Kt"], a["Vt"], pg, b)
+            K, Vv = K2, V2
+            st["kv"][l] = (K, Vv)
+    for l in range(len(st["kv"])):
+        assert np.array_equal(host(d["kv"][l][0]).view(np.uint16), st["kv"][l][0].view(np.uint16))
+        assert np.array_equal(host(d["kv"][l][1]).view(np.uint16), st["kv"][l][1].view(np.uint16))
+
+
+def test_commit_replay_equals_select_bitwise(gpu):
+    banner("commit replay == select")
+    st = build_step(gpu, 3, [22, 64, 5], [300, 40, 999])
+    d1, _, r1 = run_step(gpu, st, ddt.DDT_COMMIT_REPLAY)
+    d2, _, r2 = run_step(gpu, st, ddt.DDT_COMMIT_SELECT)
+    assert np.array_equal(r1["L"], r2["L"]) and (r1["L"] >= 1).all()
+    for l in range(len(st["gdn"])):
+        assert torch.equal(d1["gdn"][l]["S_c"], d2["gdn"][l]["S_c"])
+        assert torch.equal(d1["conv"][l]["prefix"], d2["conv"][l]["prefix"])
+
+
+def test_step_is_deterministic_and_batch_independent(gpu):
+    banner("step determinism / batch independence")
+    st = build_step(gpu, 4, [22, 16], [500, 2000])
+    _, o1, r1 = run_step(gpu, st, 0)
+    _, o2, r2 = run_step(gpu, st, 0)
+    for k in ("conv", "gdn", "attn"):
+        for a, b in zip(o1[k], o2[k]):
+            assert torch.equal(a, b)
+    # sequence 1 alone gives the same outputs as inside the batch
+    solo = build_step(gpu, 4, [22, 16], [500, 2000])
+    o, e = solo["off"][1], solo["off"][2]
+    tree1 = solo["trees"][1]
+    one = dict(solo)
+    one["trees"] = [tree1]
+    one["par"], one["off"] = synth.concat_trees([tree1])
+    one["tb"] = ddt.TreeBatch(one["par"], one["off"], W, gpu)
+    one["n"], one["B"] = len(tree1), 1
+    one["T"] = solo["T"][1:]
+    one["gdn"] = [{k: (v[o:e] if k != "S_c" else v[1:2]) for k, v in g.items()} for g in solo["gdn"]]
+    one["conv"] = [{k: (v[o:e] if k == "x" else (v[1:2] if k == "prefix" else v)) for k, v in c.items()}
+                   for c in solo["conv"]]
+    one["attn"] = [{k: v[o:e] for k, v in a.items()} for a in solo["attn"]]
+    one["pt"] = solo["pt"][1:2]
+    one["logits"], one["tok"] = solo["logits"][o:e], solo["tok"][o:e]
+    _, o3, r3 = run_step(gpu, one, 0)
+    for k in ("conv", "gdn"):
+        for a, b in zip(o1[k], o3[k]):
+            assert torch.equal(a[o:e], b)
+    # attention splits the context by the batch's longest sequence, which
+    # is the same here, so the result is bitwise the same as well
+    for a, b in zip(o1["attn"], o3["attn"]):
+        assert torch.equal(a[o:e], b)
+    assert r3["L"][0] == r1["L"][1]

@@ -1,0 +1,235 @@
+"""ctypes binding of libddtree.so: argument marshalling only.
+
+Every function keeps the name of the C entry point it wraps (include/ddtree.h)
+and passes torch tensors as raw device pointers plus the current HIP stream.
+Nothing here computes any part of the verify step; if the library is
+missing, loading fails loudly.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libddtree.so")
+
+DDT_F32, DDT_F16, DDT_BF16 = 0, 1, 2
+DDT_COMMIT_REPLAY, DDT_COMMIT_SELECT = 0, 1
+DDT_ST_TREE, DDT_ST_LEVELS, DDT_ST_TOKEN, DDT_ST_ARGMAX, DDT_ST_CTX, DDT_ST_COMMIT = 1, 2, 4, 8, 16, 32
+DDT_PAGE = 16
+DDT_MAX_NODES = 64
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("B", _i32), ("n_total", _i32), ("n_max", _i32), ("W", _i32),
+                ("tree_off", _vp), ("parent", _vp), ("depth", _vp), ("anc", _vp),
+                ("win", _vp), ("order", _vp), ("slot", _vp), ("status", _vp)]
+
+
+class GdnLayer(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("alpha", _vp), ("beta", _vp),
+                ("S_c", _vp), ("node_states", _vp), ("x", _vp), ("prefix", _vp)]
+
+
+class AttnLayer(ctypes.Structure):
+    _fields_ = [("Kt", _vp), ("Vt", _vp), ("Kc", _vp), ("Vc", _vp)]
+
+
+class DDTError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {code} ({status_str(code)})")
+        self.code = code
+
+
+_SIGS = {
+    "ddt_version": ([], _i32),
+    "ddt_status_str": ([_i32], ctypes.c_char_p),
+    "ddt_plan_slots": ([_i32], _i32),
+    "ddt_tree_plan_host": ([ctypes.POINTER(Plan), _i32], _i32),
+    "ddt_tree_plan": ([ctypes.POINTER(Plan), _i32, _vp], _i32),
+    "ddt_tree_conv": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
+    "ddt_tree_gdn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                      _f32, _i32, _vp, _vp, _vp], _i32),
+    "ddt_tree_attn_workspace": ([ctypes.POINTER(Plan), _i32, _i32, _i32, _i32, _i32], _sz),
+    "ddt_tree_attn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
+                       _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
+    "ddt_accept_walk_workspace": ([ctypes.POINTER(Plan), _i32], _sz),
+    "ddt_accept_walk": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                         _vp], _i32),
+    "ddt_commit_state": ([ctypes.POINTER(Plan), _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                          _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp], _i32),
+}
+
+_LIB = None
+
+
+def lib():
+    """The loaded libddtree.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python -m tree_verification_ddtree_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _LIB = L
+    return _LIB
+
+
+def status_str(code):
+    return lib().ddt_status_str(int(code)).decode()
+
+
+def _check(code, what):
+    if code != 0:
+        raise DDTError(code, what)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor / ndarray, None for None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dtype_code(t):
+    import torch
+    return {torch.float32: DDT_F32, torch.float16: DDT_F16, torch.bfloat16: DDT_BF16}[t.dtype]
+
+
+def plan_struct(B, n_total, n_max, W, tree_off, parent, depth, anc, win, order, slot, status):
+    """Fill a Plan from tensors / arrays (device for ddt_tree_plan, host for
+    ddt_tree_plan_host)."""
+    return Plan(B, n_total, n_max, W, *[_ptr(x) for x in
+                                         (tree_off, parent, depth, anc, win, order, slot, status)])
+
+
+class TreeBatch:
+    """Device buffers of one step's plan: parent/tree_off inputs and every
+    output array of ddt_tree_plan, sized per include/ddtree.h."""
+
+    def __init__(self, parent, tree_off, W, device, n_max=None):
+        import torch
+        parent = np.asarray(parent, dtype=np.int32)
+        tree_off = np.asarray(tree_off, dtype=np.int32)
+        self.B = len(tree_off) - 1
+        self.n_total = int(tree_off[-1])
+        sizes = np.diff(tree_off)
+        self.n_max = int(n_max if n_max is not None else max(1, int(sizes.max())))
+        self.W = int(W)
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.parent = torch.tensor(parent, **i32)
+        self.tree_off = torch.tensor(tree_off, **i32)
+        n = max(self.n_total, 1)
+        self.depth = torch.zeros(n, **i32)
+        self.anc = torch.zeros(n, dtype=torch.int64, device=dev)
+        self.win = torch.zeros(n * max(self.W - 1, 1), **i32)
+        self.order = torch.zeros(n, **i32)
+        self.slot = torch.zeros(n, **i32)
+        self.status = torch.zeros(self.B, **i32)
+        self.struct = plan_struct(self.B, self.n_total, self.n_max, self.W, self.tree_off,
+                                  self.parent, self.depth, self.anc, self.win, self.order,
+                                  self.slot, self.status)
+
+
+def _plan(p):
+    return ctypes.byref(p.struct if isinstance(p, TreeBatch) else p)
+
+
+# ------------------------------------------------------------------ entry points
+def ddt_version():
+    return lib().ddt_version()
+
+
+def ddt_plan_slots(n_max):
+    return lib().ddt_plan_slots(int(n_max))
+
+
+def ddt_tree_plan_host(plan_struct_host, max_levels):
+    """Returns the status code (no raise): host-side validation is the point."""
+    return lib().ddt_tree_plan_host(ctypes.byref(plan_struct_host), int(max_levels))
+
+
+def ddt_tree_plan(plan, max_levels, stream=None):
+    _check(lib().ddt_tree_plan(_plan(plan), int(max_levels), _stream(stream)), "ddt_tree_plan")
+
+
+def ddt_tree_conv(plan, x, prefix, w, act, y, stream=None):
+    _check(lib().ddt_tree_conv(_plan(plan), _ptr(x), _ptr(prefix), _ptr(w), int(x.shape[-1]),
+                               int(act), dtype_code(x), _ptr(y), _stream(stream)), "ddt_tree_conv")
+
+
+def ddt_tree_gdn(plan, q, k, v, alpha, beta, S_c, scale, out, node_states=None, stream=None):
+    Hk, dk = int(q.shape[1]), int(q.shape[2])
+    Hv, dv = int(v.shape[1]), int(v.shape[2])
+    _check(lib().ddt_tree_gdn(_plan(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                              _ptr(S_c), Hk, Hv, dk, dv, float(scale), dtype_code(q), _ptr(out),
+                              _ptr(node_states), _stream(stream)), "ddt_tree_gdn")
+
+
+def ddt_tree_attn_workspace(plan, Hq, Hkv, D, T_max, n_splits=0):
+    return lib().ddt_tree_attn_workspace(_plan(plan), int(Hq), int(Hkv), int(D), int(T_max),
+                                         int(n_splits))
+
+
+def ddt_tree_attn(plan, q, Kc, Vc, page_table, T, T_max, Kt, Vt, out, ws, scale=None,
+                  n_splits=0, stream=None):
+    Hq, D = int(q.shape[1]), int(q.shape[2])
+    Hkv = int(Kt.shape[1])
+    max_pages = int(page_table.shape[1]) if page_table is not None else 0
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(D))
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().ddt_tree_attn(_plan(plan), _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(page_table),
+                               max_pages, _ptr(T), int(T_max), _ptr(Kt), _ptr(Vt), Hq, Hkv, D,
+                               scale, dtype_code(q), int(n_splits), _ptr(out), _ptr(ws), wsb,
+                               _stream(stream)), "ddt_tree_attn")
+
+
+def ddt_accept_walk_workspace(plan, V):
+    return lib().ddt_accept_walk_workspace(_plan(plan), int(V))
+
+
+def ddt_accept_walk(plan, logits, draft_tok, argmax, path, L, bonus, ws, stream=None):
+    V = int(logits.shape[-1])
+    wsb = ws.numel() * ws.element_size()
+    _check(lib().ddt_accept_walk(_plan(plan), _ptr(logits), dtype_code(logits), V,
+                                 _ptr(draft_tok), _ptr(argmax), _ptr(path), _ptr(L), _ptr(bonus),
+                                 _ptr(ws), wsb, _stream(stream)), "ddt_accept_walk")
+
+
+def layer_table(structs, device):
+    """Copy an array of GdnLayer / AttnLayer structs to device memory (uint8 tensor)."""
+    import torch
+    if not structs:
+        return None
+    arr = (type(structs[0]) * len(structs))(*structs)
+    host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return host.to(device)
+
+
+def ddt_commit_state(plan, path, L, mode, gdn_table, n_gdn, Hk, Hv, dk, dv, gdn_dtype, C,
+                     conv_dtype, attn_table, n_attn, Hkv, D, kv_dtype, page_table, T,
+                     stream=None):
+    max_pages = int(page_table.shape[1]) if page_table is not None else 0
+    _check(lib().ddt_commit_state(_plan(plan), _ptr(path), _ptr(L), int(mode), _ptr(gdn_table),
+                                  int(n_gdn), int(Hk), int(Hv), int(dk), int(dv), int(gdn_dtype),
+                                  int(C), int(conv_dtype), _ptr(attn_table), int(n_attn),
+                                  int(Hkv), int(D), int(kv_dtype), _ptr(page_table), max_pages,
+                                  _ptr(T), _stream(stream)), "ddt_commit_state")

@@ -1,0 +1,59 @@
+"""Build libddtree.so (HIP, gfx950) in place: one object per source, then link.
+
+    python -m tree_verification_ddtree_amd.build [--jobs N]
+"""
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libddtree.so")
+SOURCES = ["plan.hip", "conv.hip", "gdn.hip", "attn.hip", "walk.hip", "commit.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+    "-I" + os.path.join(ROOT, "include"),
+    # packed fp32 math off (v_pk_*_f32): only plain fp32 VALU ops are emitted
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _compile(src):
+    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{msgs}")
+    return obj, msgs
+
+
+def build(jobs=None, verbose=False):
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        res = list(ex.map(_compile, SOURCES))
+    for _, m in res:
+        if m.strip() and verbose:
+            print(m)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in res]]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(a.jobs, a.verbose))
+    sys.exit(0)

@@ -1,0 +1,634 @@
+// a4: tree-masked attention over a paged fp16 KV cache.
+//
+// Each tree node attends to all committed tokens of its sequence and to the
+// draft tokens on its own root path (the whole tree is verified in one pass:
+// lucebox-hub README, "02 · DFlash DDtree", "Algorithms used"); attention is
+// full (codehub lucebox-hub@main, "Server flags", --fa-window 0) and the
+// cache may be paged (Luce-Org/lucebox README, "Inference Engine
+// Optimizations").  The pages call the verify step bandwidth bound
+// (lucebox-hub README, "Retune per GPU"; "AMD Strix Halo (HIP backend)").
+//
+// Design for gfx950.  All G = Hq/Hkv query heads of all n tree nodes share
+// one KV head, so a workgroup owns one KV head, one context split and up to
+// 192 query rows (row = node * G + head): every K/V byte is read from HBM
+// once per split and feeds 6*n rows (132 at budget 22).
+//  - Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_16x16x32_f16: A = 16 keys x 32 channels (from LDS),
+//    B = 32 channels x 16 rows (Q, resident in VGPRs for the whole split).
+//    The accumulator then holds, per lane, 4 keys of ONE query row, so the
+//    online-softmax statistics of a row live in one lane (replicated over
+//    the 4 lane groups) and the probabilities are already in the B-operand
+//    layout of the next product: O^T += V^T P^T (A = 16 channels x 32 keys
+//    of V^T from LDS, B = P).  Keys are permuted inside a 32-key tile so
+//    that lane group q holds keys 8q..8q+7 -- exactly the 8 consecutive
+//    tokens that one 16-byte read of a channel-major V page provides.
+//  - K and V pages go straight from HBM into a 3-stage LDS ring
+//    (global_load_lds_dwordx4, two 32-key tiles in flight, no staging
+//    registers); 16-byte chunks are XOR-swizzled so the operand reads of a
+//    wavefront hit distinct banks.  The ragged last tile and the tree tiles
+//    go through registers so keys past the end can be zero-filled.
+//  - Rows: 16-row blocks are dealt round-robin to the 4 wavefronts (NB
+//    blocks each).  A wavefront skips blocks past the sequence's rows.
+//  - The tree itself is one or two extra 32-key tiles (draft K/V of up to
+//    64 nodes) processed by the last split of the sequence, masked by the
+//    plan's ancestor bitmask; cache keys are never masked per row.
+//  - Online softmax without rescaling the accumulators: a row's reference
+//    max is fixed by its first tile and probabilities are formed against
+//    it (fp16 P has 15 binades of headroom above 1).  A split whose scores
+//    outgrow that headroom is recomputed with the true maxima, so the
+//    result is exact either way; on ordinary data the redo never happens.
+//  - Each split writes unnormalised partial O^T, its reference max and the
+//    row sum; a combine kernel merges the splits in fixed order
+//    (deterministic, no atomics).
+#include "common.h"
+
+namespace ddt {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TILE = 32;  // keys per pipeline stage (two pages)
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct AttnArgs {
+  ddt_plan P;
+  const _Float16 *q, *Kc, *Vc, *Kt, *Vt;
+  const int32_t *pt;
+  int max_pages;
+  const int32_t *T;
+  int T_max;
+  int Hq, Hkv, G;
+  float c;  // scale * log2(e)
+  int chunk, n_splits, n_rg, rows_wg;
+  float *Opart;  // [B][Hkv][n_rg][n_splits][rows_wg][D]
+  float2 *ML;    // [B][Hkv][n_rg][n_splits][rows_wg]
+  float *out;    // [n_total][Hq][D]
+};
+
+// committed length actually readable for sequence b (and whether it was cut)
+__device__ __forceinline__ int ctx_len(const AttnArgs &A, int b, bool *cut) {
+  int t = A.T[b];
+  bool bad = false;
+  if (t < 0) { t = 0; bad = true; }
+  if (t > A.T_max) { t = A.T_max; bad = true; }
+  if (A.pt && t > A.max_pages * DDT_PAGE) { t = A.max_pages * DDT_PAGE; bad = true; }
+  if (cut) *cut = bad;
+  return t;
+}
+
+__device__ __forceinline__ int n_active_splits(const AttnArgs &A, int Tb) {
+  int n = (Tb + A.chunk - 1) / A.chunk;
+  n = n < 1 ? 1 : n;
+  return n > A.n_splits ? A.n_splits : n;
+}
+
+template <int D>
+struct Lds {
+  // K stage: [32 rows][D] halves; row r = 16*tt + m holds the key that the
+  // score MFMA of key-half tt reads as A-row m; the 16-byte chunk c of a row
+  // sits at chunk position c ^ (r & 7).
+  // V stage: [D channels][4 groups][8 keys] halves; group q of channel d
+  // sits at slot q ^ ((d >> 1) & 3).
+  static constexpr int K_HALVES = TILE * D;
+  static constexpr int V_HALVES = TILE * D;
+  static constexpr int STAGE = K_HALVES + V_HALVES;
+};
+constexpr int NSTAGE = 3;
+
+// tile-local key tau (0..31) <-> K row in LDS
+__device__ __forceinline__ int krow_of(int tau) {
+  return 16 * ((tau >> 2) & 1) + 4 * (tau >> 3) + (tau & 3);
+}
+__device__ __forceinline__ int key_of_krow(int r) {
+  const int tt = r >> 4, m = r & 15;
+  return 8 * (m >> 2) + 4 * tt + (m & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int NB>
+__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
+  constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  constexpr int WAVE_CH = (TILE * CPR) / 256;  // direct loads per wave, per tensor and tile
+  constexpr int KS = D / 32;               // k-steps of the score product
+  constexpr int DB = D / 16;               // channel blocks of the value product
+  extern __shared__ half8 lds_raw[];
+  _Float16 *lds = reinterpret_cast<_Float16 *>(lds_raw);
+
+  const int split = blockIdx.x, g = blockIdx.y;
+  const int b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
+  const Seq s = seq_of(A.P, b);
+  const int rows_b = A.G * s.n;
+  const int row0 = rg * A.rows_wg;
+  if (row0 >= rows_b) return;
+  bool cut;
+  const int Tb = ctx_len(A, b, &cut);
+  const int nsp = n_active_splits(A, Tb);
+  if (split >= nsp) return;
+  if (cut && split == 0 && g == 0 && rg == 0 && threadIdx.x == 0) A.P.status[b] |= DDT_ST_CTX;
+
+  const int t_beg = split * A.chunk;
+  const int t_end = min(Tb, t_beg + A.chunk);
+  const int n_keys = t_end > t_beg ? t_end - t_beg : 0;
+  const int n_full = n_keys / TILE;                      // direct-load tiles
+  const bool has_part = (n_keys % TILE) != 0;            // ragged last cache tile
+  const int n_tree = (split == nsp - 1) ? (s.n + TILE - 1) / TILE : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lq = lane >> 4;
+
+  // ---- resident Q fragments and per-row tree masks
+  half8 qf[NB][KS];
+  unsigned long long ancr[NB];
+  bool blk_on[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int blk0 = row0 + 16 * (w + 4 * j);
+    blk_on[j] = blk0 < rows_b;
+    const int rho = blk0 + l16;
+    const bool ok = rho < rows_b;
+    const int node = ok ? rho / A.G : 0;
+    const int hq = g * A.G + (ok ? rho % A.G : 0);
+    ancr[j] = ok ? A.P.anc[s.o + node] : 0ull;
+    const _Float16 *qp = A.q + ((size_t)(s.o + node) * A.Hq + hq) * D + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ok)
+        qf[j][ks] = *reinterpret_cast<const half8 *>(qp + 32 * ks);
+      else
+        qf[j][ks] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  f32x4 o[NB][DB];
+  float mrow[NB], mseen[NB], lsum[NB];
+  bool ovf = false;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) mrow[j] = -INFINITY;
+
+  auto page_of = [&](int t) -> int {
+    return A.pt ? A.pt[(size_t)b * A.max_pages + (t >> 4)] : (t >> 4);
+  };
+  const size_t kv_head = (size_t)g;
+
+  // ---- full cache tile -> LDS stage, straight from HBM (global_load_lds).
+  // Wave w fills 1 KB pieces w, w+4, ...; lane l of a piece lands at byte
+  // 16*l, so each lane fetches whichever chunk belongs there.
+  auto issue_tile = [&](int it, int stage) {
+    const int t0 = t_beg + it * TILE;
+    const int pg0 = page_of(t0), pg1 = page_of(t0 + 16);
+    _Float16 *Ks = lds + stage * Lds<D>::STAGE;
+    _Float16 *Vs = Ks + Lds<D>::K_HALVES;
+#pragma unroll
+    for (int k = 0; k < WAVE_CH; ++k) {
+      const int piece = w + 4 * k;
+      const int P = piece * 64 + lane;       // chunk position in the stage
+      const int r = P / CPR, cpos = P % CPR;  // K row and chunk slot
+      const int cc = cpos ^ (r & 7);
+      const int tau = key_of_krow(r);
+      const int pg = tau < 16 ? pg0 : pg1;
+      const _Float16 *src = A.Kc + (((size_t)pg * A.Hkv + kv_head) * DDT_PAGE + (tau & 15)) * D + 8 * cc;
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Ks + piece * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < WAVE_CH; ++k) {
+      const int piece = w + 4 * k;
+      const int P = piece * 64 + lane;
+      const int d = P >> 2, slot = P & 3;
+      const int qg = slot ^ ((d >> 1) & 3);
+      const int pg = (qg >> 1) ? pg1 : pg0;
+      const _Float16 *src = A.Vc + (((size_t)pg * A.Hkv + kv_head) * D + d) * DDT_PAGE + 8 * (qg & 1);
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Vs + piece * 512), 16, 0, 0);
+    }
+  };
+
+  // ---- ragged cache tile or tree tile -> LDS stage through registers,
+  // zero-filling keys past the end (unwritten cache slots may hold NaN).
+  auto fill_tile = [&](bool tree, int kbase, int stage) {
+    _Float16 *Ks = lds + stage * Lds<D>::STAGE;
+    _Float16 *Vs = Ks + Lds<D>::K_HALVES;
+    for (int ci = tid; ci < TILE * CPR; ci += 256) {
+      const int tau = ci / CPR, cc = ci % CPR;
+      const int key = kbase + tau;
+      uint4 kx = make_uint4(0, 0, 0, 0);
+      half8 vx = half8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (tree) {
+        if (key < s.n) {
+          const size_t src = ((size_t)(s.o + key) * A.Hkv + kv_head) * D + 8 * cc;
+          kx = *reinterpret_cast<const uint4 *>(A.Kt + src);
+          vx = *reinterpret_cast<const half8 *>(A.Vt + src);
+        }
+      } else if (key < t_end) {
+        const size_t pg = (size_t)page_of(key) * A.Hkv + kv_head;
+        kx = *reinterpret_cast<const uint4 *>(A.Kc + (pg * DDT_PAGE + (key & 15)) * D + 8 * cc);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) vx[x] = A.Vc[(pg * D + 8 * cc + x) * DDT_PAGE + (key & 15)];
+      }
+      const int r = krow_of(tau);
+      *reinterpret_cast<uint4 *>(Ks + r * D + 8 * (cc ^ (r & 7))) = kx;
+      const int qg = tau >> 3, e = tau & 7;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int d = 8 * cc + x;
+        Vs[d * 32 + 8 * (qg ^ ((d >> 1) & 3)) + e] = vx[x];
+      }
+    }
+  };
+
+  // ---- one 32-key tile: scores, online softmax, value product
+  auto compute_tile = [&](int stage, bool tree, int kbase) {
+    const _Float16 *Ks = lds + stage * Lds<D>::STAGE;
+    const _Float16 *Vs = Ks + Lds<D>::K_HALVES;
+    f32x4 acc[2][NB];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int r = 16 * tt + l16;
+        const int cc = 4 * ks + lq;
+        const half8 kf = *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ (r & 7)));
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (blk_on[j]) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[j][ks], acc[tt][j], 0, 0, 0);
+      }
+    }
+    // this lane holds keys kbase + 8*lq + e (e = 4*tt + i) of row l16
+    half8 pf[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (!blk_on[j]) continue;
+      float sv[8];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kbase + 8 * lq + e;
+        const bool valid = tree ? (key < s.n && ((ancr[j] >> key) & 1ull)) : (key < t_end);
+        sv[e] = valid ? acc[e >> 2][j][e & 3] : -INFINITY;
+        mloc = fmaxf(mloc, sv[e]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      // the row's reference max is its first finite tile max; later tiles
+      // may exceed it by up to 2^15 in probability (fp16 P keeps range),
+      // beyond that the split is redone with the true max
+      if (mrow[j] == -INFINITY) mrow[j] = mloc;
+      mseen[j] = fmaxf(mseen[j], mloc);
+      ovf |= (mloc - mrow[j]) * A.c > 15.0f;
+      const float mc = mrow[j] * A.c;
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = (mrow[j] == -INFINITY) ? 0.f : exp2f(fmaf(sv[e], A.c, -mc));  // masked: exp2(-inf) = 0
+        ps += p[e];
+      }
+      lsum[j] += ps;
+      pf[j] = half8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                    (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+    }
+#pragma unroll
+    for (int n = 0; n < DB; ++n) {
+      const int d = 16 * n + l16;
+      const half8 vf = *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ ((d >> 1) & 3)));
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (blk_on[j]) o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[j], o[j][n], 0, 0, 0);
+    }
+  };
+
+  // The split normally runs once.  If some score exceeded its row's
+  // reference by more than fp16 P can hold, it runs again with every
+  // reference set to the true maximum seen, which cannot overflow.
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      mseen[j] = -INFINITY;
+      lsum[j] = 0.f;
+#pragma unroll
+      for (int n = 0; n < DB; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // ---- main loop: full tiles through a 3-stage ring, two tiles in flight
+    if (n_full > 0) issue_tile(0, 0);
+    if (n_full > 1) issue_tile(1, 1);
+    for (int it = 0; it < n_full; ++it) {
+      if (it + 1 < n_full)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // tile it landed for every wave; stage (it+2)%3 is free
+      if (it + 2 < n_full) issue_tile(it + 2, (it + 2) % NSTAGE);
+      compute_tile(it % NSTAGE, false, t_beg + it * TILE);
+    }
+    // ---- epilogue: ragged cache tile, then the tree tiles
+    const int n_ep = (has_part ? 1 : 0) + n_tree;
+    for (int e = 0; e < n_ep; ++e) {
+      const bool tree = !(has_part && e == 0);
+      const int kbase = tree ? (e - (has_part ? 1 : 0)) * TILE : t_beg + n_full * TILE;
+      __syncthreads();  // the stage is no longer read
+      fill_tile(tree, kbase, 0);
+      __syncthreads();
+      compute_tile(0, tree, kbase);
+    }
+    if (!__syncthreads_or(ovf)) break;
+    ovf = false;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) mrow[j] = mseen[j];
+  }
+
+  // ---- partial results of this split
+  const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits + split) * A.rows_wg;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (!blk_on[j]) continue;
+    float l = lsum[j];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int rl = 16 * (w + 4 * j) + l16;  // row within the workgroup
+    if (row0 + rl >= rows_b) continue;
+    if (lq == 0) A.ML[base + rl] = make_float2(mrow[j], l);
+    float *op = A.Opart + (base + rl) * D + 4 * lq;
+#pragma unroll
+    for (int n = 0; n < DB; ++n)
+      *reinterpret_cast<float4 *>(op + 16 * n) = make_float4(o[j][n][0], o[j][n][1], o[j][n][2], o[j][n][3]);
+  }
+}
+
+// Merge the splits of one query row: one workgroup per row.  The split
+// weights 2^((m_s - M) c) go to LDS, then each thread sums 4 channels over a
+// strided subset of the splits and the subsets are added in a fixed order.
+constexpr int MAX_SPLITS = 1024;
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
+  constexpr int TPR = D / 4;        // threads per channel sweep
+  constexpr int SG = 256 / TPR;     // split groups
+  __shared__ float wts[MAX_SPLITS];
+  __shared__ float red[256];
+  __shared__ float4 part[SG][TPR];
+  const int rl = blockIdx.x, g = blockIdx.y, b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
+  const Seq s = seq_of(A.P, b);
+  const int rho = rg * A.rows_wg + rl;
+  if (rho >= A.G * s.n) return;
+  const int tid = threadIdx.x;
+  const int nsp = n_active_splits(A, ctx_len(A, b, nullptr));
+  const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
+  float m = -INFINITY;
+  for (int sp = tid; sp < nsp; sp += 256) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
+  red[tid] = m;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float l = 0.f;
+  for (int sp = tid; sp < nsp; sp += 256) {
+    const float2 ml = A.ML[base + (size_t)sp * A.rows_wg];
+    const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f((ml.x - M) * A.c);
+    wts[sp] = wgt;
+    l = fmaf(ml.y, wgt, l);
+  }
+  red[tid] = l;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (tid < k) red[tid] += red[tid + k];
+    __syncthreads();
+  }
+  const float L = red[0];
+  const int dc = tid % TPR, sg = tid / TPR;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int sp = sg; sp < nsp; sp += SG) {
+    const float wgt = wts[sp];
+    const float4 v = *reinterpret_cast<const float4 *>(A.Opart + (base + (size_t)sp * A.rows_wg) * D + 4 * dc);
+    acc.x = fmaf(v.x, wgt, acc.x);
+    acc.y = fmaf(v.y, wgt, acc.y);
+    acc.z = fmaf(v.z, wgt, acc.z);
+    acc.w = fmaf(v.w, wgt, acc.w);
+  }
+  part[sg][dc] = acc;
+  __syncthreads();
+  if (sg == 0) {
+    for (int k = 1; k < SG; ++k) {
+      const float4 v = part[k][dc];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const float inv = 1.f / L;
+    const int node = rho / A.G, hq = g * A.G + rho % A.G;
+    *reinterpret_cast<float4 *>(A.out + ((size_t)(s.o + node) * A.Hq + hq) * D + 4 * dc) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+}
+
+// Small head dims (D <= 64) and fp32 caches: one workgroup per (node, q
+// head); each thread keeps an online softmax over a strided subset of the
+// keys, then the 64 partial states are merged in LDS.
+template <typename E, int D>
+__global__ __launch_bounds__(64) void attn_small_kernel(ddt_plan P, const E *__restrict__ q,
+                                                        const E *__restrict__ Kc,
+                                                        const E *__restrict__ Vc,
+                                                        const int32_t *pt, int max_pages,
+                                                        const int32_t *T, int T_max,
+                                                        const E *__restrict__ Kt,
+                                                        const E *__restrict__ Vt, int Hq, int Hkv,
+                                                        float scale, float *__restrict__ out) {
+  const int hq = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const Seq s = seq_of(P, b);
+  if (i >= s.n) return;
+  const int g = hq / (Hq / Hkv), gi = s.o + i;
+  int Tb = T[b];
+  bool cut = false;
+  if (Tb < 0) { Tb = 0; cut = true; }
+  if (Tb > T_max) { Tb = T_max; cut = true; }
+  if (pt && Tb > max_pages * DDT_PAGE) { Tb = max_pages * DDT_PAGE; cut = true; }
+  if (cut && hq == 0 && i == 0 && threadIdx.x == 0) P.status[b] |= DDT_ST_CTX;
+  float qv[D];
+  for (int d = 0; d < D; ++d) qv[d] = (float)q[((size_t)gi * Hq + hq) * D + d];
+  const unsigned long long anc = P.anc[gi];
+  float m = -INFINITY, l = 0.f, acc[D];
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  const int nkeys = Tb + s.n;
+  for (int key = threadIdx.x; key < nkeys; key += 64) {
+    const E *kp, *vp;
+    int vstride;
+    if (key < Tb) {
+      const int page = pt ? pt[(size_t)b * max_pages + key / DDT_PAGE] : key / DDT_PAGE;
+      const size_t pg = (size_t)page * Hkv + g;
+      kp = Kc + (pg * DDT_PAGE + key % DDT_PAGE) * D;
+      vp = Vc + pg * D * DDT_PAGE + key % DDT_PAGE;
+      vstride = DDT_PAGE;
+    } else {
+      const int j = key - Tb;
+      if (!((anc >> j) & 1ull)) continue;
+      kp = Kt + ((size_t)(s.o + j) * Hkv + g) * D;
+      vp = Vt + ((size_t)(s.o + j) * Hkv + g) * D;
+      vstride = 1;
+    }
+    float sc = 0.f;
+    for (int d = 0; d < D; ++d) sc = fmaf(qv[d], (float)kp[d], sc);
+    sc *= scale;
+    const float mn = fmaxf(m, sc);
+    const float corr = __expf(m - mn), p = __expf(sc - mn);
+    l = l * corr + p;
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], corr, p * (float)vp[d * vstride]);
+    m = mn;
+  }
+  __shared__ float sm[64], sl[64], so[64][D + 1];
+  sm[threadIdx.x] = m;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int t = 0; t < 64; ++t) M = fmaxf(M, sm[t]);
+  const float wgt = (m == -INFINITY) ? 0.f : __expf(m - M);
+  sl[threadIdx.x] = l * wgt;
+  for (int d = 0; d < D; ++d) so[threadIdx.x][d] = acc[d] * wgt;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float L = 0.f, O = 0.f;
+    for (int t = 0; t < 64; ++t) {
+      L += sl[t];
+      O += so[t][threadIdx.x];
+    }
+    out[((size_t)gi * Hq + hq) * D + threadIdx.x] = O / L;
+  }
+}
+
+int check_plan(const ddt_plan *P);
+
+struct Cfg {
+  bool mfma;
+  int nb, rows_wg, n_rg, n_splits, chunk;
+};
+
+static Cfg attn_cfg(const ddt_plan *P, int Hq, int Hkv, int D, int T_max, int n_splits, int dtype) {
+  Cfg c{};
+  const int G = Hq / Hkv;
+  c.mfma = (dtype == DDT_F16) && (D == 128 || D == 256);
+  if (!c.mfma) return c;
+  const int rows = G * P->n_max;
+  const int blocks = (rows + 15) / 16;
+  c.nb = (blocks + 3) / 4;
+  if (c.nb > 3) c.nb = 3;
+  c.rows_wg = 64 * c.nb;
+  c.n_rg = (rows + c.rows_wg - 1) / c.rows_wg;
+  int tmax = T_max > 0 ? T_max : 1;
+  if (n_splits <= 0) {
+    // about one workgroup per compute unit over the whole batch
+    const long long units = (long long)P->B * Hkv * c.n_rg;
+    long long want = (256 + units - 1) / units;
+    long long by_len = (tmax + 255) / 256;  // keep splits >= 256 keys
+    n_splits = (int)(want < by_len ? want : by_len);
+    if (n_splits < 1) n_splits = 1;
+  }
+  int chunk = (tmax + n_splits - 1) / n_splits;
+  chunk = (chunk + TILE - 1) / TILE * TILE;
+  c.chunk = chunk;
+  c.n_splits = (tmax + chunk - 1) / chunk;
+  if (c.n_splits < 1) c.n_splits = 1;
+  if (c.n_splits > MAX_SPLITS) {  // the combine keeps one weight per split in LDS
+    chunk = (tmax + MAX_SPLITS - 1) / MAX_SPLITS;
+    c.chunk = chunk = (chunk + TILE - 1) / TILE * TILE;
+    c.n_splits = (tmax + chunk - 1) / chunk;
+  }
+  return c;
+}
+
+}  // namespace ddt
+
+using namespace ddt;
+
+extern "C" size_t ddt_tree_attn_workspace(const ddt_plan *P, int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t T_max, int32_t n_splits) {
+  if (!P || Hkv < 1 || Hq < Hkv || Hq % Hkv || D < 1) return 0;
+  Cfg c = attn_cfg(P, Hq, Hkv, D, T_max, n_splits, DDT_F16);
+  if (!c.mfma) return 0;
+  const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
+  return rows * (size_t)D * sizeof(float) + rows * sizeof(float2);
+}
+
+extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, const void *Vc,
+                             const int32_t *page_table, int32_t max_pages, const int32_t *T,
+                             int32_t T_max, const void *Kt, const void *Vt, int32_t Hq,
+                             int32_t Hkv, int32_t D, float scale, int32_t dtype,
+                             int32_t n_splits, float *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  int r = check_plan(P);
+  if (r) return r;
+  if (!q || !Kc || !Vc || !T || !Kt || !Vt || !out) return DDT_E_ARG;
+  if (!page_table && P->B != 1) return DDT_E_ARG;
+  if (page_table && max_pages < 1) return DDT_E_SHAPE;
+  if (Hkv < 1 || Hq < Hkv || Hq % Hkv) return DDT_E_SHAPE;
+  if (T_max < 0 || n_splits < 0) return DDT_E_RANGE;
+  if (dtype != DDT_F16 && dtype != DDT_F32) return DDT_E_DTYPE;
+  hipStream_t st = (hipStream_t)stream;
+  Cfg c = attn_cfg(P, Hq, Hkv, D, T_max, n_splits, dtype);
+  if (!c.mfma) {
+    if (D != 16 && D != 32 && D != 64) return DDT_E_SHAPE;
+    dim3 grid(Hq, P->n_max, P->B);
+#define DDT_SMALL(E, DD)                                                                          \
+  hipLaunchKernelGGL((attn_small_kernel<E, DD>), grid, dim3(64), 0, st, *P, (const E *)q,         \
+                     (const E *)Kc, (const E *)Vc, page_table, max_pages, T, T_max, (const E *)Kt, \
+                     (const E *)Vt, Hq, Hkv, scale, out)
+    if (dtype == DDT_F32) {
+      if (D == 16) DDT_SMALL(float, 16); else if (D == 32) DDT_SMALL(float, 32); else DDT_SMALL(float, 64);
+    } else {
+      if (D == 16) DDT_SMALL(_Float16, 16); else if (D == 32) DDT_SMALL(_Float16, 32); else DDT_SMALL(_Float16, 64);
+    }
+#undef DDT_SMALL
+    return launch_status();
+  }
+  if (!ws || ws_bytes < ddt_tree_attn_workspace(P, Hq, Hkv, D, T_max, n_splits)) return DDT_E_WS;
+  AttnArgs A{};
+  A.P = *P;
+  A.q = (const _Float16 *)q;
+  A.Kc = (const _Float16 *)Kc;
+  A.Vc = (const _Float16 *)Vc;
+  A.Kt = (const _Float16 *)Kt;
+  A.Vt = (const _Float16 *)Vt;
+  A.pt = page_table;
+  A.max_pages = max_pages;
+  A.T = T;
+  A.T_max = T_max;
+  A.Hq = Hq;
+  A.Hkv = Hkv;
+  A.G = Hq / Hkv;
+  A.c = scale * LOG2E;
+  A.chunk = c.chunk;
+  A.n_splits = c.n_splits;
+  A.n_rg = c.n_rg;
+  A.rows_wg = c.rows_wg;
+  const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
+  A.Opart = (float *)ws;
+  A.ML = (float2 *)((char *)ws + rows * D * sizeof(float));
+  A.out = out;
+  dim3 grid(c.n_splits, Hkv, P->B * c.n_rg);
+  const size_t lds = (size_t)NSTAGE * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
+#define DDT_ATTN(DD, NBB)                                                                       \
+  do {                                                                                          \
+    hipError_t e_ = hipFuncSetAttribute((const void *)attn_mfma_kernel<DD, NBB>,                \
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+    if (e_ != hipSuccess) {                                                                     \
+      set_hip_error(e_);                                                                        \
+      return DDT_E_HIP;                                                                         \
+    }                                                                                           \
+    hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB>), grid, dim3(256), lds, st, A);               \
+  } while (0)
+  if (D == 256) {
+    if (c.nb == 1) DDT_ATTN(256, 1); else if (c.nb == 2) DDT_ATTN(256, 2); else DDT_ATTN(256, 3);
+  } else {
+    if (c.nb == 1) DDT_ATTN(128, 1); else if (c.nb == 2) DDT_ATTN(128, 2); else DDT_ATTN(128, 3);
+  }
+#undef DDT_ATTN
+  r = launch_status();
+  if (r) return r;
+  dim3 cgrid(c.rows_wg, Hkv, P->B * c.n_rg);
+  if (D == 256)
+    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, dim3(256), 0, st, A);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, A);
+  return launch_status();
+}
