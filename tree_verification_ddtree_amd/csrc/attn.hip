@@ -22,9 +22,10 @@
 //    of V^T from LDS, B = P).  Keys are permuted inside a 32-key tile so
 //    that lane group q holds keys 8q..8q+7 -- exactly the 8 consecutive
 //    tokens that one 16-byte read of a channel-major V page provides.
-//  - K and V pages go straight from HBM into a 3-stage LDS ring
-//    (global_load_lds_dwordx4, two 32-key tiles in flight, no staging
-//    registers); 16-byte chunks are XOR-swizzled so the operand reads of a
+//  - K and V pages go straight from HBM into a 4-stage LDS ring
+//    (global_load_lds_dwordx4, up to three 32-key tiles in flight, no
+//    staging registers); the scores of the next tile are computed while
+//    the current tile's probabilities and value product are formed; 16-byte chunks are XOR-swizzled so the operand reads of a
 //    wavefront hit distinct banks.  The ragged last tile and the tree tiles
 //    go through registers so keys past the end can be zero-filled.
 //  - Rows: 16-row blocks are dealt round-robin to the 4 wavefronts (NB
@@ -32,9 +33,10 @@
 //  - The tree itself is one or two extra 32-key tiles (draft K/V of up to
 //    64 nodes) processed by the last split of the sequence, masked by the
 //    plan's ancestor bitmask; cache keys are never masked per row.
-//  - Online softmax without rescaling the accumulators: a row's reference
-//    max is fixed by its first tile and probabilities are formed against
-//    it (fp16 P has 15 binades of headroom above 1).  A split whose scores
+//  - Online softmax without rescaling the accumulators and without a
+//    cross-lane max per tile: a row's reference max is fixed by its first
+//    tile and probabilities are formed against it (fp16 P has 15 binades
+//    of headroom above 1); each lane only checks its own scores.  A split whose scores
 //    outgrow that headroom is recomputed with the true maxima, so the
 //    result is exact either way; on ordinary data the redo never happens.
 //  - Each split writes unnormalised partial O^T, its reference max and the
@@ -93,7 +95,7 @@ struct Lds {
   static constexpr int V_HALVES = TILE * D;
   static constexpr int STAGE = K_HALVES + V_HALVES;
 };
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 4;
 
 // tile-local key tau (0..31) <-> K row in LDS
 __device__ __forceinline__ int krow_of(int tau) {
@@ -236,15 +238,13 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     }
   };
 
-  // ---- one 32-key tile: scores, online softmax, value product
-  auto compute_tile = [&](int stage, bool tree, int kbase) {
+  // ---- scores of one 32-key tile: S^T = K Q^T (two 16-key halves)
+  auto qk = [&](int stage, f32x4 (&S)[2][NB]) {
     const _Float16 *Ks = lds + stage * Lds<D>::STAGE;
-    const _Float16 *Vs = Ks + Lds<D>::K_HALVES;
-    f32x4 acc[2][NB];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NB; ++j) S[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -254,49 +254,143 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         const half8 kf = *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ (r & 7)));
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          if (blk_on[j]) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[j][ks], acc[tt][j], 0, 0, 0);
+          S[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[j][ks], S[tt][j], 0, 0, 0);
       }
     }
-    // this lane holds keys kbase + 8*lq + e (e = 4*tt + i) of row l16
-    half8 pf[NB];
+  };
+
+  // ---- probabilities of one tile against each row's reference max.
+  // This lane holds keys kbase + 8*lq + e (e = 4*tt + i) of row l16.
+  // mask = 1: ragged cache tile; 2: tree tile.  Row blocks past the
+  // sequence's rows compute harmless values that are never written out.
+  auto softmax = [&](const f32x4 (&S)[2][NB], int mask, int kbase, half8 (&pf)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (!blk_on[j]) continue;
       float sv[8];
-      float mloc = -INFINITY;
+      float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = kbase + 8 * lq + e;
-        const bool valid = tree ? (key < s.n && ((ancr[j] >> key) & 1ull)) : (key < t_end);
-        sv[e] = valid ? acc[e >> 2][j][e & 3] : -INFINITY;
-        mloc = fmaxf(mloc, sv[e]);
+        const bool valid = mask == 2 ? (key < s.n && ((ancr[j] >> key) & 1ull)) : (key < t_end);
+        sv[e] = valid ? S[e >> 2][j][e & 3] : -INFINITY;
+        tmax = fmaxf(tmax, sv[e]);
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      // the row's reference max is its first finite tile max; later tiles
-      // may exceed it by up to 2^15 in probability (fp16 P keeps range),
-      // beyond that the split is redone with the true max
-      if (mrow[j] == -INFINITY) mrow[j] = mloc;
-      mseen[j] = fmaxf(mseen[j], mloc);
-      ovf |= (mloc - mrow[j]) * A.c > 15.0f;
-      const float mc = mrow[j] * A.c;
+      if (__ballot(mrow[j] == -INFINITY)) {
+        // a row's first tile with valid keys fixes its reference max
+        float mloc = fmaxf(tmax, __shfl_xor(tmax, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        if (mrow[j] == -INFINITY) mrow[j] = mloc;
+      }
+      mseen[j] = fmaxf(mseen[j], tmax);
+      ovf |= (tmax - mrow[j]) * A.c > 15.0f;  // fp16 P keeps 15 binades above 1
+      const float mc = mrow[j] == -INFINITY ? 0.f : mrow[j] * A.c;
       float p[8], ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = (mrow[j] == -INFINITY) ? 0.f : exp2f(fmaf(sv[e], A.c, -mc));  // masked: exp2(-inf) = 0
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], A.c, -mc));  // masked keys: exp2(-inf) = 0
         ps += p[e];
       }
       lsum[j] += ps;
       pf[j] = half8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
                     (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
     }
+  };
+  // full cache tile, every reference already fixed: no masks, no branches
+  auto softmax_blk = [&](const f32x4 (&S)[2][NB], int j, half8 &pfj) {
+    float sv[8], p[8], ps = 0.f, tmax = -INFINITY;
+    const float mc = mrow[j] * A.c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = S[e >> 2][j][e & 3];
+      tmax = fmaxf(tmax, sv[e]);
+      p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], A.c, -mc));
+      ps += p[e];
+    }
+    mseen[j] = fmaxf(mseen[j], tmax);
+    ovf |= (tmax - mrow[j]) * A.c > 15.0f;
+    lsum[j] += ps;
+    pfj = half8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+  };
+  // K fragment (tile stage, key half tt, k-step ks) and V fragment (channel block n)
+  auto kfrag = [&](const _Float16 *Ks, int tt, int ks) -> half8 {
+    const int r = 16 * tt + l16;
+    const int cc = 4 * ks + lq;
+    return *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ (r & 7)));
+  };
+  auto vfrag = [&](const _Float16 *Vs, int n) -> half8 {
+    const int d = 16 * n + l16;
+    return *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ ((d >> 1) & 3)));
+  };
+  // One full tile of the main loop: scores of the next tile (Ks1) while the
+  // probabilities and value product of this tile (S, Vs0) are formed.
+  // sched_barrier fences keep each batch of LDS reads one batch ahead of
+  // the MFMAs that consume it and put the softmax next to the score MFMAs.
+  auto tile_step = [&](const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
+                       f32x4 (&Sn)[2][NB]) {
+    constexpr int KH = KS / 2;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) Sn[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    half8 ka[2][KH], kb[2][KH], pf[NB];
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) ka[tt][ks] = kfrag(Ks1, tt, ks);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) kb[tt][ks] = kfrag(Ks1, tt, KH + ks);
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tt][ks], qf[j][ks], Sn[tt][j], 0, 0, 0);
+    softmax_blk(S, 0, pf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int VH = DB / 2;
+    half8 va[VH], vb[VH];
+#pragma unroll
+    for (int n = 0; n < VH; ++n) va[n] = vfrag(Vs0, n);
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[tt][ks], qf[j][KH + ks], Sn[tt][j], 0, 0, 0);
+#pragma unroll
+    for (int j = 1; j < NB; ++j) softmax_blk(S, j, pf[j]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < VH; ++n) vb[n] = vfrag(Vs0, VH + n);
+#pragma unroll
+    for (int n = 0; n < VH; ++n)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[n], pf[j], o[j][n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < VH; ++n)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        o[j][VH + n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb[n], pf[j], o[j][VH + n], 0, 0, 0);
+  };
+
+  // ---- O^T += V^T P^T for one tile
+  auto pv = [&](int stage, const half8 (&pf)[NB]) {
+    const _Float16 *Vs = lds + stage * Lds<D>::STAGE + Lds<D>::K_HALVES;
 #pragma unroll
     for (int n = 0; n < DB; ++n) {
       const int d = 16 * n + l16;
       const half8 vf = *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ ((d >> 1) & 3)));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        if (blk_on[j]) o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[j], o[j][n], 0, 0, 0);
+        o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[j], o[j][n], 0, 0, 0);
     }
   };
 
@@ -311,17 +405,52 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int n = 0; n < DB; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // ---- main loop: full tiles through a 3-stage ring, two tiles in flight
-    if (n_full > 0) issue_tile(0, 0);
-    if (n_full > 1) issue_tile(1, 1);
-    for (int it = 0; it < n_full; ++it) {
-      if (it + 1 < n_full)
+    // ---- main loop over full tiles: 4-stage LDS ring with up to three
+    // tiles in flight; the scores of tile it+1 are formed while the
+    // probabilities and value product of tile it are worked on.
+    if (n_full > 0) {
+      issue_tile(0, 0);
+      if (n_full > 1) issue_tile(1, 1);
+      if (n_full > 2) issue_tile(2, 2);
+      if (n_full > 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * WAVE_CH) : "memory");
+      else if (n_full > 1)
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // tile it landed for every wave; stage (it+2)%3 is free
-      if (it + 2 < n_full) issue_tile(it + 2, (it + 2) % NSTAGE);
-      compute_tile(it % NSTAGE, false, t_beg + it * TILE);
+      __syncthreads();
+      f32x4 Sn[2][NB];
+      qk(0, Sn);
+      // the first full tile fixes every row's reference max (pass 0 only)
+      if (__ballot(mrow[0] == -INFINITY)) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          float t = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t = fmaxf(t, Sn[e >> 2][j][e & 3]);
+          t = fmaxf(t, __shfl_xor(t, 16));
+          mrow[j] = fmaxf(t, __shfl_xor(t, 32));
+        }
+      }
+      for (int it = 0; it < n_full; ++it) {
+        if (it + 1 < n_full) {
+          if (it + 2 < n_full)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();  // tile it+1 landed; every wave is past tile it-1
+        if (it + 3 < n_full) issue_tile(it + 3, (it + 3) % NSTAGE);
+        // scores of tile it+1 (past the last tile they read a stale stage
+        // and are dropped), probabilities and value product of tile it
+        f32x4 Sc[2][NB];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
+        tile_step(lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
+                  lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn);
+      }
     }
     // ---- epilogue: ragged cache tile, then the tree tiles
     const int n_ep = (has_part ? 1 : 0) + n_tree;
@@ -331,12 +460,19 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       __syncthreads();  // the stage is no longer read
       fill_tile(tree, kbase, 0);
       __syncthreads();
-      compute_tile(0, tree, kbase);
+      f32x4 S[2][NB];
+      half8 pf[NB];
+      qk(0, S);
+      softmax(S, tree ? 2 : 1, kbase, pf);
+      pv(0, pf);
     }
     if (!__syncthreads_or(ovf)) break;
     ovf = false;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) mrow[j] = mseen[j];
+    for (int j = 0; j < NB; ++j) {
+      float m = fmaxf(mseen[j], __shfl_xor(mseen[j], 16));
+      mrow[j] = fmaxf(m, __shfl_xor(m, 32));
+    }
   }
 
   // ---- partial results of this split
