@@ -149,7 +149,7 @@ int ddt_tree_plan(const ddt_plan *plan, int32_t max_levels, void *stream);
  *   prefix device [B][W-1][C]         dtype, oldest first (read only)
  *   w      device [C][W]              dtype, tap W-1 = current token
  *   y      device [n_total][C]        fp32
- *   act    0 = identity, 1 = SiLU;  dtype DDT_F32 or DDT_BF16;  C % 8 == 0.
+ *   act    0 = identity, 1 = SiLU;  dtype DDT_F32 or DDT_BF16;  C % 64 == 0.
  */
 int ddt_tree_conv(const ddt_plan *plan, const void *x, const void *prefix, const void *w,
                   int32_t C, int32_t act, int32_t dtype, float *y, void *stream);

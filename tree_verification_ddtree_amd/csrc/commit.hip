@@ -8,7 +8,7 @@
 // replay (or select) delta-net state tiles, then conv prefixes, then one
 // block per sequence appending K/V for all attention layers and finally
 // advancing T.
-#include "common.h"
+#include "gdn_wy.h"
 
 namespace ddt {
 
@@ -36,7 +36,7 @@ __device__ __forceinline__ int path_node(const CommitArgs &A, int b, int r, int 
 }
 
 template <typename T, int DK>
-__device__ void commit_state_tile(const CommitArgs &A, int unit) {
+__device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
   constexpr int LPR = DK / 8;
   const int tile = unit % A.tiles;
   int rest = unit / A.tiles;
@@ -44,40 +44,51 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit) {
   rest /= A.Hv;
   const int b = rest % A.P.B;
   const int layer = rest / A.P.B;
-  if ((int)threadIdx.x >= A.R * LPR) return;
-  const int lr = threadIdx.x / LPR, c0 = (threadIdx.x % LPR) * 8;
-  const int row = tile * A.R + lr;
+  const int tid = threadIdx.x;
+  const bool lane_on = tid < A.R * LPR;
+  const int lr = tid / LPR, cg = tid % LPR, row0 = tile * A.R;
   const Seq s = seq_of(A.P, b);
   const int Lb = path_len(A, b, s.n);
   if (Lb == 0) return;
   const ddt_gdn_layer lay = A.gl[layer];
-  float *Sr = lay.S_c + (((size_t)b * A.Hv + h) * A.dv + row) * DK + c0;
-  float s8[8];
+  float *Sr = lay.S_c + (((size_t)b * A.Hv + h) * A.dv + row0 + lr) * DK + cg * 8;
   if (A.mode == DDT_COMMIT_SELECT) {
     if (!lay.node_states) {
-      if (threadIdx.x == 0) atomicOr((unsigned *)&A.P.status[b], DDT_ST_COMMIT);
+      if (tid == 0) atomicOr((unsigned *)&A.P.status[b], DDT_ST_COMMIT);
       return;
     }
+    if (!lane_on) return;
     const int gn = s.o + path_node(A, b, Lb - 1, s.n);
-    ld8f(lay.node_states + (((size_t)gn * A.Hv + h) * A.dv + row) * DK + c0, s8);
-  } else {
-    const int g = h / (A.Hv / A.Hk);
-    const T *k = (const T *)lay.k, *v = (const T *)lay.v;
-    const T *al = (const T *)lay.alpha, *be = (const T *)lay.beta;
-    ld8f(Sr, s8);
-    for (int r = 0; r < Lb; ++r) {
-      const int gn = s.o + path_node(A, b, r, s.n);
-      float kk[8], sn[8];
-      load8(k + ((size_t)gn * A.Hk + g) * DK + c0, kk);
-      const float vr = load1(v + ((size_t)gn * A.Hv + h) * A.dv + row);
-      const float a = load1(al + (size_t)gn * A.Hv + h);
-      const float bb = load1(be + (size_t)gn * A.Hv + h);
-      gdn_row_step<LPR>(s8, kk, vr, a, bb, sn);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s8[e] = sn[e];
-    }
+    float s8[8];
+    ld8f(lay.node_states + (((size_t)gn * A.Hv + h) * A.dv + row0 + lr) * DK + cg * 8, s8);
+    st8f(Sr, s8);
+    return;
   }
-  st8f(Sr, s8);
+  // replay: the tree kernel's WY evaluation restricted to the accepted path
+  // (a chain), so the state is bitwise the one that kernel would persist
+  const GdnLds L(A.P.n_max, A.R, DK);
+  GdnView V(lds, L, A.P.n_max, A.R);
+  const int g = h / (A.Hv / A.Hk);
+  for (int r = tid; r < Lb; r += blockDim.x) {
+    V.gid[r] = s.o + path_node(A, b, r, s.n);
+    V.anc[r] = (2ull << r) - 1;
+    V.lvl[r] = r;
+  }
+  for (int d = tid; d <= Lb; d += blockDim.x) V.lvs[d] = d;
+  float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (lane_on) ld8f(Sr, sc);
+  __syncthreads();
+  gdn_stage<T, DK>(V, Lb, (const T *)lay.q, (const T *)lay.k, (const T *)lay.v,
+                   (const T *)lay.alpha, (const T *)lay.beta, A.Hk, A.Hv, A.dv, g, h, row0);
+  __syncthreads();
+  if (lane_on) gdn_products<LPR, DK>(V, Lb, sc, lr, cg, false);
+  __syncthreads();
+  if (lane_on) {
+    gdn_solve(V, Lb, A.R * LPR);
+    float s8[8];
+    gdn_state<DK>(V, Lb - 1, sc, lr, cg, s8);
+    st8f(Sr, s8);
+  }
 }
 
 // 16-byte chunk of E elements
@@ -154,9 +165,10 @@ __global__ void commit_len_kernel(CommitArgs A) {
 
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void commit_kernel(CommitArgs A) {
+  extern __shared__ float4 commit_lds[];
   int u = blockIdx.x;
   if (u < A.nA) {
-    commit_state_tile<T, DK>(A, u);
+    commit_state_tile<T, DK>(A, u, reinterpret_cast<char *>(commit_lds));
     return;
   }
   u -= A.nA;
@@ -235,7 +247,13 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
   const int blocks = A.nA + A.nB + nC;
   if (blocks == 0) return DDT_OK;
   hipStream_t st = (hipStream_t)stream;
-#define DDT_COMMIT(TT, DD) hipLaunchKernelGGL((commit_kernel<TT, DD>), dim3(blocks), dim3(256), 0, st, A)
+  const size_t lds = (n_gdn > 0 && mode == DDT_COMMIT_REPLAY) ? GdnLds(P->n_max, A.R, dkc).total : 0;
+#define DDT_COMMIT(TT, DD)                                                                  \
+  do {                                                                                      \
+    (void)hipFuncSetAttribute((const void *)commit_kernel<TT, DD>,                          \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);        \
+    hipLaunchKernelGGL((commit_kernel<TT, DD>), dim3(blocks), dim3(256), lds, st, A);      \
+  } while (0)
   const bool bf = (n_gdn == 0) || gdn_dtype == DDT_BF16;
   switch (dkc) {
     case 16: if (bf) DDT_COMMIT(uint16_t, 16); else DDT_COMMIT(float, 16); break;

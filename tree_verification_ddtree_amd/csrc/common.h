@@ -66,23 +66,6 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// One gated delta-rule step for the 8 columns of a state row this lane owns
-// (LPR lanes per row): s_n = a s_p + u k with u = b (v_r - a (s_p . k)).
-// Shared by the tree kernel and the commit's replay so that both produce
-// bitwise the same states.
-template <int LPR>
-__device__ __forceinline__ float gdn_row_step(const float (&sp)[8], const float (&kk)[8], float vr,
-                                              float a, float bb, float (&sn)[8]) {
-  float d = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) d = fmaf(sp[e], kk[e], d);
-  d = group_sum<LPR>(d);
-  const float u = bb * fmaf(-a, d, vr);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sn[e] = fmaf(a, sp[e], u * kk[e]);
-  return u;
-}
-
 __device__ __forceinline__ void ld8f(const float *p, float (&f)[8]) {
   float4 a0 = reinterpret_cast<const float4 *>(p)[0];
   float4 a1 = reinterpret_cast<const float4 *>(p)[1];
