@@ -109,19 +109,58 @@ __device__ void gdn_stage(GdnView &V, int n, const T *__restrict__ q, const T *_
                           const T *__restrict__ v, const T *__restrict__ alpha,
                           const T *__restrict__ beta, int Hk, int Hv, int dv, int g, int h,
                           int row0) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int U = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int PPR = DK / U;             // pieces per k or q row
+  constexpr int MAXP = 8;                 // pieces staged in registers per thread
   const int tid = threadIdx.x, nth = blockDim.x;
-  constexpr int CPN = DK / 8;
-  for (int idx = tid; idx < n * 2 * CPN; idx += nth) {
-    const int j = idx / (2 * CPN), which = (idx / CPN) & 1, cc = idx % CPN;
-    float f[8];
-    load8((which ? q : k) + ((size_t)V.gid[j] * Hk + g) * DK + 8 * cc, f);
-    st8f(V.kq + ((size_t)j * 2 + which) * DK + 8 * cc, f);
+  const int np = n * 2 * PPR;
+  auto src = [&](int idx) -> const u32x4 * {
+    const int j = idx / (2 * PPR), which = (idx / PPR) & 1, pc = idx % PPR;
+    return reinterpret_cast<const u32x4 *>((which ? q : k) + ((size_t)V.gid[j] * Hk + g) * DK) + pc;
+  };
+  auto put = [&](int idx, u32x4 x) {
+    const int j = idx / (2 * PPR), which = (idx / PPR) & 1, pc = idx % PPR;
+    float *dst = V.kq + ((size_t)j * 2 + which) * DK + pc * U;
+    if constexpr (sizeof(T) == 2) {
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(x[i] << 16);
+        f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+      }
+      st8f(dst, f);
+    } else {
+      *reinterpret_cast<u32x4 *>(dst) = x;
+    }
+  };
+  // every global load of this thread first (clamped indices), then the stores
+  u32x4 buf[MAXP];
+#pragma unroll
+  for (int u = 0; u < MAXP; ++u) buf[u] = *src(min(tid + u * nth, np - 1));
+  float vb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = min(tid + u * nth, n * V.R - 1);
+    vb[u] = load1(v + ((size_t)V.gid[idx / V.R] * Hv + h) * dv + row0 + idx % V.R);
   }
-  for (int idx = tid; idx < n * V.R; idx += nth) {
-    const int j = idx / V.R, r = idx % V.R;
-    V.v[idx] = load1(v + ((size_t)V.gid[j] * Hv + h) * dv + row0 + r);
+  const int jt = min(tid, n - 1);
+  const float a0 = load1(alpha + (size_t)V.gid[jt] * Hv + h);
+  const float b0 = load1(beta + (size_t)V.gid[jt] * Hv + h);
+#pragma unroll
+  for (int u = 0; u < MAXP; ++u)
+    if (tid + u * nth < np) put(tid + u * nth, buf[u]);
+  for (int idx = tid + MAXP * nth; idx < np; idx += nth) put(idx, *src(idx));
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (tid + u * nth < n * V.R) V.v[tid + u * nth] = vb[u];
+  for (int idx = tid + 4 * nth; idx < n * V.R; idx += nth)
+    V.v[idx] = load1(v + ((size_t)V.gid[idx / V.R] * Hv + h) * dv + row0 + idx % V.R);
+  if (tid < n) {
+    V.al[tid] = a0;
+    V.be[tid] = b0;
   }
-  for (int j = tid; j < n; j += nth) {
+  for (int j = tid + nth; j < n; j += nth) {
     V.al[j] = load1(alpha + (size_t)V.gid[j] * Hv + h);
     V.be[j] = load1(beta + (size_t)V.gid[j] * Hv + h);
   }
@@ -134,12 +173,22 @@ template <int LPR, int DK>
 __device__ void gdn_products(GdnView &V, int n, const float (&sc)[8], int lr, int cg,
                              bool want_F) {
   const int c0 = cg * 8;
-  for (int j = 0; j < n; ++j) {
-    const float d = ldot<LPR>(sc, V.kq + (size_t)j * 2 * DK + c0);
-    if (cg == 0) V.D[lr * V.nmax + j] = d;
-    if (want_F) {
-      const float f = ldot<LPR>(sc, V.kq + ((size_t)j * 2 + 1) * DK + c0);
-      if (cg == 0) V.F[lr * V.nmax + j] = f;
+  // four nodes at a time so the lane-group sums of independent dots overlap
+  for (int j0 = 0; j0 < n; j0 += 4) {
+    float d[4], f[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u, n - 1);
+      d[u] = ldot<LPR>(sc, V.kq + (size_t)j * 2 * DK + c0);
+      f[u] = want_F ? ldot<LPR>(sc, V.kq + ((size_t)j * 2 + 1) * DK + c0) : 0.f;
+    }
+    if (cg == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n) {
+          V.D[lr * V.nmax + j0 + u] = d[u];
+          V.F[lr * V.nmax + j0 + u] = f[u];
+        }
     }
   }
   // pair coefficients: row group lr takes nodes i = lr, lr + R, ...
