@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests: moving synth arrays to the device and
 the tolerance metric.  Imports no oracle arithmetic."""
+import os
+
 import numpy as np
 import torch
 
@@ -28,7 +30,12 @@ def rel_err(got, ref, axes):
     num = np.abs(got - ref).max(axis=red) if red else np.abs(got - ref)
     den = np.abs(ref).max(axis=red) if red else np.abs(ref)
     den = np.where(den == 0, 1.0, den)
-    return float((num / den).max())
+    r = float((num / den).max())
+    log = os.environ.get("DDT_REL_LOG")
+    if log:  # record observed errors: one line per comparison
+        with open(log, "a") as f:
+            f.write(f"{os.environ.get('PYTEST_CURRENT_TEST', '?').split(' ')[0]} {r:.3e}\n")
+    return r
 
 
 def banner(msg):
