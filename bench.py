@@ -2,7 +2,8 @@
 
 One step = the whole hot path on one batch of synthetic input:
   plan -> 16 x [3 x (tree conv + tree gated delta-net), tree attention]
-       -> verify argmax + greedy walk -> commit of the accepted path (replay)
+       -> verify argmax + greedy walk -> commit of the accepted path (the
+          delta-net states rebuilt from the u the tree kernel saved)
 on the hybrid stack of 48 gated delta-net layers and 16 attention layers at
 131,072 committed tokens and a 22-node draft tree (the pages' budget 22:
 lucebox-hub README, "02 · DFlash DDtree", "Implemented here"; 128K context:
@@ -62,13 +63,14 @@ class Stack:
         npages = (self.T_max + N + 15) // 16
         g = torch.Generator(device=device)
         n_gdn, n_attn = c["n_gdn"], c["n_attn"]
-        self.gdn, self.conv, self.gdn_out, self.conv_out = [], [], [], []
+        self.gdn, self.conv, self.gdn_out, self.conv_out, self.gdn_u = [], [], [], [], []
         for l in range(n_gdn):
             gi = synth.gdn_inputs(seed, (3, l), N, c["Hk"], c["Hv"], c["dk"], c["dv"], "bf16")
             self.gdn.append({k: _dev(v, device) for k, v in gi.items()})
             ci = synth.conv_inputs(seed, (3, 1000 + l), N, c["C"], c["W"], "bf16")
             self.conv.append({k: _dev(v, device) for k, v in ci.items()})
             self.gdn_out.append(torch.empty(N, c["Hv"], c["dv"], dtype=torch.float32, device=device))
+            self.gdn_u.append(torch.empty(N, c["Hv"], c["dv"], dtype=torch.float32, device=device))
             self.conv_out.append(torch.empty(N, c["C"], dtype=torch.float32, device=device))
         self.attn, self.kv, self.attn_out = [], [], []
         for l in range(n_attn):
@@ -95,10 +97,11 @@ class Stack:
         self.path = torch.empty(1, self.tb.n_max, **i32)
         self.L = torch.empty(1, **i32)
         self.bonus = torch.empty(1, **i32)
-        gl = [ddt.GdnLayer(a["q"].data_ptr(), a["k"].data_ptr(), a["v"].data_ptr(),
-                           a["alpha"].data_ptr(), a["beta"].data_ptr(), a["S_c"].data_ptr(), None,
-                           x["x"].data_ptr(), x["prefix"].data_ptr())
-              for a, x in zip(self.gdn, self.conv)]
+        gl = [ddt.GdnLayer(q=a["q"].data_ptr(), k=a["k"].data_ptr(), v=a["v"].data_ptr(),
+                           alpha=a["alpha"].data_ptr(), beta=a["beta"].data_ptr(),
+                           S_c=a["S_c"].data_ptr(), node_u=u.data_ptr(), x=x["x"].data_ptr(),
+                           prefix=x["prefix"].data_ptr())
+              for a, x, u in zip(self.gdn, self.conv, self.gdn_u)]
         al = [ddt.AttnLayer(a["Kt"].data_ptr(), a["Vt"].data_ptr(), K.data_ptr(), Vv.data_ptr())
               for a, (K, Vv) in zip(self.attn, self.kv)]
         self.gdn_table, self.attn_table = ddt.layer_table(gl, device), ddt.layer_table(al, device)
@@ -113,7 +116,7 @@ class Stack:
                 x, g = self.conv[gi], self.gdn[gi]
                 ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0, self.conv_out[gi], stream)
                 ddt.ddt_tree_gdn(self.tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"],
-                                 1.0, self.gdn_out[gi], None, stream)
+                                 1.0, self.gdn_out[gi], None, self.gdn_u[gi], stream)
                 gi += 1
             at, (K, V) = self.attn[a], self.kv[a]
             ev = self.attn_events
@@ -125,7 +128,7 @@ class Stack:
                 ev[a][1].record()
         ddt.ddt_accept_walk(self.tb, self.logits, self.tok, self.amax, self.path, self.L,
                             self.bonus, self.walk_ws, stream)
-        ddt.ddt_commit_state(self.tb, self.path, self.L, ddt.DDT_COMMIT_REPLAY, self.gdn_table,
+        ddt.ddt_commit_state(self.tb, self.path, self.L, ddt.DDT_COMMIT_UPDATE, self.gdn_table,
                              c["n_gdn"], c["Hk"], c["Hv"], c["dk"], c["dv"], ddt.DDT_BF16, c["C"],
                              ddt.DDT_BF16, self.attn_table, c["n_attn"], c["Hkv"], c["D"],
                              ddt.DDT_F16, None, self.T, stream)

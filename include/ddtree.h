@@ -97,7 +97,10 @@ typedef struct ddt_plan {
   int32_t n_total; /* nodes over all sequences = tree_off[B]               */
   int32_t n_max;   /* largest tree, 1..DDT_MAX_NODES                       */
   int32_t W;       /* conv width the windows are built for, 1..DDT_MAX_W   */
-  const int32_t *tree_off; /* [B+1] node offsets, tree_off[0] = 0           */
+  const int32_t *tree_off; /* [B+1] node offsets, tree_off[0] = 0; with B = 1
+                              the layer kernels do not read it (the tree is
+                              nodes 0..n_total-1) and the device plan flags
+                              DDT_ST_TREE if it says otherwise             */
   const int32_t *parent;   /* [n_total] local parent ids                    */
   int32_t *depth;  /* out [n_total] edge depth (root 0)                    */
   uint64_t *anc;   /* out [n_total] bit j = local node j on the root path  */
@@ -169,13 +172,21 @@ int ddt_tree_conv(const ddt_plan *plan, const void *x, const void *prefix, const
  *   node_states device [n_total][Hv][dv][dk] fp32 or NULL: when given, every
  *               node's state is stored ("persist"), so the commit can
  *               select the accepted node's state instead of replaying.
- * Requires Hv % Hk == 0, dk in {16, 32, 64, 128}, dv % 16 == 0 (dv <= 128
- * or a multiple of the row tile), dtype DDT_F32 or DDT_BF16.
+ *   node_u      device [n_total][Hv][dv] fp32 or NULL: when given, every
+ *               node's u_n = beta_n (v_n - alpha_n S_p k_n) is stored (the
+ *               state update is S_n = alpha_n S_p + u_n k_n^T), so the commit
+ *               can rebuild the accepted node's state from S_c with one
+ *               rank-L update (DDT_COMMIT_UPDATE), 46x less than node_states.
+ * Requires Hv % Hk == 0, dk in {16, 32, 64, 128}, dv % 16 == 0, dtype
+ * DDT_F32 or DDT_BF16; q, k, v rows 16-byte aligned.  Outputs of nodes on
+ * the same root path are consistent to the last bit: the state a node gets
+ * here, in a replay of its path, or in an update from the saved u is the
+ * same.
  */
 int ddt_tree_gdn(const ddt_plan *plan, const void *q, const void *k, const void *v,
                  const void *alpha, const void *beta, const float *S_c, int32_t Hk, int32_t Hv,
                  int32_t dk, int32_t dv, float scale, int32_t dtype, float *out,
-                 float *node_states, void *stream);
+                 float *node_states, float *node_u, void *stream);
 
 /*
  * a4. Tree-masked attention over the committed KV cache.  Node i, query
@@ -237,7 +248,12 @@ int ddt_accept_walk(const ddt_plan *plan, const void *logits, int32_t dtype, int
  *  - each gated delta-net layer: S_c[b] <- state of node p_{L-1}.
  *    mode DDT_COMMIT_REPLAY re-runs the rule along the path from S_c;
  *    mode DDT_COMMIT_SELECT copies the persisted node state (node_states of
- *    that layer must be non-NULL).
+ *    that layer must be non-NULL); mode DDT_COMMIT_UPDATE applies
+ *    S_c <- a_i P_i S_c + sum_a a_i w(a,i) u_a k_a^T + u_i k_i^T over the
+ *    path, with the u saved by ddt_tree_gdn (node_u must be non-NULL; P_i is
+ *    the product of the gates of i's ancestors, w(a,i) of those strictly
+ *    between a and i).  All three give bitwise the same state.  A layer
+ *    without the buffer its mode needs sets DDT_ST_COMMIT and is left as is.
  *  - each conv: prefix[b] <- last W-1 rows of prefix[b] ++ x[path].
  *  - each attention layer: the path's Kt/Vt are written to cache positions
  *    T[b] .. T[b]+L-1 (the page table must already map them), and finally
@@ -248,11 +264,13 @@ int ddt_accept_walk(const ddt_plan *plan, const void *logits, int32_t dtype, int
  */
 #define DDT_COMMIT_REPLAY 0
 #define DDT_COMMIT_SELECT 1
+#define DDT_COMMIT_UPDATE 2
 
 typedef struct ddt_gdn_layer {
   const void *q, *k, *v, *alpha, *beta; /* this step's tree inputs (ddt_tree_gdn) */
   float *S_c;                           /* [B][Hv][dv][dk], updated in place */
   const float *node_states;             /* SELECT source, or NULL            */
+  const float *node_u;                  /* UPDATE source, or NULL            */
   const void *x;                        /* conv input [n_total][C], NULL = no conv */
   void *prefix;                         /* [B][W-1][C], updated in place     */
 } ddt_gdn_layer;

@@ -117,10 +117,10 @@ def test_device_entry_points_validate_before_launch():
     bp = ctypes.byref(P)
     one = ctypes.c_void_p(16)
     # gated delta-net: Hv not a multiple of Hk; unsupported dk; dtype
-    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 3, 4, 128, 128, 1.0, 2, one, None, None) == -3
-    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 2, 4, 96, 128, 1.0, 2, one, None, None) == -3
-    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 2, 4, 128, 128, 1.0, 1, one, None, None) == -4
-    assert L.ddt_tree_gdn(bp, None, one, one, one, one, one, 2, 4, 128, 128, 1.0, 2, one, None, None) == -1
+    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 3, 4, 128, 128, 1.0, 2, one, None, None, None) == -3
+    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 2, 4, 96, 128, 1.0, 2, one, None, None, None) == -3
+    assert L.ddt_tree_gdn(bp, one, one, one, one, one, one, 2, 4, 128, 128, 1.0, 1, one, None, None, None) == -4
+    assert L.ddt_tree_gdn(bp, None, one, one, one, one, one, 2, 4, 128, 128, 1.0, 2, one, None, None, None) == -1
     # conv: channels not a multiple of 8, bad activation
     assert L.ddt_tree_conv(bp, one, one, one, 12, 0, 2, one, None) == -3
     assert L.ddt_tree_conv(bp, one, one, one, 16, 2, 2, one, None) == -1

@@ -119,13 +119,25 @@ def test_gdn(gpu, case):
     out = torch.empty(n, c["Hv"], c["d"], dtype=torch.float32, device=gpu)
     out2 = torch.empty_like(out)
     ns = torch.empty(n, c["Hv"], c["d"], c["d"], dtype=torch.float32, device=gpu)
+    nu = torch.empty(n, c["Hv"], c["d"], dtype=torch.float32, device=gpu)
     ddt.ddt_tree_gdn(tb, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_c"], 1.0, out)
-    ddt.ddt_tree_gdn(tb, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_c"], 1.0, out2, ns)
+    ddt.ddt_tree_gdn(tb, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_c"], 1.0, out2, ns, nu)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)  # persisting states does not change the outputs
     if c["Hv"] * c["d"] ** 2 * n <= 32 * 128 * 128 * 22:
         ref, states = oracle.tree_gdn(par, **inp, tree_off=off, want_states=True)
         assert rel_err(host(ns), states, (0, 1)) < TOL
+        # saved u_i = beta_i (v_i - alpha_i S_parent k_i), from the oracle's states
+        f = oracle.num.f64
+        k64, v64, a64, b64, S64 = f(inp["k"]), f(inp["v"]), f(inp["alpha"]), f(inp["beta"]), f(inp["S_c"])
+        grp = c["Hv"] // c["Hk"]
+        u_ref = np.empty((n, c["Hv"], c["d"]))
+        for bb in range(B):
+            for j in range(off[bb], off[bb + 1]):
+                for hh in range(c["Hv"]):
+                    Sp = S64[bb, hh] if par[j] < 0 else states[off[bb] + par[j], hh]
+                    u_ref[j, hh] = b64[j, hh] * (v64[j, hh] - a64[j, hh] * (Sp @ k64[j, hh // grp]))
+        assert rel_err(host(nu), u_ref, (0, 1)) < TOL
     else:
         ref = oracle.tree_gdn(par, **inp, tree_off=off)
     assert rel_err(host(out), ref, (0, 1)) < TOL

@@ -55,11 +55,13 @@ def run_step(gpu, st, mode):
         y = torch.empty(n, C, dtype=torch.float32, device=gpu)
         ddt.ddt_tree_conv(tb, c["x"], c["prefix"], c["w"], 0, y)
         o = torch.empty(n, Hv, dk, dtype=torch.float32, device=gpu)
-        nsl = torch.empty(n, Hv, dk, dk, dtype=torch.float32, device=gpu) if mode == 1 else None
-        ddt.ddt_tree_gdn(tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"], 1.0, o, nsl)
+        nsl = (torch.empty(n, Hv, dk, dk, dtype=torch.float32, device=gpu)
+               if mode == ddt.DDT_COMMIT_SELECT else None)
+        nul = torch.empty(n, Hv, dk, dtype=torch.float32, device=gpu) if mode == ddt.DDT_COMMIT_UPDATE else None
+        ddt.ddt_tree_gdn(tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"], 1.0, o, nsl, nul)
         outs["conv"].append(y)
         outs["gdn"].append(o)
-        ns.append(nsl)
+        ns.append((nsl, nul))
     ws = torch.empty(ddt.ddt_tree_attn_workspace(tb, Hq, Hkv, D, T_max), dtype=torch.uint8, device=gpu)
     for (K, Vv), a in zip(d["kv"], d["attn"]):
         o = torch.empty(n, Hq, D, dtype=torch.float32, device=gpu)
@@ -71,10 +73,11 @@ def run_step(gpu, st, mode):
     L = torch.empty(B, dtype=torch.int32, device=gpu)
     bonus = torch.empty(B, dtype=torch.int32, device=gpu)
     ddt.ddt_accept_walk(tb, dev(st["logits"]), dev(st["tok"]), am, path, L, bonus, wws)
-    gl = [ddt.GdnLayer(g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["alpha"].data_ptr(),
-                       g["beta"].data_ptr(), g["S_c"].data_ptr(),
-                       ns[l].data_ptr() if ns[l] is not None else None,
-                       c["x"].data_ptr(), c["prefix"].data_ptr())
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    gl = [ddt.GdnLayer(q=g["q"].data_ptr(), k=g["k"].data_ptr(), v=g["v"].data_ptr(),
+                       alpha=g["alpha"].data_ptr(), beta=g["beta"].data_ptr(), S_c=g["S_c"].data_ptr(),
+                       node_states=ptr(ns[l][0]), node_u=ptr(ns[l][1]), x=c["x"].data_ptr(),
+                       prefix=c["prefix"].data_ptr())
           for l, (g, c) in enumerate(zip(d["gdn"], d["conv"]))]
     al = [ddt.AttnLayer(a["Kt"].data_ptr(), a["Vt"].data_ptr(), K.data_ptr(), Vv.data_ptr())
           for (K, Vv), a in zip(d["kv"], d["attn"])]
@@ -86,13 +89,13 @@ def run_step(gpu, st, mode):
                          status=host(tb.status))
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_step_against_oracle(gpu, seed):
-    banner(f"step seed={seed}")
+@pytest.mark.parametrize("seed,mode", [(0, 0), (1, 2)])
+def test_step_against_oracle(gpu, seed, mode):
+    banner(f"step seed={seed} commit mode={mode}")
     sizes = [22, 8, 33]
     T = [700, 1000, 64]
     st = build_step(gpu, seed, sizes, T)
-    d, outs, res = run_step(gpu, st, ddt.DDT_COMMIT_REPLAY)
+    d, outs, res = run_step(gpu, st, mode)
     par, off = st["par"], st["off"]
     assert not res["status"].any()
     for l in range(len(st["gdn"])):
@@ -126,14 +129,17 @@ def test_step_against_oracle(gpu, seed):
         assert np.array_equal(host(d["kv"][l][1]).view(np.uint16), st["kv"][l][1].view(np.uint16))
 
 
-def test_commit_replay_equals_select_bitwise(gpu):
-    banner("commit replay == select")
+def test_commit_modes_agree_bitwise(gpu):
+    banner("commit replay == select == update")
     st = build_step(gpu, 3, [22, 64, 5], [300, 40, 999])
     d1, _, r1 = run_step(gpu, st, ddt.DDT_COMMIT_REPLAY)
     d2, _, r2 = run_step(gpu, st, ddt.DDT_COMMIT_SELECT)
-    assert np.array_equal(r1["L"], r2["L"]) and (r1["L"] >= 1).all()
+    d3, _, r3 = run_step(gpu, st, ddt.DDT_COMMIT_UPDATE)
+    assert np.array_equal(r1["L"], r2["L"]) and np.array_equal(r1["L"], r3["L"]) and (r1["L"] >= 1).all()
+    assert (r1["L"] > 1).any()
     for l in range(len(st["gdn"])):
         assert torch.equal(d1["gdn"][l]["S_c"], d2["gdn"][l]["S_c"])
+        assert torch.equal(d1["gdn"][l]["S_c"], d3["gdn"][l]["S_c"])
         assert torch.equal(d1["conv"][l]["prefix"], d2["conv"][l]["prefix"])
 
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libddtree.so")
 
 DDT_F32, DDT_F16, DDT_BF16 = 0, 1, 2
-DDT_COMMIT_REPLAY, DDT_COMMIT_SELECT = 0, 1
+DDT_COMMIT_REPLAY, DDT_COMMIT_SELECT, DDT_COMMIT_UPDATE = 0, 1, 2
 DDT_ST_TREE, DDT_ST_LEVELS, DDT_ST_TOKEN, DDT_ST_ARGMAX, DDT_ST_CTX, DDT_ST_COMMIT = 1, 2, 4, 8, 16, 32
 DDT_PAGE = 16
 DDT_MAX_NODES = 64
@@ -30,7 +30,7 @@ class Plan(ctypes.Structure):
 
 class GdnLayer(ctypes.Structure):
     _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("alpha", _vp), ("beta", _vp),
-                ("S_c", _vp), ("node_states", _vp), ("x", _vp), ("prefix", _vp)]
+                ("S_c", _vp), ("node_states", _vp), ("node_u", _vp), ("x", _vp), ("prefix", _vp)]
 
 
 class AttnLayer(ctypes.Structure):
@@ -51,7 +51,7 @@ _SIGS = {
     "ddt_tree_plan": ([ctypes.POINTER(Plan), _i32, _vp], _i32),
     "ddt_tree_conv": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
     "ddt_tree_gdn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                      _f32, _i32, _vp, _vp, _vp], _i32),
+                      _f32, _i32, _vp, _vp, _vp, _vp], _i32),
     "ddt_tree_attn_workspace": ([ctypes.POINTER(Plan), _i32, _i32, _i32, _i32, _i32], _sz),
     "ddt_tree_attn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
                        _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
@@ -176,12 +176,13 @@ def ddt_tree_conv(plan, x, prefix, w, act, y, stream=None):
                                int(act), dtype_code(x), _ptr(y), _stream(stream)), "ddt_tree_conv")
 
 
-def ddt_tree_gdn(plan, q, k, v, alpha, beta, S_c, scale, out, node_states=None, stream=None):
+def ddt_tree_gdn(plan, q, k, v, alpha, beta, S_c, scale, out, node_states=None, node_u=None,
+                 stream=None):
     Hk, dk = int(q.shape[1]), int(q.shape[2])
     Hv, dv = int(v.shape[1]), int(v.shape[2])
     _check(lib().ddt_tree_gdn(_plan(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                               _ptr(S_c), Hk, Hv, dk, dv, float(scale), dtype_code(q), _ptr(out),
-                              _ptr(node_states), _stream(stream)), "ddt_tree_gdn")
+                              _ptr(node_states), _ptr(node_u), _stream(stream)), "ddt_tree_gdn")
 
 
 def ddt_tree_attn_workspace(plan, Hq, Hkv, D, T_max, n_splits=0):

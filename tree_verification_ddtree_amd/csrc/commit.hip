@@ -17,7 +17,7 @@ struct CommitArgs {
   const int32_t *path, *L;
   int mode;
   const ddt_gdn_layer *gl;
-  int n_gdn, Hk, Hv, dk, dv, gdt, C, cdt, tiles, R;
+  int n_gdn, Hk, Hv, dk, dv, gdt, C, cdt, tiles;
   const ddt_attn_layer *al;
   int n_attn, Hkv, D, kvdt;
   const int32_t *pt;
@@ -35,7 +35,54 @@ __device__ __forceinline__ int path_node(const CommitArgs &A, int b, int r, int 
   return (x >= 0 && x < n) ? x : 0;
 }
 
+// UPDATE: state of the last path node for 8 columns of one committed row,
+// rebuilt from the u saved by the tree kernel.  Same sequence of fp32
+// operations as gdn_state (ancestors nearest first), so the result is
+// bitwise the state the tree kernel would persist; all loads of a batch of
+// eight ancestors are issued before any arithmetic, and nothing goes
+// through LDS.
 template <typename T, int DK>
+__device__ void commit_update_row(const CommitArgs &A, const ddt_gdn_layer &lay, const Seq &s, int b,
+                                  int h, int row, int c0, int Lb, float *Srow) {
+  const T *k = (const T *)lay.k, *al = (const T *)lay.alpha;
+  const int g = h / (A.Hv / A.Hk);
+  auto uidx = [&](int gn) { return ((size_t)gn * A.Hv + h) * A.dv + row; };
+  float sc[8], ki[8];
+  ld8f(Srow, sc);
+  const int gi = s.o + path_node(A, b, Lb - 1, s.n);
+  load8(k + ((size_t)gi * A.Hk + g) * DK + c0, ki);
+  const float ai = load1(al + (size_t)gi * A.Hv + h);
+  const float ui = lay.node_u[uidx(gi)];
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float w = 1.f;
+  for (int r0 = Lb - 2; r0 >= 0; r0 -= 8) {
+    float ka[8][8], aa[8], ua[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int ga = s.o + path_node(A, b, max(r0 - t, 0), s.n);
+      load8(k + ((size_t)ga * A.Hk + g) * DK + c0, ka[t]);
+      aa[t] = load1(al + (size_t)ga * A.Hv + h);
+      ua[t] = lay.node_u[uidx(ga)];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (r0 - t >= 0) {
+        const float c = (ai * w) * ua[t];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(c, ka[t][e], acc[e]);
+        w *= aa[t];
+      }
+  }
+  const float cs = ai * w;
+  float s8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s8[e] = fmaf(ui, ki[e], fmaf(cs, sc[e], acc[e]));
+  st8f(Srow, s8);
+}
+
+template <typename T, int DK, int MODE>
 __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
   constexpr int LPR = DK / 8;
   const int tile = unit % A.tiles;
@@ -45,14 +92,14 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
   const int b = rest % A.P.B;
   const int layer = rest / A.P.B;
   const int tid = threadIdx.x;
-  const bool lane_on = tid < A.R * LPR;
-  const int lr = tid / LPR, cg = tid % LPR, row0 = tile * A.R;
+  const bool lane_on = tid < GDN_R * LPR;
+  const int lr = tid / LPR, c0 = (tid % LPR) * 8, row0 = tile * GDN_R;
   const Seq s = seq_of(A.P, b);
   const int Lb = path_len(A, b, s.n);
   if (Lb == 0) return;
   const ddt_gdn_layer lay = A.gl[layer];
-  float *Sr = lay.S_c + (((size_t)b * A.Hv + h) * A.dv + row0 + lr) * DK + cg * 8;
-  if (A.mode == DDT_COMMIT_SELECT) {
+  float *Sbase = lay.S_c + (((size_t)b * A.Hv + h) * A.dv + row0) * DK;
+  if (MODE == DDT_COMMIT_SELECT) {
     if (!lay.node_states) {
       if (tid == 0) atomicOr((unsigned *)&A.P.status[b], DDT_ST_COMMIT);
       return;
@@ -60,34 +107,38 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
     if (!lane_on) return;
     const int gn = s.o + path_node(A, b, Lb - 1, s.n);
     float s8[8];
-    ld8f(lay.node_states + (((size_t)gn * A.Hv + h) * A.dv + row0 + lr) * DK + cg * 8, s8);
-    st8f(Sr, s8);
+    ld8f(lay.node_states + (((size_t)gn * A.Hv + h) * A.dv + row0 + lr) * DK + c0, s8);
+    st8f(Sbase + lr * DK + c0, s8);
     return;
   }
-  // replay: the tree kernel's WY evaluation restricted to the accepted path
-  // (a chain), so the state is bitwise the one that kernel would persist
-  const GdnLds L(A.P.n_max, A.R, DK);
-  GdnView V(lds, L, A.P.n_max, A.R);
-  const int g = h / (A.Hv / A.Hk);
-  for (int r = tid; r < Lb; r += blockDim.x) {
-    V.gid[r] = s.o + path_node(A, b, r, s.n);
-    V.anc[r] = (2ull << r) - 1;
-    V.lvl[r] = r;
+  if (MODE == DDT_COMMIT_UPDATE) {
+    if (!lay.node_u) {
+      if (tid == 0) atomicOr((unsigned *)&A.P.status[b], DDT_ST_COMMIT);
+      return;
+    }
+    if (lane_on)
+      commit_update_row<T, DK>(A, lay, s, b, h, row0 + lr, c0, Lb, Sbase + lr * DK + c0);
+    return;
   }
-  for (int d = tid; d <= Lb; d += blockDim.x) V.lvs[d] = d;
-  float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (lane_on) ld8f(Sr, sc);
+  // Replay: the tree kernel's evaluation restricted to the accepted path, a
+  // chain whose nodes take positions 0..Lb-1 (position r has ancestors
+  // 0..r-1, visited nearest first as in the tree).
+  const GdnLds L(A.P.n_max);
+  GdnView V(lds, L, A.P.n_max);
+  const int g = h / (A.Hv / A.Hk);
+  const T *k = (const T *)lay.k;
+  auto gid = [&](int r) { return s.o + path_node(A, b, r, s.n); };
+  auto chain = [&](int r) { return ~0ull >> (63 - r); };
+  gdn_front<T, DK>(V, Lb, gid, chain, (const T *)lay.q, k, (const T *)lay.v, (const T *)lay.alpha,
+                   (const T *)lay.beta, Sbase, A.Hk, A.Hv, A.dv, g, h, row0);
   __syncthreads();
-  gdn_stage<T, DK>(V, Lb, (const T *)lay.q, (const T *)lay.k, (const T *)lay.v,
-                   (const T *)lay.alpha, (const T *)lay.beta, A.Hk, A.Hv, A.dv, g, h, row0);
-  __syncthreads();
-  if (lane_on) gdn_products<LPR, DK>(V, Lb, sc, lr, cg, false);
+  gdn_scalar<false>(V, Lb, Lb, 1.f);
   __syncthreads();
   if (lane_on) {
-    gdn_solve(V, Lb, A.R * LPR);
     float s8[8];
-    gdn_state<DK>(V, Lb - 1, sc, lr, cg, s8);
-    st8f(Sr, s8);
+    auto krow = [&](int r) { return k + ((size_t)gid(r) * A.Hk + g) * DK; };
+    gdn_state(V, Lb - 1, lr, c0, Sbase + lr * DK, krow, s8);
+    st8f(Sbase + lr * DK + c0, s8);
   }
 }
 
@@ -163,12 +214,14 @@ __global__ void commit_len_kernel(CommitArgs A) {
     A.P.status[b] |= DDT_ST_CTX;
 }
 
-template <typename T, int DK>
+// One instantiation per mode, so that the replay's register demand does not
+// lower the occupancy of the streaming modes.
+template <typename T, int DK, int MODE>
 __global__ __launch_bounds__(256) void commit_kernel(CommitArgs A) {
   extern __shared__ float4 commit_lds[];
   int u = blockIdx.x;
   if (u < A.nA) {
-    commit_state_tile<T, DK>(A, u, reinterpret_cast<char *>(commit_lds));
+    commit_state_tile<T, DK, MODE>(A, u, reinterpret_cast<char *>(commit_lds));
     return;
   }
   u -= A.nA;
@@ -202,7 +255,8 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
   int r = check_plan(P);
   if (r) return r;
   if (!path || !L) return DDT_E_ARG;
-  if (mode != DDT_COMMIT_REPLAY && mode != DDT_COMMIT_SELECT) return DDT_E_ARG;
+  if (mode != DDT_COMMIT_REPLAY && mode != DDT_COMMIT_SELECT && mode != DDT_COMMIT_UPDATE)
+    return DDT_E_ARG;
   if (n_gdn < 0 || n_attn < 0) return DDT_E_SHAPE;
   CommitArgs A{};
   A.P = *P;
@@ -221,13 +275,12 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
     if (!gdn_layers) return DDT_E_ARG;
     if (Hk < 1 || Hv < 1 || Hv % Hk) return DDT_E_SHAPE;
     if (dk != 16 && dk != 32 && dk != 64 && dk != 128) return DDT_E_SHAPE;
-    if (dv < 1 || dv % gdn_rows(dk, dv)) return DDT_E_SHAPE;
+    if (dv < GDN_R || dv % GDN_R) return DDT_E_SHAPE;
     if (gdn_dtype != DDT_BF16 && gdn_dtype != DDT_F32) return DDT_E_DTYPE;
     if (conv_dtype != DDT_BF16 && conv_dtype != DDT_F32) return DDT_E_DTYPE;
     if (C < 0 || C % 8) return DDT_E_SHAPE;
     A.Hk = Hk; A.Hv = Hv; A.dk = dk; A.dv = dv; A.gdt = gdn_dtype; A.C = C; A.cdt = conv_dtype;
-    A.R = gdn_rows(dk, dv);
-    A.tiles = dv / A.R;
+    A.tiles = dv / GDN_R;
     A.nA = n_gdn * P->B * Hv * A.tiles;
     A.nB = (C > 0) ? n_gdn * P->B : 0;
     dkc = dk;
@@ -247,14 +300,20 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
   const int blocks = A.nA + A.nB + nC;
   if (blocks == 0) return DDT_OK;
   hipStream_t st = (hipStream_t)stream;
-  const size_t lds = (n_gdn > 0 && mode == DDT_COMMIT_REPLAY) ? GdnLds(P->n_max, A.R, dkc).total : 0;
-#define DDT_COMMIT(TT, DD)                                                                  \
-  do {                                                                                      \
-    (void)hipFuncSetAttribute((const void *)commit_kernel<TT, DD>,                          \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);        \
-    hipLaunchKernelGGL((commit_kernel<TT, DD>), dim3(blocks), dim3(256), lds, st, A);      \
-  } while (0)
   const bool bf = (n_gdn == 0) || gdn_dtype == DDT_BF16;
+  const size_t lds = (n_gdn > 0 && mode == DDT_COMMIT_REPLAY) ? GdnLds(P->n_max).total : 0;
+#define DDT_COMMIT3(TT, DD, MM)                                                           \
+  do {                                                                                    \
+    (void)hipFuncSetAttribute((const void *)commit_kernel<TT, DD, MM>,                    \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);      \
+    hipLaunchKernelGGL((commit_kernel<TT, DD, MM>), dim3(blocks), dim3(256), lds, st, A); \
+  } while (0)
+#define DDT_COMMIT(TT, DD)                                                         \
+  do {                                                                             \
+    if (mode == DDT_COMMIT_REPLAY) DDT_COMMIT3(TT, DD, DDT_COMMIT_REPLAY);         \
+    else if (mode == DDT_COMMIT_SELECT) DDT_COMMIT3(TT, DD, DDT_COMMIT_SELECT);    \
+    else DDT_COMMIT3(TT, DD, DDT_COMMIT_UPDATE);                                   \
+  } while (0)
   switch (dkc) {
     case 16: if (bf) DDT_COMMIT(uint16_t, 16); else DDT_COMMIT(float, 16); break;
     case 32: if (bf) DDT_COMMIT(uint16_t, 32); else DDT_COMMIT(float, 32); break;
@@ -262,6 +321,7 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
     default: if (bf) DDT_COMMIT(uint16_t, 128); else DDT_COMMIT(float, 128); break;
   }
 #undef DDT_COMMIT
+#undef DDT_COMMIT3
   r = launch_status();
   if (r || n_attn == 0) return r;
   hipLaunchKernelGGL(commit_len_kernel, dim3((P->B + 63) / 64), dim3(64), 0, st, A);

@@ -35,11 +35,17 @@ __device__ __forceinline__ float load1(const float *p) { return *p; }
 
 // ---------------------------------------------------------------- plan access
 // A sequence's node range, clamped so that a corrupt tree_off can never
-// send a kernel outside the per-node arrays.
+// send a kernel outside the per-node arrays.  A single tree is nodes
+// 0..n_total-1 and costs no load (the device plan flags a tree_off that
+// says otherwise).
 struct Seq {
   int o, n;
 };
 __device__ __forceinline__ Seq seq_of(const ddt_plan &P, int b) {
+  if (P.B == 1) {
+    const int n = P.n_total < P.n_max ? P.n_total : P.n_max;
+    return {0, n < 0 ? 0 : n};
+  }
   int o = P.tree_off[b], e = P.tree_off[b + 1];
   o = o < 0 ? 0 : (o > P.n_total ? P.n_total : o);
   e = e < o ? o : (e > P.n_total ? P.n_total : e);
@@ -75,12 +81,6 @@ __device__ __forceinline__ void ld8f(const float *p, float (&f)[8]) {
 __device__ __forceinline__ void st8f(float *p, const float (&f)[8]) {
   reinterpret_cast<float4 *>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
   reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
-}
-
-// rows per workgroup of the gated delta-net kernels for key width dk
-__host__ __device__ inline int gdn_rows(int dk, int dv) {
-  int r = 256 / (dk / 8);
-  return r > dv ? dv : r;
 }
 
 }  // namespace ddt

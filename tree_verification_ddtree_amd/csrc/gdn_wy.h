@@ -1,5 +1,5 @@
 // Gated delta rule over a tree of tokens in its WY form (shared by the tree
-// kernel and the commit's replay).
+// kernel and the commit).
 //
 // Row r of a value head's state evolves on its own: for node i with parent
 // p, s_i = a_i s_p + u_i k_i with u_i = b_i (v_i - a_i s_p . k_i).  Unrolled
@@ -8,302 +8,610 @@
 //   s_p . x = P_i (S_c . x) + sum_{a ancestor of i} w(a,i) u_a (k_a . x)
 // with w(a,i) the product of the gates strictly between a and i and P_i the
 // product of the gates of all ancestors of i.  So, per row,
-//   u_i = b_i (v_i - a_i P_i D_i) - sum_a M(i,a) u_a,  M(i,a) = b_i a_i w(a,i) k_a.k_i
+//   u_i = b_i (v_i - a_i P_i D_i) - sum_a b_i a_i w(a,i) (k_a.k_i) u_a
 //   o_i = scale (a_i (P_i F_i + sum_a w(a,i) (k_a.q_i) u_a) + u_i k_i.q_i)
-//   s_i = a_i P_i S_c + sum_a a_i w(a,i) u_a k_a + u_i k_i
-// where D_i = S_c . k_i and F_i = S_c . q_i.  The products D, F and the
-// pair coefficients are independent work; only the scalar solve for u is
-// ordered, by tree level, and needs no cross-lane reduction.
+//   s_i = sum_a a_i w(a,i) u_a k_a + a_i P_i S_c + u_i k_i
+// where D_i = S_c . k_i and F_i = S_c . q_i.  Every dot product above is an
+// entry of one small matrix product, [S_c tile ; K] x [k_0 q_0 k_1 q_1 ...],
+// done on the matrix cores with operands fetched straight from global
+// memory.  The scalar part then runs with one lane per (node, 4 rows): the
+// lane walks its node's root path in registers, so no lane waits on
+// another.  Trees deeper than that register path fall back to a
+// level-by-level solve through LDS with per-node coefficient records.
 //
-// Every dot product is a lane-group sum whose value does not depend on the
-// position of the node in the batch, and every recurrence walks ancestors
-// in the same order (nearest first), so a node's state comes out bitwise the
-// same whether the tree or only its root path is processed.
+// Matrix-core precision: with bf16 inputs, k and q are bf16 already and the
+// fp32 committed rows are split exactly into three bf16 parts (8 + 8 + 8
+// significand bits), so every product is exact and only the fp32
+// accumulation rounds.  With fp32 inputs the fp32 matrix instruction is used.
+//
+// Every product entry depends only on its own row and column, and both
+// solves evaluate, for every node, the same sequence of fp32 operations
+// (ancestors nearest first), so a node's u and state come out bitwise the
+// same whether the tree, only its root path, or only the saved u of that
+// path is used.
 #pragma once
 #include "common.h"
 
 namespace ddt {
 
-// LDS carve-up, every array 16-byte aligned
+typedef float gf32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int GDN_R = 16;     // state rows per workgroup (one matrix-core row block)
+constexpr int GDN_MAXA = 8;   // nearest ancestors whose coefficients a node record keeps
+constexpr int GDN_PATH = 12;  // deepest tree (levels) the register path solve takes
+
+// Everything the level-by-level solve needs of one node (128 bytes).
+struct GdnRec {
+  int i, cnt;            // node; ancestors recorded (<= GDN_MAXA)
+  float bi, c1;          // b_i; -(a_i P_i)
+  float ai, P, kqd, wM;  // a_i; P_i; k_i . q_i; w(.,i) past the recorded ancestors
+  int a[GDN_MAXA];       // ancestors, nearest first (padding: i)
+  float m[GDN_MAXA];     // -(b_i a_i w(a,i) k_a . k_i)
+  float h[GDN_MAXA];     // w(a,i) k_a . q_i
+};
+
+// LDS carve-up, every array 16-byte aligned; per-node row data is
+// node-major ([node][16 rows]) so a lane's 4 rows are one 16-byte access.
 struct GdnLds {
-  size_t kq, v, al, be, P, kqd, anc, gid, dep, lvl, lvs, D, F, M, N, Wt, U, O, total;
-  __host__ __device__ GdnLds(int nmax, int R, int dk) {
+  int n16, gs;
+  size_t v, al, be, anc, lvl, pos, lvs, meta, Gm, D, F, U, O, rec, total;
+  __host__ __device__ GdnLds(int nmax) {
     auto up = [](size_t x) { return (x + 15) / 16 * 16; };
-    const size_t nn = (size_t)nmax * nmax * 4;
-    kq = 0;
-    v = up(kq + (size_t)nmax * 2 * dk * 4);  // k, q as fp32
-    al = up(v + (size_t)nmax * R * 4);
-    be = up(al + (size_t)nmax * 4);
-    P = up(be + (size_t)nmax * 4);
-    kqd = up(P + (size_t)nmax * 4);
-    anc = up(kqd + (size_t)nmax * 4);
-    gid = up(anc + (size_t)nmax * 8);
-    dep = up(gid + (size_t)nmax * 4);
-    lvl = up(dep + (size_t)nmax * 4);
-    lvs = up(lvl + (size_t)nmax * 4);
-    D = up(lvs + (size_t)(nmax + 1) * 4);
-    F = up(D + (size_t)R * nmax * 4);
-    M = up(F + (size_t)R * nmax * 4);
-    N = up(M + nn);
-    Wt = up(N + nn);
-    U = up(Wt + nn);
-    O = up(U + (size_t)R * nmax * 4);
-    total = up(O + (size_t)nmax * R * 4);
+    n16 = (nmax + 15) / 16 * 16;
+    gs = 2 * n16;
+    v = 0;                                       // [nmax][16] v of the tile's rows
+    al = up(v + (size_t)nmax * GDN_R * 4);       // [nmax]
+    be = up(al + (size_t)nmax * 4);              // [nmax]
+    anc = up(be + (size_t)nmax * 4);             // [nmax] u64, self included
+    lvl = up(anc + (size_t)nmax * 8);            // [nmax] nodes by level
+    pos = up(lvl + (size_t)nmax * 4);            // [nmax] position in lvl
+    lvs = up(pos + (size_t)nmax * 4);            // [nmax + 2] level starts
+    meta = up(lvs + (size_t)(nmax + 2) * 4);     // [4]: number of levels
+    Gm = up(meta + 16);                          // [n16][gs] k_a . (k|q)_j
+    D = up(Gm + (size_t)n16 * gs * 4);           // [nmax][16] S_c . k_j
+    F = up(D + (size_t)nmax * GDN_R * 4);        // [nmax][16] S_c . q_j
+    U = up(F + (size_t)nmax * GDN_R * 4);        // [nmax][16] u
+    O = up(U + (size_t)nmax * GDN_R * 4);        // [nmax][16] outputs
+    rec = up(O + (size_t)nmax * GDN_R * 4);      // [nmax] GdnRec (deep trees only)
+    total = up(rec + (size_t)nmax * sizeof(GdnRec));
   }
 };
 
 struct GdnView {
-  float *kq, *v, *al, *be, *P, *kqd, *D, *F, *M, *N, *Wt, *U, *O;
+  float *v, *al, *be, *Gm, *D, *F, *U, *O;
   unsigned long long *anc;
-  int *gid, *dep, *lvl, *lvs;
-  int nmax, R;
-  __device__ GdnView(char *base, const GdnLds &L, int nmax_, int R_) : nmax(nmax_), R(R_) {
-    kq = reinterpret_cast<float *>(base + L.kq);
+  int *lvl, *pos, *lvs, *meta;
+  GdnRec *rec;
+  int nmax, gs;
+  __device__ GdnView(char *base, const GdnLds &L, int nmax_) : nmax(nmax_), gs(L.gs) {
     v = reinterpret_cast<float *>(base + L.v);
     al = reinterpret_cast<float *>(base + L.al);
     be = reinterpret_cast<float *>(base + L.be);
-    P = reinterpret_cast<float *>(base + L.P);
-    kqd = reinterpret_cast<float *>(base + L.kqd);
     anc = reinterpret_cast<unsigned long long *>(base + L.anc);
-    gid = reinterpret_cast<int *>(base + L.gid);
-    dep = reinterpret_cast<int *>(base + L.dep);
     lvl = reinterpret_cast<int *>(base + L.lvl);
+    pos = reinterpret_cast<int *>(base + L.pos);
     lvs = reinterpret_cast<int *>(base + L.lvs);
+    meta = reinterpret_cast<int *>(base + L.meta);
+    Gm = reinterpret_cast<float *>(base + L.Gm);
     D = reinterpret_cast<float *>(base + L.D);
     F = reinterpret_cast<float *>(base + L.F);
-    M = reinterpret_cast<float *>(base + L.M);
-    N = reinterpret_cast<float *>(base + L.N);
-    Wt = reinterpret_cast<float *>(base + L.Wt);
     U = reinterpret_cast<float *>(base + L.U);
     O = reinterpret_cast<float *>(base + L.O);
+    rec = reinterpret_cast<GdnRec *>(base + L.rec);
   }
 };
 
-// closest ancestor of node i still in `bits` (indices grow along a root path)
+// closest ancestor of a node still in `bits` (indices grow along a root path)
 __device__ __forceinline__ int top_bit(unsigned long long bits) { return 63 - __clzll((long long)bits); }
 
-// dot of 8 local columns with an LDS row, finished over the lane group
-template <int LPR>
-__device__ __forceinline__ float ldot(const float (&a)[8], const float *b) {
-  float bb[8];
-  ld8f(b, bb);
-  float d0 = 0.f, d1 = 0.f;
+__device__ __forceinline__ gu32x4 ld16(const void *p) { return *reinterpret_cast<const gu32x4 *>(p); }
+
+// 16-byte piece of T -> 16 / sizeof(T) floats
+template <typename T>
+__device__ __forceinline__ void piece_f32(gu32x4 x, float *f) {
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    d0 = fmaf(a[e], bb[e], d0);
-    d1 = fmaf(a[e + 4], bb[e + 4], d1);
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(x[i] << 16);
+      f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(x[i]);
   }
-  return group_sum<LPR>(d0 + d1);
-}
-template <int LPR>
-__device__ __forceinline__ float ldot2(const float *a, const float *b) {
-  float aa[8];
-  ld8f(a, aa);
-  return ldot<LPR>(aa, b);
 }
 
-// Stage the inputs of nodes gid[0..n) (global ids, already in LDS):
-// k and q rows of key head g as fp32, v of the tile's rows, gates.
-template <typename T, int DK>
-__device__ void gdn_stage(GdnView &V, int n, const T *__restrict__ q, const T *__restrict__ k,
-                          const T *__restrict__ v, const T *__restrict__ alpha,
-                          const T *__restrict__ beta, int Hk, int Hv, int dv, int g, int h,
-                          int row0) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  constexpr int U = 16 / (int)sizeof(T);  // elements per 16-byte piece
-  constexpr int PPR = DK / U;             // pieces per k or q row
-  constexpr int MAXP = 8;                 // pieces staged in registers per thread
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const int np = n * 2 * PPR;
-  auto src = [&](int idx) -> const u32x4 * {
-    const int j = idx / (2 * PPR), which = (idx / PPR) & 1, pc = idx % PPR;
-    return reinterpret_cast<const u32x4 *>((which ? q : k) + ((size_t)V.gid[j] * Hk + g) * DK) + pc;
-  };
-  auto put = [&](int idx, u32x4 x) {
-    const int j = idx / (2 * PPR), which = (idx / PPR) & 1, pc = idx % PPR;
-    float *dst = V.kq + ((size_t)j * 2 + which) * DK + pc * U;
-    if constexpr (sizeof(T) == 2) {
-      float f[8];
+// piece idx of the per-node v rows (16 / sizeof(T) elements) -> LDS fp32
+template <typename T>
+__device__ __forceinline__ void put_v(GdnView &V, int idx, gu32x4 x) {
+  constexpr int UE = 16 / (int)sizeof(T), VP = GDN_R / UE;
+  float f[UE];
+  piece_f32<T>(x, f);
+  float *dst = V.v + (idx / VP) * GDN_R + (idx % VP) * UE;
+  *reinterpret_cast<gf32x4 *>(dst) = gf32x4{f[0], f[1], f[2], f[3]};
+  if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(dst + 4) = gf32x4{f[4], f[5], f[6], f[7]};
+}
+
+// exact three-way split of 8 fp32 values into bf16 parts hi, mid, lo
+__device__ __forceinline__ void split3(gf32x4 x0, gf32x4 x1, gu32x4 (&o)[3]) {
+  unsigned short p[3][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(x[i] << 16);
-        f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
-      }
-      st8f(dst, f);
-    } else {
-      *reinterpret_cast<u32x4 *>(dst) = x;
+  for (int e = 0; e < 8; ++e) {
+    const float x = e < 4 ? x0[e] : x1[e - 4];
+    const unsigned u0 = __float_as_uint(x);
+    const float r1 = x - __uint_as_float(u0 & 0xffff0000u);
+    const unsigned u1 = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+    p[0][e] = (unsigned short)(u0 >> 16);
+    p[1][e] = (unsigned short)(u1 >> 16);
+    p[2][e] = (unsigned short)(__float_as_uint(r2) >> 16);
+  }
+#pragma unroll
+  for (int part = 0; part < 3; ++part)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[part][w] = (unsigned)p[part][2 * w] | ((unsigned)p[part][2 * w + 1] << 16);
+}
+
+// Everything a workgroup reads for node set j = 0..n-1 (global node gid(j))
+// and the committed rows row0..row0+15 of value head h (Srows), with the
+// matrix-core products done on the way:
+//   v of the 16 rows, gates, ancestor masks (anc_of(j), self included) -> LDS
+//   D, F (committed rows x k, q) and Gm (keys x k, q) -> LDS
+// Every global load of a thread is issued before its first use.  Operand
+// layouts of the products (16 x 16 output): lane l feeds A row l%16 and B
+// column l%16 with its share of the reduction dimension (k = 8(l/16) ..
+// 8(l/16)+7 of each 32-wide step for the bf16 form; the contiguous quarter
+// (l/16) of the channels for the 16x16x4 fp32 form) and receives rows
+// 4(l/16) .. 4(l/16)+3 of column l%16.  Column c of kq is k (even c) or q
+// (odd c) of node c/2; row block 0 is the committed tile, row block 1+m the
+// keys of nodes 16m .. 16m+15.  Wave w takes column blocks w, w+4, ...
+template <typename T, int DK, class Gid, class Anc>
+__device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__restrict__ q,
+                          const T *__restrict__ k, const T *__restrict__ v,
+                          const T *__restrict__ alpha, const T *__restrict__ beta,
+                          const float *__restrict__ Srows, int Hk, int Hv, int dv, int g, int h,
+                          int row0) {
+  constexpr int UE = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int VP = GDN_R / UE;           // pieces of one node's 16 v entries
+  constexpr int MAXRB = DDT_MAX_NODES / 16;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = nth >> 6;
+  const int lane = tid & 63, i16 = lane & 15, kk = lane >> 4;
+  const int nrb = (n + 15) / 16, ncb = (2 * n + 15) / 16;
+  const gu32x4 z = {0u, 0u, 0u, 0u};
+  auto vsrc = [&](int idx) {
+    return *(reinterpret_cast<const gu32x4 *>(v + ((size_t)gid(idx / VP) * Hv + h) * dv + row0) + idx % VP);
+  };
+  auto put_vs = [&](gu32x4 first) {
+    const int nv = n * VP;
+    if (tid < nv) put_v<T>(V, tid, first);
+    for (int idx = tid + nth; idx < nv; idx += nth) put_v<T>(V, idx, vsrc(idx));
+  };
+  // ---- per-node inputs (loads first, stores once the product loads are out)
+  const gu32x4 vb = vsrc(min(tid, n * VP - 1));
+  const int jt = min(tid, n - 1);
+  const float a0 = load1(alpha + (size_t)gid(jt) * Hv + h);
+  const float b0 = load1(beta + (size_t)gid(jt) * Hv + h);
+  const unsigned long long m0 = anc_of(jt);
+  auto kq_row = [&](int c) -> const T * {  // column c of kq, c < 2n
+    return ((c & 1) ? q : k) + ((size_t)gid(c >> 1) * Hk + g) * DK;
+  };
+  auto store_D = [&](int c, const gf32x4 &acc) {
+    if (c < 2 * n) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
     }
   };
-  // every global load of this thread first (clamped indices), then the stores
-  u32x4 buf[MAXP];
+  auto store_G = [&](int c, int m, const gf32x4 &g4) {
+    if (c < 2 * n) {
 #pragma unroll
-  for (int u = 0; u < MAXP; ++u) buf[u] = *src(min(tid + u * nth, np - 1));
-  float vb[4];
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * m + 4 * kk + e;
+        if (a < n) V.Gm[a * V.gs + c] = g4[e];
+      }
+    }
+  };
+  if (wave >= ncb) put_vs(vb);
+  if constexpr (sizeof(T) == 2) {
+    constexpr int NS = (DK + 31) / 32;
+    gu32x4 sa[3][NS], ka[MAXRB][NS], bv[NS];
+    if (wave < ncb) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = min(tid + u * nth, n * V.R - 1);
-    vb[u] = load1(v + ((size_t)V.gid[idx / V.R] * Hv + h) * dv + row0 + idx % V.R);
+      for (int s = 0; s < NS; ++s) {
+        const int k0 = 32 * s + 8 * kk;
+        gf32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+        if (k0 < DK) {
+          x0 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
+          x1 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
+        }
+        gu32x4 t3[3];
+        split3(x0, x1, t3);
+#pragma unroll
+        for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
+      }
+#pragma unroll
+      for (int m = 0; m < MAXRB; ++m)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int k0 = 32 * s + 8 * kk, a = 16 * m + i16;
+          ka[m][s] = (m < nrb && a < n && k0 < DK) ? ld16(k + ((size_t)gid(a) * Hk + g) * DK + k0) : z;
+        }
+    }
+    for (int cb = wave; cb < ncb; cb += nw) {
+      const int c = 16 * cb + i16;
+      const T *bsrc = kq_row(min(c, 2 * n - 1));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int k0 = 32 * s + 8 * kk;
+        bv[s] = (c < 2 * n && k0 < DK) ? ld16(bsrc + k0) : z;
+      }
+      if (cb == wave) put_vs(vb);
+      gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int part = 2; part >= 0; --part)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[part][s]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s]), acc, 0, 0, 0);
+      store_D(c, acc);
+#pragma unroll
+      for (int m = 0; m < MAXRB; ++m) {
+        if (m < nrb) {
+          gf32x4 g4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s]),
+                                                         __builtin_bit_cast(gbf16x8, bv[s]), g4, 0, 0, 0);
+          store_G(c, m, g4);
+        }
+      }
+    }
+  } else {
+    constexpr int KS = DK / 4;  // channels per lane group
+    constexpr int NP = KS / 4;  // float4 pieces per operand
+    const gf32x4 zf = {0.f, 0.f, 0.f, 0.f};
+    gf32x4 sa[NP], ka[MAXRB][NP], bv[NP];
+    if (wave < ncb) {
+#pragma unroll
+      for (int s = 0; s < NP; ++s) sa[s] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + kk * KS + 4 * s);
+#pragma unroll
+      for (int m = 0; m < MAXRB; ++m)
+#pragma unroll
+        for (int s = 0; s < NP; ++s) {
+          const int a = 16 * m + i16;
+          ka[m][s] = (m < nrb && a < n)
+                         ? *reinterpret_cast<const gf32x4 *>(k + ((size_t)gid(a) * Hk + g) * DK + kk * KS + 4 * s)
+                         : zf;
+        }
+    }
+    auto prod = [&](const gf32x4 *A) {
+      gf32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s][0], bv[s][0], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s][1], bv[s][1], c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s][2], bv[s][2], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s][3], bv[s][3], c1, 0, 0, 0);
+      }
+      return c0 + c1;
+    };
+    for (int cb = wave; cb < ncb; cb += nw) {
+      const int c = 16 * cb + i16;
+      const T *bsrc = kq_row(min(c, 2 * n - 1));
+#pragma unroll
+      for (int s = 0; s < NP; ++s)
+        bv[s] = c < 2 * n ? *reinterpret_cast<const gf32x4 *>(bsrc + kk * KS + 4 * s) : zf;
+      if (cb == wave) put_vs(vb);
+      store_D(c, prod(sa));
+#pragma unroll
+      for (int m = 0; m < MAXRB; ++m)
+        if (m < nrb) store_G(c, m, prod(ka[m]));
+    }
   }
-  const int jt = min(tid, n - 1);
-  const float a0 = load1(alpha + (size_t)V.gid[jt] * Hv + h);
-  const float b0 = load1(beta + (size_t)V.gid[jt] * Hv + h);
-#pragma unroll
-  for (int u = 0; u < MAXP; ++u)
-    if (tid + u * nth < np) put(tid + u * nth, buf[u]);
-  for (int idx = tid + MAXP * nth; idx < np; idx += nth) put(idx, *src(idx));
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (tid + u * nth < n * V.R) V.v[tid + u * nth] = vb[u];
-  for (int idx = tid + 4 * nth; idx < n * V.R; idx += nth)
-    V.v[idx] = load1(v + ((size_t)V.gid[idx / V.R] * Hv + h) * dv + row0 + idx % V.R);
   if (tid < n) {
     V.al[tid] = a0;
     V.be[tid] = b0;
+    V.anc[tid] = m0;
   }
   for (int j = tid + nth; j < n; j += nth) {
-    V.al[j] = load1(alpha + (size_t)V.gid[j] * Hv + h);
-    V.be[j] = load1(beta + (size_t)V.gid[j] * Hv + h);
+    V.al[j] = load1(alpha + (size_t)gid(j) * Hv + h);
+    V.be[j] = load1(beta + (size_t)gid(j) * Hv + h);
+    V.anc[j] = anc_of(j);
   }
 }
 
-// Products with the committed rows and the per-node coefficients.
-// Thread (lr, cg) owns columns c0..c0+7 of tile row lr; sc = those values.
-// want_F: also S_c . q (outputs); coefs for nodes [0, n).
-template <int LPR, int DK>
-__device__ void gdn_products(GdnView &V, int n, const float (&sc)[8], int lr, int cg,
-                             bool want_F) {
-  const int c0 = cg * 8;
-  // four nodes at a time so the lane-group sums of independent dots overlap
-  for (int j0 = 0; j0 < n; j0 += 4) {
-    float d[4], f[4];
+// Levels of a tree (max depth + 1) from the masks, by one wavefront; the
+// result is the same in every lane.
+__device__ __forceinline__ int gdn_nlev(int n, unsigned long long a) {
+  const int lane = threadIdx.x & 63;
+  int d = lane < n ? __popcll(a) : 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = min(j0 + u, n - 1);
-      d[u] = ldot<LPR>(sc, V.kq + (size_t)j * 2 * DK + c0);
-      f[u] = want_F ? ldot<LPR>(sc, V.kq + ((size_t)j * 2 + 1) * DK + c0) : 0.f;
-    }
-    if (cg == 0) {
+  for (int o = 32; o >= 1; o >>= 1) d = max(d, __shfl_xor(d, o));
+  return d;
+}
+
+// ------------------------------------------------------------ register path solve
+// One lane per (node i, rows r0..r0+3): u of every node on i's root path,
+// root first, then i's outputs.  Requires every node's depth < GDN_PATH.
+template <bool WANT_O>
+__device__ void gdn_path_solve(GdnView &V, int n, float scale) {
+  const int i = threadIdx.x & 63, r0 = (threadIdx.x >> 6) * 4;
+  if (i >= n || r0 >= GDN_R) return;
+  const unsigned long long anc = V.anc[i] & ((2ull << i) - 1);
+  const int d = min(__popcll(anc) - 1, GDN_PATH - 1);
+  int p[GDN_PATH];
+  {
+    unsigned long long bits = anc;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (j0 + u < n) {
-          V.D[lr * V.nmax + j0 + u] = d[u];
-          V.F[lr * V.nmax + j0 + u] = f[u];
-        }
+    for (int k = 0; k < GDN_PATH; ++k) {
+      p[k] = bits ? __ffsll((long long)bits) - 1 : i;
+      bits &= bits - 1;
     }
   }
-  // pair coefficients: row group lr takes nodes i = lr, lr + R, ...
-  for (int i = lr; i < n; i += V.R) {
-    const float *ki = V.kq + (size_t)i * 2 * DK + c0;
-    const float *qi = V.kq + ((size_t)i * 2 + 1) * DK + c0;
-    const float ai = V.al[i], ba = V.be[i] * ai;
-    unsigned long long bits = V.anc[i] & ~(1ull << i);
+  float al[GDN_PATH], be[GDN_PATH];
+  gf32x4 Dk[GDN_PATH], vk[GDN_PATH];
+#pragma unroll
+  for (int k = 0; k < GDN_PATH; ++k)
+    if (k <= d) {
+      al[k] = V.al[p[k]];
+      be[k] = V.be[p[k]];
+      Dk[k] = *reinterpret_cast<const gf32x4 *>(V.D + p[k] * GDN_R + r0);
+      vk[k] = *reinterpret_cast<const gf32x4 *>(V.v + p[k] * GDN_R + r0);
+    }
+  gf32x4 u[GDN_PATH], ul = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < GDN_PATH; ++k) {
+    if (k <= d) {
+      const float ba = be[k] * al[k];
+      float w = 1.f;
+      gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = k - 1; j >= 0; --j) {  // ancestors nearest first
+        const float m = -(ba * (w * V.Gm[p[j] * V.gs + 2 * p[k]]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(m, u[j][e], acc[e]);
+        w *= al[j];
+      }
+      const float c1 = -(al[k] * w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[k][e] = fmaf(be[k], fmaf(c1, Dk[k][e], vk[k][e]), acc[e]);
+      if (k == d) ul = u[k];
+    }
+  }
+  *reinterpret_cast<gf32x4 *>(V.U + i * GDN_R + r0) = ul;
+  if (WANT_O) {
+    float w = 1.f, ai = 0.f;
+    gf32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = GDN_PATH - 1; j >= 0; --j) {
+      if (j == d) ai = al[j];
+      if (j < d) {
+        const float hh = w * V.Gm[p[j] * V.gs + 2 * i + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(hh, u[j][e], y[e]);
+        w *= al[j];
+      }
+    }
+    const gf32x4 Fi = *reinterpret_cast<const gf32x4 *>(V.F + i * GDN_R + r0);
+    const float kqd = V.Gm[i * V.gs + 2 * i + 1];
+    gf32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = scale * fmaf(ai, fmaf(w, Fi[e], y[e]), ul[e] * kqd);
+    *reinterpret_cast<gf32x4 *>(V.O + i * GDN_R + r0) = o;
+  }
+}
+
+// ------------------------------------------------------------ deep-tree solve
+// Level lists, run by one wavefront: lane j < n holds node j's ancestor mask.
+// lvl = nodes ordered by (depth, index), pos = inverse, lvs[d] = first
+// position of depth d, meta[0] = number of levels.
+__device__ void gdn_levels(GdnView &V, int n, unsigned long long a) {
+  const int lane = threadIdx.x & 63;
+  const bool on = lane < n;
+  const int d = on ? __popcll(a) - 1 : 64;
+  // depths of a plan's tree are contiguous (0..levels-1); the bound on dd
+  // keeps a corrupt mask from looping, and pos stays in range regardless
+  int base = 0, pos = min(lane, n - 1), dd = 0;
+  for (; dd < 64 && base < n; ++dd) {
+    const unsigned long long m = __ballot(d == dd);
+    if (d == dd) pos = base + __popcll(m & ((1ull << lane) - 1));
+    if (lane == 0) V.lvs[dd] = base;
+    base += __popcll(m);
+  }
+  if (lane == 0) {
+    V.lvs[dd] = n;
+    V.meta[0] = dd;
+  }
+  if (on) {
+    V.lvl[pos] = lane;
+    V.pos[lane] = pos;
+  }
+}
+
+// Next (up to) eight ancestors of a node from `bits`, nearest first; -1 pads.
+__device__ __forceinline__ void next8(unsigned long long &bits, int (&a)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    a[t] = bits ? top_bit(bits) : -1;
+    if (a[t] >= 0) bits &= ~(1ull << a[t]);
+  }
+}
+
+// One record per node, stored at its level-order position.
+__device__ void gdn_records(GdnView &V, int n) {
+  static_assert(GDN_MAXA == 8, "records hold eight ancestors");
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    GdnRec R;
+    const float ai = V.al[i], bi = V.be[i], ba = bi * ai;
+    unsigned long long bits = V.anc[i] & ((1ull << i) - 1);
+    int a[8];
+    next8(bits, a);
+    float G[8], H[8], A[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int x = a[t] < 0 ? i : a[t];
+      G[t] = V.Gm[x * V.gs + 2 * i];
+      H[t] = V.Gm[x * V.gs + 2 * i + 1];
+      A[t] = V.al[x];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float w = 1.f;
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (a[t] >= 0) {
+        R.a[t] = a[t];
+        R.m[t] = -(ba * (w * G[t]));
+        R.h[t] = w * H[t];
+        w *= A[t];
+        ++cnt;
+      } else {
+        R.a[t] = i;
+        R.m[t] = 0.f;
+        R.h[t] = 0.f;
+      }
+    }
+    R.wM = w;
+    while (bits) {
+      const int x = top_bit(bits);
+      bits &= ~(1ull << x);
+      w *= V.al[x];
+    }
+    R.i = i;
+    R.cnt = cnt;
+    R.bi = bi;
+    R.ai = ai;
+    R.P = w;
+    R.c1 = -(ai * w);
+    R.kqd = V.Gm[i * V.gs + 2 * i + 1];
+    V.rec[min(V.pos[i], n - 1)] = R;
+  }
+}
+
+// u (and, when WANT_O, the output) of one node for row r.  The node's loads
+// go out first, then `between` runs (the caller's prefetch), then the
+// arithmetic: the same operations, in the same order, as the path solve.
+template <bool WANT_O, class Between>
+__device__ __forceinline__ void gdn_node(GdnView &V, const GdnRec &R, int n, int r, float scale,
+                                         Between between) {
+  // indices are clamped so that even a corrupt plan cannot send a read
+  // outside the arrays
+  const int i = min((unsigned)R.i, (unsigned)(n - 1));
+  float Ua[GDN_MAXA];
+#pragma unroll
+  for (int t = 0; t < GDN_MAXA; ++t) Ua[t] = V.U[min((unsigned)R.a[t], (unsigned)(n - 1)) * GDN_R + r];
+  const float Di = V.D[i * GDN_R + r], vi = V.v[i * GDN_R + r];
+  const float Fi = WANT_O ? V.F[i * GDN_R + r] : 0.f;
+  between();
+  __builtin_amdgcn_sched_barrier(0);
+  float acc = 0.f, y = 0.f;
+#pragma unroll
+  for (int t = 0; t < GDN_MAXA; ++t)
+    if (t < R.cnt) {
+      acc = fmaf(R.m[t], Ua[t], acc);
+      if (WANT_O) y = fmaf(R.h[t], Ua[t], y);
+    }
+  if (R.cnt == GDN_MAXA) {  // ancestors past the recorded ones
+    unsigned long long bits = V.anc[i] & ((1ull << (R.a[GDN_MAXA - 1] & 63)) - 1) & ((1ull << i) - 1);
+    const float ba = R.bi * R.ai;
+    float w = R.wM;
     while (bits) {
       const int a = top_bit(bits);
       bits &= ~(1ull << a);
-      const float *ka = V.kq + (size_t)a * 2 * DK + c0;
-      const float G = ldot2<LPR>(ka, ki);
-      const float H = want_F ? ldot2<LPR>(ka, qi) : 0.f;
-      if (cg == 0) {
-        V.Wt[i * V.nmax + a] = w;
-        V.M[i * V.nmax + a] = ba * (w * G);
-        V.N[i * V.nmax + a] = w * H;
-      }
+      const float ua = V.U[a * GDN_R + r];
+      acc = fmaf(-(ba * (w * V.Gm[a * V.gs + 2 * i])), ua, acc);
+      if (WANT_O) y = fmaf(w * V.Gm[a * V.gs + 2 * i + 1], ua, y);
       w *= V.al[a];
     }
-    const float kqv = want_F ? ldot2<LPR>(ki, qi) : 0.f;
-    if (cg == 0) {
-      V.P[i] = w;
-      V.kqd[i] = kqv;
-    }
   }
+  const float u = fmaf(R.bi, fmaf(R.c1, Di, vi), acc);
+  V.U[i * GDN_R + r] = u;
+  if (WANT_O) V.O[i * GDN_R + r] = scale * fmaf(R.ai, fmaf(R.P, Fi, y), u * R.kqd);
 }
 
-// Level lists from dep[0..n): lvl = nodes ordered by (depth, index),
-// lvs[d] = first position of depth d.  Returns the number of levels.
-__device__ int gdn_levels(GdnView &V, int n) {
-  int maxd = 0;
-  for (int j = 0; j < n; ++j) maxd = max(maxd, V.dep[j]);
-  for (int t = threadIdx.x; t < n; t += blockDim.x) {
-    const int d = V.dep[t];
-    int pos = 0;
-    for (int j = 0; j < n; ++j) pos += (V.dep[j] < d) || (V.dep[j] == d && j < t);
-    V.lvl[pos] = t;
-  }
-  for (int d = threadIdx.x; d <= maxd + 1; d += blockDim.x) {
-    int c = 0;
-    for (int j = 0; j < n; ++j) c += V.dep[j] < d;
-    V.lvs[d] = c;
-  }
-  return maxd + 1;
-}
-
-// u for every (row, node), level by level.  Of the nth = R * lanes-per-row
-// active threads, thread t handles row t / TS and slot t % TS; a row's threads share one wavefront, so results of one level
-// are visible to the next without a workgroup barrier.
-__device__ void gdn_solve(GdnView &V, int nlev, int nth) {
-  const int TS = nth / V.R;
-  const int r = threadIdx.x / TS, slot = threadIdx.x % TS;
-  float *Ur = V.U + r * V.nmax;
-  for (int d = 0; d < nlev; ++d) {
-    for (int s = V.lvs[d] + slot; s < V.lvs[d + 1]; s += TS) {
-      const int i = V.lvl[s];
-      const float ai = V.al[i];
-      float u = V.be[i] * fmaf(-(ai * V.P[i]), V.D[r * V.nmax + i], V.v[i * V.R + r]);
-      unsigned long long bits = V.anc[i] & ~(1ull << i);
-      while (bits) {
-        const int a = top_bit(bits);
-        bits &= ~(1ull << a);
-        u = fmaf(-V.M[i * V.nmax + a], Ur[a], u);
-      }
-      Ur[i] = u;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-// outputs o_i of every (row, node) into O[node][row]
-__device__ void gdn_outputs(GdnView &V, int n, float scale, int nth) {
-  const int TS = nth / V.R;
-  const int r = threadIdx.x / TS, slot = threadIdx.x % TS;
-  const float *Ur = V.U + r * V.nmax;
-  for (int i = slot; i < n; i += TS) {
-    float y = V.P[i] * V.F[r * V.nmax + i];
-    unsigned long long bits = V.anc[i] & ~(1ull << i);
-    while (bits) {
-      const int a = top_bit(bits);
-      bits &= ~(1ull << a);
-      y = fmaf(V.N[i * V.nmax + a], Ur[a], y);
-    }
-    V.O[i * V.R + r] = scale * fmaf(V.al[i], y, Ur[i] * V.kqd[i]);
-  }
-}
-
-// state of node i for this lane's 8 columns of row lr
-template <int DK>
-__device__ __forceinline__ void gdn_state(GdnView &V, int i, const float (&sc)[8], int lr, int cg,
-                                          float (&s)[8]) {
-  const int c0 = cg * 8;
-  const float *Ur = V.U + lr * V.nmax;
-  const float ai = V.al[i];
-  const float cs = ai * V.P[i];
+__device__ __forceinline__ GdnRec load_rec(const GdnView &V, int p) {
+  GdnRec R;
+  const gu32x4 *src = reinterpret_cast<const gu32x4 *>(V.rec + p);
+  gu32x4 *dst = reinterpret_cast<gu32x4 *>(&R);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = cs * sc[e];
-  unsigned long long bits = V.anc[i] & ~(1ull << i);
+  for (int t = 0; t < (int)(sizeof(GdnRec) / 16); ++t) dst[t] = src[t];
+  return R;
+}
+
+// Level-by-level solve for deep trees.  Needs 256 threads: thread t handles
+// row t / 16 and slot t % 16; a row's threads share one wavefront, so the
+// results of one level are visible to the next without a workgroup
+// barrier.  Level starts live in one register (lane d holds lvs[d]); the
+// record of the next level is loaded while the current one is computed.
+template <bool WANT_O>
+__device__ void gdn_level_solve(GdnView &V, int n, float scale) {
+  const int r = threadIdx.x >> 4, slot = threadIdx.x & 15, lane = threadIdx.x & 63;
+  const int nlev = __builtin_amdgcn_readfirstlane(V.meta[0]);
+  const int lvv = V.lvs[min(lane, nlev)];
+  auto lvs = [&](int d) { return d >= nlev ? n : __builtin_amdgcn_readlane(lvv, d); };
+  int p = slot, pe = lvs(1);
+  GdnRec cur = load_rec(V, min(p, n - 1)), nxt;
+  for (int d = 0; d < nlev; ++d) {
+    const int pn = lvs(d + 1) + slot, pen = lvs(d + 2);
+    auto prefetch = [&]() { nxt = load_rec(V, min(pn, n - 1)); };
+    if (p < pe)
+      gdn_node<WANT_O>(V, cur, n, r, scale, prefetch);
+    else
+      prefetch();
+    for (int q = p + 16; q < pe; q += 16) gdn_node<WANT_O>(V, load_rec(V, min(q, n - 1)), n, r, scale, [] {});
+    __builtin_amdgcn_wave_barrier();
+    cur = nxt;
+    p = pn;
+    pe = pen;
+  }
+}
+
+// The whole scalar part after the products, called by every thread of a
+// 256-thread workgroup after a barrier that follows gdn_front.  `nlev`
+// (levels of the tree) must be the same in every thread.
+template <bool WANT_O>
+__device__ void gdn_scalar(GdnView &V, int n, int nlev, float scale) {
+  if (nlev <= GDN_PATH) {
+    gdn_path_solve<WANT_O>(V, n, scale);
+  } else {
+    if (threadIdx.x < 64) gdn_levels(V, n, threadIdx.x < n ? V.anc[threadIdx.x] : 0ull);
+    __syncthreads();
+    gdn_records(V, n);
+    __syncthreads();
+    gdn_level_solve<WANT_O>(V, n, scale);
+  }
+}
+
+// State of node i for columns c0..c0+7 of committed row Srow (global), from
+// the keys (global rows krow(a)), the gates and u (LDS) of the node and its
+// ancestors.  The same operations, in the same order, as the commit's
+// rebuild from saved u.
+template <class KRow>
+__device__ __forceinline__ void gdn_state(const GdnView &V, int i, int r, int c0, const float *Srow,
+                                          KRow krow, float (&s)[8]) {
+  const float ai = V.al[i];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.f;
+  unsigned long long bits = V.anc[i] & ((1ull << i) - 1);
+  float w = 1.f;
   while (bits) {
     const int a = top_bit(bits);
     bits &= ~(1ull << a);
-    const float c = (ai * V.Wt[i * V.nmax + a]) * Ur[a];
+    const float c = (ai * w) * V.U[a * GDN_R + r];
     float ka[8];
-    ld8f(V.kq + (size_t)a * 2 * DK + c0, ka);
+    load8(krow(a) + c0, ka);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = fmaf(c, ka[e], s[e]);
+    w *= V.al[a];
   }
-  float ki[8];
-  ld8f(V.kq + (size_t)i * 2 * DK + c0, ki);
-  const float ui = Ur[i];
+  float sc[8], ki[8];
+  ld8f(Srow + c0, sc);
+  load8(krow(i) + c0, ki);
+  const float cs = ai * w, ui = V.U[i * GDN_R + r];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = fmaf(ui, ki[e], s[e]);
+  for (int e = 0; e < 8; ++e) s[e] = fmaf(ui, ki[e], fmaf(cs, sc[e], s[e]));
 }
 
 }  // namespace ddt

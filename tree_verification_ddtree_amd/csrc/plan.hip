@@ -60,6 +60,7 @@ __global__ __launch_bounds__(64) void plan_kernel(ddt_plan P, int max_levels) {
   unsigned st = 0;
   int o = P.tree_off[b], e = P.tree_off[b + 1];
   if (!(o >= 0 && e > o && e <= P.n_total && e - o <= P.n_max)) st |= DDT_ST_TREE;
+  if (P.B == 1 && (o != 0 || e != P.n_total)) st |= DDT_ST_TREE;
   Seq s = seq_of(P, b);
   o = s.o;
   const int n = s.n;
