@@ -493,68 +493,86 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   }
 }
 
-// Merge the splits of one query row: one workgroup per row.  The split
-// weights 2^((m_s - M) c) go to LDS, then each thread sums 4 channels over a
-// strided subset of the splits and the subsets are added in a fixed order.
+// Merge the splits of one query row: one workgroup per row.  Every thread
+// first issues the loads of its share of the partial outputs (4 channels x
+// splits sg, sg + SG, ...); meanwhile wavefront 0 turns the split maxima
+// and sums into weights 2^((m_s - M) c) and the total L.  The weighted sums
+// are then added in a fixed order, so the result does not depend on timing.
 constexpr int MAX_SPLITS = 1024;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
-  constexpr int TPR = D / 4;        // threads per channel sweep
-  constexpr int SG = 256 / TPR;     // split groups
+  constexpr int TPR = D / 4;     // threads per channel sweep
+  constexpr int SG = 256 / TPR;  // split groups
+  constexpr int BATCH = 16;      // partial loads in flight per thread
   __shared__ float wts[MAX_SPLITS];
-  __shared__ float red[256];
+  __shared__ float Lsh;
   __shared__ float4 part[SG][TPR];
   const int rl = blockIdx.x, g = blockIdx.y, b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
   const Seq s = seq_of(A.P, b);
   const int rho = rg * A.rows_wg + rl;
   if (rho >= A.G * s.n) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int nsp = n_active_splits(A, ctx_len(A, b, nullptr));
   const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
-  float m = -INFINITY;
-  for (int sp = tid; sp < nsp; sp += 256) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
-  red[tid] = m;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float l = 0.f;
-  for (int sp = tid; sp < nsp; sp += 256) {
-    const float2 ml = A.ML[base + (size_t)sp * A.rows_wg];
-    const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f((ml.x - M) * A.c);
-    wts[sp] = wgt;
-    l = fmaf(ml.y, wgt, l);
-  }
-  red[tid] = l;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (tid < k) red[tid] += red[tid + k];
-    __syncthreads();
-  }
-  const float L = red[0];
   const int dc = tid % TPR, sg = tid / TPR;
+  const float *src = A.Opart + base * D + 4 * dc;
+  const size_t sstride = (size_t)A.rows_wg * D;
+  float4 v[BATCH];
+#pragma unroll
+  for (int t = 0; t < BATCH; ++t) {
+    const int sp = sg + t * SG;
+    v[t] = sp < nsp ? *reinterpret_cast<const float4 *>(src + sp * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (tid < 64) {
+    float m = -INFINITY;
+    for (int sp = lane; sp < nsp; sp += 64) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+    for (int sp = lane; sp < nsp; sp += 64) {
+      const float2 ml = A.ML[base + (size_t)sp * A.rows_wg];
+      const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f((ml.x - m) * A.c);
+      wts[sp] = wgt;
+      l = fmaf(ml.y, wgt, l);
+    }
+    // fixed-order total: lane partials gathered in lane order
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_down(l, o);
+      if ((lane & (2 * o - 1)) == 0) l += t;
+    }
+    if (lane == 0) Lsh = l;
+  }
+  __syncthreads();
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int sp = sg; sp < nsp; sp += SG) {
+#pragma unroll
+  for (int t = 0; t < BATCH; ++t) {
+    const int sp = sg + t * SG;
+    if (sp < nsp) {
+      const float wgt = wts[sp];
+      acc.x = fmaf(v[t].x, wgt, acc.x);
+      acc.y = fmaf(v[t].y, wgt, acc.y);
+      acc.z = fmaf(v[t].z, wgt, acc.z);
+      acc.w = fmaf(v[t].w, wgt, acc.w);
+    }
+  }
+  for (int sp = sg + BATCH * SG; sp < nsp; sp += SG) {
     const float wgt = wts[sp];
-    const float4 v = *reinterpret_cast<const float4 *>(A.Opart + (base + (size_t)sp * A.rows_wg) * D + 4 * dc);
-    acc.x = fmaf(v.x, wgt, acc.x);
-    acc.y = fmaf(v.y, wgt, acc.y);
-    acc.z = fmaf(v.z, wgt, acc.z);
-    acc.w = fmaf(v.w, wgt, acc.w);
+    const float4 x = *reinterpret_cast<const float4 *>(src + sp * sstride);
+    acc.x = fmaf(x.x, wgt, acc.x);
+    acc.y = fmaf(x.y, wgt, acc.y);
+    acc.z = fmaf(x.z, wgt, acc.z);
+    acc.w = fmaf(x.w, wgt, acc.w);
   }
   part[sg][dc] = acc;
   __syncthreads();
   if (sg == 0) {
     for (int k = 1; k < SG; ++k) {
-      const float4 v = part[k][dc];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      const float4 x = part[k][dc];
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
     }
-    const float inv = 1.f / L;
+    const float inv = 1.f / Lsh;
     const int node = rho / A.G, hq = g * A.G + rho % A.G;
     *reinterpret_cast<float4 *>(A.out + ((size_t)(s.o + node) * A.Hq + hq) * D + 4 * dc) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
