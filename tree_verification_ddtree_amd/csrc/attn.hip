@@ -88,14 +88,22 @@ template <int D>
 struct Lds {
   // K stage: [32 rows][D] halves; row r = 16*tt + m holds the key that the
   // score MFMA of key-half tt reads as A-row m; the 16-byte chunk c of a row
-  // sits at chunk position c ^ (r & 7).
+  // sits at chunk position c ^ ksw(r).
   // V stage: [D channels][4 groups][8 keys] halves; group q of channel d
-  // sits at slot q ^ ((d >> 1) & 3).
+  // sits at slot q ^ vsw(d).
+  // Both swizzles give the 16 lanes that read one 16-byte slot each in a
+  // matrix-core operand load 16 different bank groups.
   static constexpr int K_HALVES = TILE * D;
   static constexpr int V_HALVES = TILE * D;
   static constexpr int STAGE = K_HALVES + V_HALVES;
 };
-constexpr int NSTAGE = 4;
+constexpr int NSTAGE = 4;  // LDS ring depth: NSTAGE - 1 tiles in flight
+
+// K rows are whole bank periods (256 B) long, so rows r and r + 8 collide
+// without the low four row bits in the swizzle; V channel rows are a quarter
+// period, so channels d and d + 4 share banks unless bits 2-3 of d enter.
+__device__ __forceinline__ int ksw(int r) { return r & 15; }
+__device__ __forceinline__ int vsw(int d) { return (d >> 2) & 3; }
 
 // tile-local key tau (0..31) <-> K row in LDS
 __device__ __forceinline__ int krow_of(int tau) {
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       const int piece = w + 4 * k;
       const int P = piece * 64 + lane;       // chunk position in the stage
       const int r = P / CPR, cpos = P % CPR;  // K row and chunk slot
-      const int cc = cpos ^ (r & 7);
+      const int cc = cpos ^ ksw(r);
       const int tau = key_of_krow(r);
       const int pg = tau < 16 ? pg0 : pg1;
       const _Float16 *src = A.Kc + (((size_t)pg * A.Hkv + kv_head) * DDT_PAGE + (tau & 15)) * D + 8 * cc;
@@ -198,11 +206,25 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       const int piece = w + 4 * k;
       const int P = piece * 64 + lane;
       const int d = P >> 2, slot = P & 3;
-      const int qg = slot ^ ((d >> 1) & 3);
+      const int qg = slot ^ vsw(d);
       const int pg = (qg >> 1) ? pg1 : pg0;
       const _Float16 *src = A.Vc + (((size_t)pg * A.Hkv + kv_head) * D + d) * DDT_PAGE + 8 * (qg & 1);
       __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Vs + piece * 512), 16, 0, 0);
     }
+  };
+
+  // wait until at most `later` tiles' direct loads are outstanding (each
+  // tile is 2 * WAVE_CH loads per wave); the counts are immediates
+  auto wait_tiles = [&](int later) {
+    static_assert(NSTAGE <= 5, "wait_tiles covers up to three later tiles");
+    if (later >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * WAVE_CH) : "memory");
+    else if (later == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * WAVE_CH) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
   // ---- ragged cache tile or tree tile -> LDS stage through registers,
@@ -228,12 +250,12 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         for (int x = 0; x < 8; ++x) vx[x] = A.Vc[(pg * D + 8 * cc + x) * DDT_PAGE + (key & 15)];
       }
       const int r = krow_of(tau);
-      *reinterpret_cast<uint4 *>(Ks + r * D + 8 * (cc ^ (r & 7))) = kx;
+      *reinterpret_cast<uint4 *>(Ks + r * D + 8 * (cc ^ ksw(r))) = kx;
       const int qg = tau >> 3, e = tau & 7;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int d = 8 * cc + x;
-        Vs[d * 32 + 8 * (qg ^ ((d >> 1) & 3)) + e] = vx[x];
+        Vs[d * 32 + 8 * (qg ^ vsw(d)) + e] = vx[x];
       }
     }
   };
@@ -251,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       for (int tt = 0; tt < 2; ++tt) {
         const int r = 16 * tt + l16;
         const int cc = 4 * ks + lq;
-        const half8 kf = *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ (r & 7)));
+        const half8 kf = *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ ksw(r)));
 #pragma unroll
         for (int j = 0; j < NB; ++j)
           S[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[j][ks], S[tt][j], 0, 0, 0);
@@ -316,18 +338,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   auto kfrag = [&](const _Float16 *Ks, int tt, int ks) -> half8 {
     const int r = 16 * tt + l16;
     const int cc = 4 * ks + lq;
-    return *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ (r & 7)));
+    return *reinterpret_cast<const half8 *>(Ks + r * D + 8 * (cc ^ ksw(r)));
   };
   auto vfrag = [&](const _Float16 *Vs, int n) -> half8 {
     const int d = 16 * n + l16;
-    return *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ ((d >> 1) & 3)));
+    return *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ vsw(d)));
   };
   // One full tile of the main loop: scores of the next tile (Ks1) while the
   // probabilities and value product of this tile (S, Vs0) are formed.
   // sched_barrier fences keep each batch of LDS reads one batch ahead of
   // the MFMAs that consume it and put the softmax next to the score MFMAs.
   auto tile_step = [&](const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
-                       f32x4 (&Sn)[2][NB]) {
+                       f32x4 (&Sn)[2][NB], auto &&in_shadow) {
     constexpr int KH = KS / 2;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -338,6 +360,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     for (int ks = 0; ks < KH; ++ks)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) ka[tt][ks] = kfrag(Ks1, tt, ks);
+    __builtin_amdgcn_sched_barrier(0);
+    in_shadow();  // work that needs no fragment, done while they arrive
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KH; ++ks)
@@ -387,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int n = 0; n < DB; ++n) {
       const int d = 16 * n + l16;
-      const half8 vf = *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ ((d >> 1) & 3)));
+      const half8 vf = *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ vsw(d)));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[j], o[j][n], 0, 0, 0);
@@ -405,19 +429,15 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int n = 0; n < DB; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // ---- main loop over full tiles: 4-stage LDS ring with up to three
-    // tiles in flight; the scores of tile it+1 are formed while the
+    // ---- main loop over full tiles: NSTAGE-stage LDS ring with up to
+    // NSTAGE - 1 tiles in flight; the scores of tile it+1 are formed while the
     // probabilities and value product of tile it are worked on.
     if (n_full > 0) {
-      issue_tile(0, 0);
-      if (n_full > 1) issue_tile(1, 1);
-      if (n_full > 2) issue_tile(2, 2);
-      if (n_full > 2)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * WAVE_CH) : "memory");
-      else if (n_full > 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < NSTAGE - 1; ++t)
+        if (t < n_full) issue_tile(t, t);
+      // wait for tile 0: the loads of the later tiles may stay outstanding
+      wait_tiles(min(n_full, NSTAGE - 1) - 1);
       __syncthreads();
       f32x4 Sn[2][NB];
       qk(0, Sn);
@@ -433,23 +453,21 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         }
       }
       for (int it = 0; it < n_full; ++it) {
-        if (it + 1 < n_full) {
-          if (it + 2 < n_full)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
-          else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+        // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
+        if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
         __syncthreads();  // tile it+1 landed; every wave is past tile it-1
-        if (it + 3 < n_full) issue_tile(it + 3, (it + 3) % NSTAGE);
         // scores of tile it+1 (past the last tile they read a stale stage
-        // and are dropped), probabilities and value product of tile it
+        // and are dropped), probabilities and value product of tile it; the
+        // loads of tile it+3 go out while the first K fragments arrive
         f32x4 Sc[2][NB];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
         tile_step(lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
-                  lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn);
+                  lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
+                    if (it + NSTAGE - 1 < n_full) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+                  });
       }
     }
     // ---- epilogue: ragged cache tile, then the tree tiles
