@@ -61,7 +61,7 @@ struct AttnArgs {
   int T_max;
   int Hq, Hkv, G;
   float c;  // scale * log2(e)
-  int chunk, n_splits, n_rg, rows_wg;
+  int n_splits, n_rg, rows_wg;
   float *Opart;  // [B][Hkv][n_rg][n_splits][rows_wg][D]
   float2 *ML;    // [B][Hkv][n_rg][n_splits][rows_wg]
   float *out;    // [n_total][Hq][D]
@@ -78,8 +78,18 @@ __device__ __forceinline__ int ctx_len(const AttnArgs &A, int b, bool *cut) {
   return t;
 }
 
+// Keys per split of a sequence with Tb committed tokens: the sequence's own
+// length spread over the splits, in whole tiles, so every active split gets
+// the same number of tiles (give or take one).
+__device__ __forceinline__ int split_chunk(const AttnArgs &A, int Tb) {
+  int c = (Tb + A.n_splits - 1) / A.n_splits;
+  c = (c + TILE - 1) / TILE * TILE;
+  return c < TILE ? TILE : c;
+}
+
 __device__ __forceinline__ int n_active_splits(const AttnArgs &A, int Tb) {
-  int n = (Tb + A.chunk - 1) / A.chunk;
+  const int chunk = split_chunk(A, Tb);
+  int n = (Tb + chunk - 1) / chunk;
   n = n < 1 ? 1 : n;
   return n > A.n_splits ? A.n_splits : n;
 }
@@ -137,8 +147,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   if (split >= nsp) return;
   if (cut && split == 0 && g == 0 && rg == 0 && threadIdx.x == 0) A.P.status[b] |= DDT_ST_CTX;
 
-  const int t_beg = split * A.chunk;
-  const int t_end = min(Tb, t_beg + A.chunk);
+  const int chunk = split_chunk(A, Tb);
+  const int t_beg = split * chunk;
+  const int t_end = min(Tb, t_beg + chunk);
   const int n_keys = t_end > t_beg ? t_end - t_beg : 0;
   const int n_full = n_keys / TILE;                      // direct-load tiles
   const bool has_part = (n_keys % TILE) != 0;            // ragged last cache tile
@@ -769,7 +780,6 @@ extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, c
   A.Hkv = Hkv;
   A.G = Hq / Hkv;
   A.c = scale * LOG2E;
-  A.chunk = c.chunk;
   A.n_splits = c.n_splits;
   A.n_rg = c.n_rg;
   A.rows_wg = c.rows_wg;

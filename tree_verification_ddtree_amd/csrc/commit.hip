@@ -35,51 +35,85 @@ __device__ __forceinline__ int path_node(const CommitArgs &A, int b, int r, int 
   return (x >= 0 && x < n) ? x : 0;
 }
 
-// UPDATE: state of the last path node for 8 columns of one committed row,
-// rebuilt from the u saved by the tree kernel.  Same sequence of fp32
-// operations as gdn_state (ancestors nearest first), so the result is
-// bitwise the state the tree kernel would persist; all loads of a batch of
-// eight ancestors are issued before any arithmetic, and nothing goes
-// through LDS.
+// UPDATE rows per pass (every thread owns 8 columns of one row per pass)
+// and passes per workgroup.
+template <int DK>
+struct UpdShape {
+  static constexpr int LPR = DK / 8, RPP = 256 / LPR, PASSES = 4, ROWS = RPP * PASSES;
+  static_assert(ROWS == (256 / (DK / 8)) * 4, "host computes the same row count");
+};
+
+// UPDATE: the committed rows row0 .. row0 + ROWS - 1 (clipped to dv) of one
+// value head become the state of the last path node, rebuilt from the u
+// the tree kernel saved.  Per row, the same sequence of fp32 operations as
+// gdn_state (ancestors nearest first), so the result is bitwise the state
+// the tree kernel would persist.  The path's keys and gates are loaded once
+// for all rows of the workgroup; nothing goes through LDS.
 template <typename T, int DK>
-__device__ void commit_update_row(const CommitArgs &A, const ddt_gdn_layer &lay, const Seq &s, int b,
-                                  int h, int row, int c0, int Lb, float *Srow) {
+__device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay, const Seq &s, int b,
+                                   int h, int row0, int Lb, float *Shead) {
+  using SH = UpdShape<DK>;
   const T *k = (const T *)lay.k, *al = (const T *)lay.alpha;
   const int g = h / (A.Hv / A.Hk);
-  auto uidx = [&](int gn) { return ((size_t)gn * A.Hv + h) * A.dv + row; };
-  float sc[8], ki[8];
-  ld8f(Srow, sc);
+  const int tid = threadIdx.x, c0 = (tid % SH::LPR) * 8, rsub = tid / SH::LPR;
+  auto uidx = [&](int gn, int row) { return ((size_t)gn * A.Hv + h) * A.dv + row; };
+  int rows[SH::PASSES];
+  bool on[SH::PASSES];
+  float acc[SH::PASSES][8], sc[SH::PASSES][8], ui[SH::PASSES];
   const int gi = s.o + path_node(A, b, Lb - 1, s.n);
+#pragma unroll
+  for (int p = 0; p < SH::PASSES; ++p) {
+    const int r = row0 + rsub + SH::RPP * p;
+    on[p] = r < A.dv;
+    rows[p] = on[p] ? r : row0;
+    ld8f(Shead + (size_t)rows[p] * DK + c0, sc[p]);
+    ui[p] = lay.node_u[uidx(gi, rows[p])];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
+  }
+  float ki[8];
   load8(k + ((size_t)gi * A.Hk + g) * DK + c0, ki);
   const float ai = load1(al + (size_t)gi * A.Hv + h);
-  const float ui = lay.node_u[uidx(gi)];
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float w = 1.f;
   for (int r0 = Lb - 2; r0 >= 0; r0 -= 8) {
-    float ka[8][8], aa[8], ua[8];
+    float ka[8][8], aa[8];
+    int ga[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int ga = s.o + path_node(A, b, max(r0 - t, 0), s.n);
-      load8(k + ((size_t)ga * A.Hk + g) * DK + c0, ka[t]);
-      aa[t] = load1(al + (size_t)ga * A.Hv + h);
-      ua[t] = lay.node_u[uidx(ga)];
+      ga[t] = s.o + path_node(A, b, max(r0 - t, 0), s.n);
+      load8(k + ((size_t)ga[t] * A.Hk + g) * DK + c0, ka[t]);
+      aa[t] = load1(al + (size_t)ga[t] * A.Hv + h);
     }
+    float cw[8];  // a_i w(a,i) of each ancestor, nearest first
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       if (r0 - t >= 0) {
-        const float c = (ai * w) * ua[t];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(c, ka[t][e], acc[e]);
+        cw[t] = ai * w;
         w *= aa[t];
       }
+#pragma unroll
+    for (int p = 0; p < SH::PASSES; ++p) {
+      float ua[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ua[t] = lay.node_u[uidx(ga[t], rows[p])];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (r0 - t >= 0) {
+          const float c = cw[t] * ua[t];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[p][e] = fmaf(c, ka[t][e], acc[p][e]);
+        }
+    }
   }
   const float cs = ai * w;
-  float s8[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s8[e] = fmaf(ui, ki[e], fmaf(cs, sc[e], acc[e]));
-  st8f(Srow, s8);
+  for (int p = 0; p < SH::PASSES; ++p) {
+    if (!on[p]) continue;
+    float s8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8[e] = fmaf(ui[p], ki[e], fmaf(cs, sc[p][e], acc[p][e]));
+    st8f(Shead + (size_t)rows[p] * DK + c0, s8);
+  }
 }
 
 template <typename T, int DK, int MODE>
@@ -116,8 +150,8 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
       if (tid == 0) atomicOr((unsigned *)&A.P.status[b], DDT_ST_COMMIT);
       return;
     }
-    if (lane_on)
-      commit_update_row<T, DK>(A, lay, s, b, h, row0 + lr, c0, Lb, Sbase + lr * DK + c0);
+    commit_update_rows<T, DK>(A, lay, s, b, h, tile * UpdShape<DK>::ROWS, Lb,
+                              lay.S_c + ((size_t)b * A.Hv + h) * A.dv * DK);
     return;
   }
   // Replay: the tree kernel's evaluation restricted to the accepted path, a
@@ -280,7 +314,12 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
     if (conv_dtype != DDT_BF16 && conv_dtype != DDT_F32) return DDT_E_DTYPE;
     if (C < 0 || C % 8) return DDT_E_SHAPE;
     A.Hk = Hk; A.Hv = Hv; A.dk = dk; A.dv = dv; A.gdt = gdn_dtype; A.C = C; A.cdt = conv_dtype;
-    A.tiles = dv / GDN_R;
+    if (mode == DDT_COMMIT_UPDATE) {
+      const int rows = (256 / (dk / 8)) * 4;  // UpdShape<dk>::ROWS
+      A.tiles = (dv + rows - 1) / rows;
+    } else {
+      A.tiles = dv / GDN_R;
+    }
     A.nA = n_gdn * P->B * Hv * A.tiles;
     A.nB = (C > 0) ? n_gdn * P->B : 0;
     dkc = dk;
