@@ -44,6 +44,12 @@ def _dev(a, device):
     return torch.from_numpy(a).to(device)
 
 
+def headroom(warmup=5, steps=20, kernel_reps=5):
+    """Steps the context must have room for: each step commits up to N tokens
+    (warmup, timed steps, two eager passes of kernel_reps steps, graph capture)."""
+    return warmup + steps + 2 * kernel_reps + 8
+
+
 class Stack:
     """Device-resident inputs, outputs and descriptors of one verify step."""
 
@@ -105,33 +111,58 @@ class Stack:
         al = [ddt.AttnLayer(a["Kt"].data_ptr(), a["Vt"].data_ptr(), K.data_ptr(), Vv.data_ptr())
               for a, (K, Vv) in zip(self.attn, self.kv)]
         self.gdn_table, self.attn_table = ddt.layer_table(gl, device), ddt.layer_table(al, device)
-        self.attn_events = None
+        self.timer = None  # {op: [(start, end) events]} while timing eager steps
+
+    def _timed(self, name, fn):
+        """Run one call; with the timer on, bracket it with HIP events on the
+        current stream (every call of this benchmark uses it)."""
+        if self.timer is None or name not in self.timer:
+            return fn()
+        import torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.timer[name].append((a, b))
 
     def step(self, stream=None):
         ddt, c = self.ddt, self.c
-        ddt.ddt_tree_plan(self.tb, c["levels"], stream)
+        self._timed("plan", lambda: ddt.ddt_tree_plan(self.tb, c["levels"], stream))
         gi = 0
         for a in range(c["n_attn"]):
             for _ in range(c["n_gdn"] // c["n_attn"]):
-                x, g = self.conv[gi], self.gdn[gi]
-                ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0, self.conv_out[gi], stream)
-                ddt.ddt_tree_gdn(self.tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"],
-                                 1.0, self.gdn_out[gi], None, self.gdn_u[gi], stream)
+                x, g, l = self.conv[gi], self.gdn[gi], gi
+                self._timed("conv", lambda: ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0,
+                                                             self.conv_out[l], stream))
+                self._timed("gdn", lambda: ddt.ddt_tree_gdn(
+                    self.tb, g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S_c"], 1.0,
+                    self.gdn_out[l], None, self.gdn_u[l], stream))
                 gi += 1
             at, (K, V) = self.attn[a], self.kv[a]
-            ev = self.attn_events
-            if ev is not None:
-                ev[a][0].record()
-            ddt.ddt_tree_attn(self.tb, at["q"], K, V, None, self.T, self.T_max, at["Kt"], at["Vt"],
-                              self.attn_out[a], self.attn_ws, stream=stream)
-            if ev is not None:
-                ev[a][1].record()
-        ddt.ddt_accept_walk(self.tb, self.logits, self.tok, self.amax, self.path, self.L,
-                            self.bonus, self.walk_ws, stream)
-        ddt.ddt_commit_state(self.tb, self.path, self.L, ddt.DDT_COMMIT_UPDATE, self.gdn_table,
-                             c["n_gdn"], c["Hk"], c["Hv"], c["dk"], c["dv"], ddt.DDT_BF16, c["C"],
-                             ddt.DDT_BF16, self.attn_table, c["n_attn"], c["Hkv"], c["D"],
-                             ddt.DDT_F16, None, self.T, stream)
+            self._timed("attn", lambda: ddt.ddt_tree_attn(
+                self.tb, at["q"], K, V, None, self.T, self.T_max, at["Kt"], at["Vt"], self.attn_out[a],
+                self.attn_ws, stream=stream))
+        self._timed("walk", lambda: ddt.ddt_accept_walk(self.tb, self.logits, self.tok, self.amax,
+                                                        self.path, self.L, self.bonus, self.walk_ws,
+                                                        stream))
+        self._timed("commit", lambda: ddt.ddt_commit_state(
+            self.tb, self.path, self.L, ddt.DDT_COMMIT_UPDATE, self.gdn_table, c["n_gdn"], c["Hk"],
+            c["Hv"], c["dk"], c["dv"], ddt.DDT_BF16, c["C"], ddt.DDT_BF16, self.attn_table, c["n_attn"],
+            c["Hkv"], c["D"], ddt.DDT_F16, None, self.T, stream))
+
+    def op_batches(self):
+        """Idempotent calls of the short ops for batch timing: every layer's
+        conv, every layer's delta-net, and the plan and walk (20 each)."""
+        ddt, c = self.ddt, self.c
+        conv = [lambda x=x, y=y: ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0, y)
+                for x, y in zip(self.conv, self.conv_out)]
+        gdn = [lambda g=g, o=o, u=u: ddt.ddt_tree_gdn(self.tb, g["q"], g["k"], g["v"], g["alpha"],
+                                                      g["beta"], g["S_c"], 1.0, o, None, u)
+               for g, o, u in zip(self.gdn, self.gdn_out, self.gdn_u)]
+        plan = [lambda: ddt.ddt_tree_plan(self.tb, c["levels"])] * 20
+        walk = [lambda: ddt.ddt_accept_walk(self.tb, self.logits, self.tok, self.amax, self.path,
+                                            self.L, self.bonus, self.walk_ws)] * 20
+        return {"plan": plan, "conv": conv, "gdn": gdn, "walk": walk}
 
     # ---------------------------------------------------------------- bytes
     def attn_bytes(self, T):
@@ -140,18 +171,30 @@ class Stack:
         kv = T * c["Hkv"] * c["D"] * 2 * 2
         return kv + N * c["Hq"] * c["D"] * 2 + N * c["Hkv"] * c["D"] * 2 * 2 + N * c["Hq"] * c["D"] * 4
 
-    def step_bytes(self, T, L):
-        """Algorithmic HBM bytes of one step: every input read once, every
-        output written once, plus the commit's state / prefix / K-V writes."""
+    def op_bytes(self, T, L):
+        """Algorithmic HBM bytes of one call of each op: every input read
+        once, every output written once (the commit: the new state, prefix
+        and K/V it writes; the delta-net call: the committed state it reads)."""
         c = self.c
-        N = c["N"]
-        gdn = (c["Hv"] * c["dv"] * c["dk"] * 4 * 2 + N * c["Hk"] * c["dk"] * 2 * 2
-               + N * c["Hv"] * c["dv"] * 2 + N * c["Hv"] * 2 * 2 + N * c["Hv"] * c["dv"] * 4)
-        W1 = c["W"] - 1
-        conv = (N * c["C"] * 2 + W1 * c["C"] * 2 * 2 + c["C"] * c["W"] * 2 + N * c["C"] * 4)
-        logits = N * synth.VOCAB * 2 + N * 4
-        append = L * c["Hkv"] * c["D"] * 2 * 2 * c["n_attn"]
-        return (c["n_attn"] * self.attn_bytes(T) + c["n_gdn"] * (gdn + conv) + logits + append)
+        N, W1 = c["N"], c["W"] - 1
+        state = c["Hv"] * c["dv"] * c["dk"] * 4
+        return {
+            "plan": N * 4 + N * (4 + 8 + 4 * max(W1, 1) + 4 + 4),
+            "conv": N * c["C"] * 2 + W1 * c["C"] * 2 + c["C"] * c["W"] * 2 + N * c["C"] * 4,
+            "gdn": (state + N * c["Hk"] * c["dk"] * 2 * 2 + N * c["Hv"] * c["dv"] * 2
+                    + N * c["Hv"] * 2 * 2 + N * c["Hv"] * c["dv"] * 4),
+            "attn": self.attn_bytes(T),
+            "walk": N * synth.VOCAB * 2 + N * 4 + N * 4 + N * 4 + 8,
+            "commit": (c["n_gdn"] * (state + W1 * c["C"] * 2)
+                       + L * c["Hkv"] * c["D"] * 2 * 2 * c["n_attn"]),
+        }
+
+    def step_bytes(self, T, L):
+        """Algorithmic HBM bytes of one step (the sum over its calls)."""
+        c = self.c
+        b = self.op_bytes(T, L)
+        per = {"plan": 1, "conv": c["n_gdn"], "gdn": c["n_gdn"], "attn": c["n_attn"], "walk": 1, "commit": 1}
+        return sum(per[k] * v for k, v in b.items())
 
 
 def _traffic(kernel_src_sha):
@@ -264,7 +307,7 @@ def main():
                           "launches": 3}), flush=True)
         return
     print(f"[bench] building the 128K stack (seed {args.seed})", file=sys.stderr, flush=True)
-    st = Stack(dev, seed=args.seed, headroom_steps=args.warmup + args.steps + args.kernel_reps + 8)
+    st = Stack(dev, seed=args.seed, headroom_steps=headroom(args.warmup, args.steps, args.kernel_reps))
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     print("[bench] warmup", file=sys.stderr, flush=True)
@@ -306,19 +349,54 @@ def main():
     if status.any():
         raise RuntimeError(f"device status {status}")
 
-    # dominant kernel: time every attention call of a few eager steps with
-    # HIP events on the launch stream
-    st.attn_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(st.c["n_attn"])]
-    durs = []
-    for _ in range(args.kernel_reps):
-        st.step()
+    # Per-op call times, with HIP events on the launch stream.  Attention (the
+    # dominant kernel) and the commit are timed call by call inside eager
+    # steps, one op per pass; the short ops (plan, conv, delta-net, walk) are
+    # timed as graph-replayed back-to-back batches under one event pair,
+    # because an event pair around a single few-microsecond call adds a gap
+    # of its own.
+    timer = {}
+    for op in ("attn", "commit"):
+        st.timer = {op: []}
+        for _ in range(args.kernel_reps):
+            st.step()
+            torch.cuda.synchronize()
+        timer[op] = [a.elapsed_time(b) for a, b in st.timer[op]]
+    st.timer = None
+    for op, calls in st.op_batches().items():
+        # the batch is captured in a HIP graph so that host launch cost does
+        # not enter the measurement (as for the timed step itself)
+        for fn in calls:  # one untimed eager round first
+            fn()
+        gb = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gb):
+            for fn in calls:
+                fn()
+        gb.replay()
         torch.cuda.synchronize()
-        durs += [a.elapsed_time(b) for a, b in st.attn_events]
-    st.attn_events = None
-    attn_ms = float(np.mean(durs))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.kernel_reps):
+            gb.replay()
+        b.record()
+        torch.cuda.synchronize()
+        timer[op] = [a.elapsed_time(b) / (args.kernel_reps * len(calls))]
+        del gb
     T_mid = (T_start + T_end) / 2
-    attn_bytes = st.attn_bytes(T_mid)
+    L_step = max(L_mean, 1.0)
+    ob = st.op_bytes(T_mid, L_step)
+    per_step = {"plan": 1, "conv": st.c["n_gdn"], "gdn": st.c["n_gdn"], "attn": st.c["n_attn"],
+                "walk": 1, "commit": 1}
+    kernels = {}
+    for op in ("plan", "conv", "gdn", "attn", "walk", "commit"):
+        us = float(np.mean(timer[op])) * 1e3
+        gbps = ob[op] / (us * 1e-6) / 1e9
+        kernels[op] = {"us_per_call": us, "calls_per_step": per_step[op], "bytes_per_call": ob[op],
+                       "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+                       "timed": "per call in eager steps" if op in ("attn", "commit")
+                       else "graph-replayed back-to-back batch"}
+    attn_ms = kernels["attn"]["us_per_call"] * 1e-3
+    attn_bytes = ob["attn"]
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     src = open(os.path.join(ROOT, "tree_verification_ddtree_amd", "csrc", "attn.hip"), "rb").read()
     traffic = _traffic(hashlib.sha256(src).hexdigest())
@@ -355,6 +433,7 @@ def main():
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
             "bytes_per_call": attn_bytes, "ms_per_call": attn_ms,
         },
+        "kernels": kernels,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -34,7 +34,7 @@ def hostin(t):
 def test_stack_128k_full_size_sampled(gpu):
     import bench
     banner("stack 48 gdn+conv / 16 attn, T=131072, N=22: sampled parity")
-    st = bench.Stack(gpu, seed=0, headroom_steps=38)  # bench's default headroom
+    st = bench.Stack(gpu, seed=0, headroom_steps=bench.headroom())  # the benchmark's default
     c = st.c
     N = c["N"]
     chk_g = [0, c["n_gdn"] - 1]
