@@ -9,11 +9,12 @@ on the hybrid stack of 48 gated delta-net layers and 16 attention layers at
 lucebox-hub README, "02 · DFlash DDtree", "Implemented here"; 128K context:
 same section, first list).
 
-    python bench.py [--steps K] [--warmup W] [--no-graph] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--settle S] [--no-graph] [--no-cpu-baseline]
 
 Prints ONE JSON line.  ``value`` is verify steps per second with every input
 already resident in HBM; the step is captured once in a HIP graph and
-replayed.  ``roofline`` is for the dominant kernel (tree attention: context
+replayed.  Before the timed steps, untimed replays keep the GPU busy for
+``--settle`` seconds (its clock ramps over a few hundred ms of load).  ``roofline`` is for the dominant kernel (tree attention: context
 split kernel + split combine, timed per call with HIP events on the launch
 stream); ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the
 same step.
@@ -44,10 +45,14 @@ def _dev(a, device):
     return torch.from_numpy(a).to(device)
 
 
+SETTLE_BATCH = 10  # settle-phase steps between restores of the committed length
+
+
 def headroom(warmup=5, steps=20, kernel_reps=5):
     """Steps the context must have room for: each step commits up to N tokens
-    (warmup, timed steps, two eager passes of kernel_reps steps, graph capture)."""
-    return warmup + steps + 2 * kernel_reps + 8
+    (warmup, timed steps, two eager passes of kernel_reps steps, graph capture,
+    one batch of the settle phase)."""
+    return warmup + steps + 2 * kernel_reps + 8 + SETTLE_BATCH
 
 
 class Stack:
@@ -280,6 +285,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5, help="eager steps timed per attention call")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed sustained steps before timing (the GPU clock ramps "
+                         "over a few hundred ms of load)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel "
                          "that scales the HBM byte counters of a profiler run)")
@@ -328,8 +336,28 @@ def main():
         except Exception as e:  # noqa: BLE001 - report and time eagerly instead
             print(f"[bench] graph capture failed ({e}); timing eager launches", file=sys.stderr)
             graph, use_graph = None, False
+    # The GPU clock ramps up over a few hundred ms of sustained load and falls
+    # back while the host builds the inputs, so untimed steps keep the GPU
+    # busy for --settle seconds first.  The committed length is put back
+    # after every batch, so the timed steps run at the configured context.
+    T_set = st.T.clone()
+    t_set = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_set < args.settle:
+        for _ in range(SETTLE_BATCH):
+            if graph is not None:
+                graph.replay()
+            else:
+                st.step()
+        st.T.copy_(T_set)
+        torch.cuda.synchronize()
+        n_settle += SETTLE_BATCH
+    status = st.tb.status.cpu().numpy()
+    if status.any():
+        raise RuntimeError(f"device status {status}")
     T_start = int(st.T.item())
-    print(f"[bench] timing {args.steps} steps (graph={use_graph})", file=sys.stderr, flush=True)
+    print(f"[bench] settled for {n_settle} steps; timing {args.steps} steps (graph={use_graph})",
+          file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -408,6 +436,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": n_settle,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",

@@ -495,7 +495,16 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       softmax(S, tree ? 2 : 1, kbase, pf);
       pv(0, pf);
     }
-    if (!__syncthreads_or(ovf)) break;
+    // any overflow in the workgroup?  The flags go through the first ring
+    // stage, idle by now (a block-wide vote would take static LDS, and the
+    // ring fills all of it)
+    __syncthreads();  // every wave is done reading the ring
+    int *flag = reinterpret_cast<int *>(lds);
+    if (lane == 0) flag[w] = __ballot(ovf) != 0ull;
+    __syncthreads();
+    const bool redo = (flag[0] | flag[1] | flag[2] | flag[3]) != 0;
+    __syncthreads();  // flags read before the ring is refilled
+    if (!redo) break;
     ovf = false;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
