@@ -157,7 +157,7 @@ def test_gdn_scale(gpu):
 
 # ------------------------------------------------------------------ attention
 def attn_case(gpu, trees, T, Hq, Hkv, D, dt, seed, paged=True, nan_fill=False, n_splits=0,
-              rows=None):
+              rows=None, plant=None):
     tb, par, off = make_batch(trees, 4, gpu)
     n, B = len(par), len(trees)
     T = np.asarray(T)
@@ -169,6 +169,8 @@ def attn_case(gpu, trees, T, Hq, Hkv, D, dt, seed, paged=True, nan_fill=False, n
                 K[pt[b][t // 16], :, t % 16, :] = np.nan
                 V[pt[b][t // 16], :, :, t % 16] = np.nan
     a = synth.attn_inputs(seed, (61,), n, Hq, Hkv, D, dt)
+    if plant is not None:  # edits the inputs in place (both sides see the same values)
+        plant(K, a, pt, off)
     use_pt = paged or B > 1
     ptd = dev(pt) if use_pt else None
     Td = dev(T.astype(np.int32))
@@ -226,6 +228,62 @@ def test_attn_full_context_32k_sampled(gpu):
     rows = [(int(i), int(h)) for i, h in zip(rng.integers(0, 22, 12), rng.integers(0, 24, 12))]
     rows += [(21, 23), (0, 0)]
     err, _ = attn_case(gpu, [tree], [32768], 24, 4, 256, "f16", 10, paged=False, rows=rows)
+    assert err < TOL
+
+
+# Tree sizes that select each row-half size of the paired-wave kernel (row
+# blocks of 16 query rows, two row halves) and, past 10 blocks, the
+# four-wave kernel; contiguous and paged caches, NaN in unused page slots,
+# batches, both head sizes, fixed and automatic split counts.
+ATTN_SHAPES = {
+    #  name: (tree sizes, T, Hq, Hkv, D, paged, nan_fill, n_splits)
+    "1_block": ([1], [100], 24, 4, 256, False, False, 0),
+    "2_blocks_batch": ([5, 3], [40, 700], 24, 4, 256, True, True, 0),
+    "4_blocks": ([10], [1000], 24, 4, 256, True, False, 5),
+    "6_blocks_batch": ([16, 9], [2100, 333], 24, 4, 256, True, True, 0),
+    "8_blocks": ([20], [1234], 24, 4, 256, False, False, 1),
+    "10_blocks": ([26], [3000], 24, 4, 256, True, True, 0),
+    "11_blocks_four_wave": ([27], [3000], 24, 4, 256, True, True, 0),
+    "d128_6_blocks": ([8, 12], [777, 1500], 16, 2, 128, True, False, 0),
+    "d128_10_blocks": ([20], [2500], 16, 2, 128, True, True, 3),
+}
+
+
+@pytest.mark.parametrize("case", list(ATTN_SHAPES))
+def test_attn_mfma_shapes(gpu, case):
+    sizes, T, Hq, Hkv, D, paged, nan_fill, ns = ATTN_SHAPES[case]
+    banner(f"attn mfma {case}: sizes {sizes} T {T} Hq {Hq} Hkv {Hkv} D {D} splits {ns}")
+    trees = [synth.random_tree(synth.rng_for(15, 68, b), n, 10) for b, n in enumerate(sizes)]
+    err, _ = attn_case(gpu, trees, T, Hq, Hkv, D, "f16", 15, paged=paged, nan_fill=nan_fill,
+                       n_splits=ns)
+    assert err < TOL
+
+
+def _plant_cache(t):
+    """Key at cache position t of sequence 0, KV head 0 := 4 q of node 0,
+    q head 0: that row's score there is ~4|q|^2, about 90 binades (at scale
+    1/16) above anything in the first tile of its split."""
+    def f(K, a, pt, off):
+        page = pt[0][t // 16]
+        K[page, 0, t % 16, :] = (4.0 * a["q"][off[0], 0].astype(np.float32)).astype(K.dtype)
+    return f
+
+
+def _plant_tree(K, a, pt, off):
+    """Draft key of node 0 (seen by every node), KV head 0 := 4 q of node 0."""
+    a["Kt"][off[0], 0] = (4.0 * a["q"][off[0], 0].astype(np.float32)).astype(a["Kt"].dtype)
+
+
+@pytest.mark.parametrize("where,size", [("cache", 22), ("tree", 22), ("cache", 64), ("tree", 64)])
+def test_attn_redo_after_overflow(gpu, where, size):
+    """A score far above its row's reference (fixed by the first tile) makes
+    the split run again against the true maxima; the result must still be
+    the plain softmax.  Size 22 runs the paired-wave kernel, 64 the
+    four-wave one."""
+    banner(f"attn overflow redo: planted {where} key, tree size {size}")
+    tree = synth.random_tree(synth.rng_for(16, 69), size, 8)
+    plant = _plant_cache(2960) if where == "cache" else _plant_tree
+    err, _ = attn_case(gpu, [tree], [3000], 24, 4, 256, "f16", 16, paged=True, plant=plant)
     assert err < TOL
 
 
