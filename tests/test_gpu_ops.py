@@ -231,10 +231,10 @@ def test_attn_full_context_32k_sampled(gpu):
     assert err < TOL
 
 
-# Tree sizes that select each row-half size of the paired-wave kernel (row
-# blocks of 16 query rows, two row halves) and, past 10 blocks, the
-# four-wave kernel; contiguous and paged caches, NaN in unused page slots,
-# batches, both head sizes, fixed and automatic split counts.
+# Tree sizes that give 1, 2 and 3 row blocks (16 query rows each) per
+# wavefront, with and without padding blocks; contiguous and paged caches,
+# NaN in unused page slots, batches, both head sizes, fixed and automatic
+# split counts.
 ATTN_SHAPES = {
     #  name: (tree sizes, T, Hq, Hkv, D, paged, nan_fill, n_splits)
     "1_block": ([1], [100], 24, 4, 256, False, False, 0),
@@ -243,7 +243,7 @@ ATTN_SHAPES = {
     "6_blocks_batch": ([16, 9], [2100, 333], 24, 4, 256, True, True, 0),
     "8_blocks": ([20], [1234], 24, 4, 256, False, False, 1),
     "10_blocks": ([26], [3000], 24, 4, 256, True, True, 0),
-    "11_blocks_four_wave": ([27], [3000], 24, 4, 256, True, True, 0),
+    "11_blocks": ([27], [3000], 24, 4, 256, True, True, 0),
     "d128_6_blocks": ([8, 12], [777, 1500], 16, 2, 128, True, False, 0),
     "d128_10_blocks": ([20], [2500], 16, 2, 128, True, True, 3),
 }
@@ -278,8 +278,7 @@ def _plant_tree(K, a, pt, off):
 def test_attn_redo_after_overflow(gpu, where, size):
     """A score far above its row's reference (fixed by the first tile) makes
     the split run again against the true maxima; the result must still be
-    the plain softmax.  Size 22 runs the paired-wave kernel, 64 the
-    four-wave one."""
+    the plain softmax.  Size 64 also spreads the rows over two workgroups."""
     banner(f"attn overflow redo: planted {where} key, tree size {size}")
     tree = synth.random_tree(synth.rng_for(16, 69), size, 8)
     plant = _plant_cache(2960) if where == "cache" else _plant_tree

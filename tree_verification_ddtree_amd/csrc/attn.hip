@@ -42,17 +42,12 @@
 //  - Each split writes unnormalised partial O^T, its reference max and the
 //    row sum; a combine kernel merges the splits in fixed order
 //    (deterministic, no atomics).
-#include <type_traits>
-
 #include "common.h"
 
 namespace ddt {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TILE = 32;  // keys per pipeline stage (two pages)
 constexpr float LOG2E = 1.4426950408889634f;
@@ -90,6 +85,18 @@ __device__ __forceinline__ int split_chunk(const AttnArgs &A, int Tb) {
   int c = (Tb + A.n_splits - 1) / A.n_splits;
   c = (c + TILE - 1) / TILE * TILE;
   return c < TILE ? TILE : c;
+}
+
+typedef __attribute__((address_space(4))) const int32_t cint32;
+
+// Page of cache position t of sequence b, t the same in every lane (the
+// first key of a tile).  The read goes through the scalar cache: waiting for
+// it uses the scalar counter, so it never forces the wave to wait for the
+// K/V tiles still in flight on the vector-memory counter.
+__device__ __forceinline__ int page_uniform(const AttnArgs &A, int b, int t) {
+  if (!A.pt) return t >> 4;
+  const int pg = __builtin_amdgcn_readfirstlane(t >> 4);
+  return *(const cint32 *)(A.pt + (size_t)b * A.max_pages + pg);
 }
 
 __device__ __forceinline__ int n_active_splits(const AttnArgs &A, int Tb) {
@@ -197,13 +204,14 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     return A.pt ? A.pt[(size_t)b * A.max_pages + (t >> 4)] : (t >> 4);
   };
   const size_t kv_head = (size_t)g;
+  // pages of the two halves of full tile it (read ahead of the barrier that
+  // precedes the tile's issue, so the barrier's own wait covers the read)
+  auto tile_page = [&](int it, int half) { return page_uniform(A, b, t_beg + it * TILE + 16 * half); };
 
   // ---- full cache tile -> LDS stage, straight from HBM (global_load_lds).
   // Wave w fills 1 KB pieces w, w+4, ...; lane l of a piece lands at byte
   // 16*l, so each lane fetches whichever chunk belongs there.
-  auto issue_tile = [&](int it, int stage) {
-    const int t0 = t_beg + it * TILE;
-    const int pg0 = page_of(t0), pg1 = page_of(t0 + 16);
+  auto issue_tile = [&](int it, int stage, int pg0, int pg1) {
     _Float16 *Ks = lds + stage * Lds<D>::STAGE;
     _Float16 *Vs = Ks + Lds<D>::K_HALVES;
 #pragma unroll
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     if (n_full > 0) {
 #pragma unroll
       for (int t = 0; t < NSTAGE - 1; ++t)
-        if (t < n_full) issue_tile(t, t);
+        if (t < n_full) issue_tile(t, t, tile_page(t, 0), tile_page(t, 1));
       // wait for tile 0: the loads of the later tiles may stay outstanding
       wait_tiles(min(n_full, NSTAGE - 1) - 1);
       __syncthreads();
@@ -469,6 +477,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         }
       }
       for (int it = 0; it < n_full; ++it) {
+        const int nt = it + NSTAGE - 1;  // tile issued in this iteration
+        const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
         // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
         if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
         __syncthreads();  // tile it+1 landed; every wave is past tile it-1
@@ -482,7 +492,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
           for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
         tile_step(lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
                   lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
-                    if (it + NSTAGE - 1 < n_full) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+                    if (nt < n_full) issue_tile(nt, nt % NSTAGE, npg0, npg1);
                   });
       }
     }
@@ -535,464 +545,6 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     for (int n = 0; n < DB; ++n)
       *reinterpret_cast<float4 *>(op + 16 * n) = make_float4(o[j][n][0], o[j][n][1], o[j][n][2], o[j][n][3]);
   }
-}
-
-// ------------------------------------------------------------ paired waves
-// The same split of the context, with the work of a tile divided so that no
-// wavefront computes scores or values for rows it does not own and each K/V
-// byte in LDS is read by two wavefronts instead of four.  Wave w = 2r + c
-// owns row half r (row blocks NBH*r .. NBH*r + NBH - 1 of the workgroup):
-//  - scores for key half c of every tile (S^T = K Q^T over 16 keys),
-//  - the value product for channel half c over all 32 keys of the tile.
-// The value product needs the probabilities of both key halves, so the two
-// waves of a row half swap their halves through LDS (8 bytes per lane and
-// row block).  Both must form probabilities against the same reference, so
-// every place that sets a row's reference max takes the larger of the two
-// halves' maxima.  Per tile the LDS carries 32 KB of K/V reads, 32 KB of
-// V reads and 20 KB of probability swaps, against 128 KB of fragment reads
-// when each wave reads the whole tile, and no row block is padding beyond
-// the last one of the sequence.
-template <int D, int NBH, int C>
-__device__ __forceinline__ void attn_pair_wave(const AttnArgs &A) {
-  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
-  constexpr int WAVE_CH = (TILE * CPR) / 256;  // direct loads per wave, per tensor and tile
-  constexpr int KS = D / 32;                   // k-steps of the score product
-  constexpr int DBH = D / 32;                  // channel blocks per half
-  constexpr int NBAT = 4;                      // fragment batches per tile
-  constexpr int KPB = KS / NBAT, VPB = DBH / NBAT;
-  extern __shared__ half8 lds_raw[];
-  _Float16 *lds = reinterpret_cast<_Float16 *>(lds_raw);
-  // probability halves [parity][wave][row block][lane], 4 halves each
-  u32x2 *pbuf = reinterpret_cast<u32x2 *>(lds + NSTAGE * Lds<D>::STAGE);
-  // per-row scalars swapped between the two waves of a row half
-  float *xch = reinterpret_cast<float *>(pbuf + 2 * 4 * NBH * 64);
-
-  const int split = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
-  const Seq s = seq_of(A.P, b);
-  const int rows_b = A.G * s.n;
-  const int row0 = rg * A.rows_wg;
-  if (row0 >= rows_b) return;
-  bool cut;
-  const int Tb = ctx_len(A, b, &cut);
-  const int nsp = n_active_splits(A, Tb);
-  if (split >= nsp) return;
-  if (cut && split == 0 && g == 0 && rg == 0 && threadIdx.x == 0) A.P.status[b] |= DDT_ST_CTX;
-
-  const int chunk = split_chunk(A, Tb);
-  const int t_beg = split * chunk;
-  const int t_end = min(Tb, t_beg + chunk);
-  const int n_keys = t_end > t_beg ? t_end - t_beg : 0;
-  const int n_full = n_keys / TILE;
-  const bool has_part = (n_keys % TILE) != 0;
-  const int n_tree = (split == nsp - 1) ? (s.n + TILE - 1) / TILE : 0;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = w >> 1, wp = w ^ 1;
-  constexpr int c = C;
-  const int l16 = lane & 15, lq = lane >> 4;
-  auto xi = [&](int wave, int j) { return (wave * NBH + j) * 64 + lane; };
-  auto pi = [&](int par, int wave, int j) { return ((par * 4 + wave) * NBH + j) * 64 + lane; };
-
-  // ---- resident Q fragments of this row half
-  half8 qf[NBH][KS];
-  bool blk_on[NBH];
-#pragma unroll
-  for (int j = 0; j < NBH; ++j) {
-    const int blk0 = row0 + 16 * (NBH * r + j);
-    blk_on[j] = blk0 < rows_b;
-    const int rho = blk0 + l16;
-    const bool ok = rho < rows_b;
-    const int node = ok ? rho / A.G : 0;
-    const int hq = g * A.G + (ok ? rho % A.G : 0);
-    const _Float16 *qp = A.q + ((size_t)(s.o + node) * A.Hq + hq) * D + 8 * lq;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ok)
-        qf[j][ks] = *reinterpret_cast<const half8 *>(qp + 32 * ks);
-      else
-        qf[j][ks] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
-  // tree mask of row l16 of block j (ancestors of its node, itself included);
-  // read when a tree tile needs it rather than held through the main loop
-  auto anc_row = [&](int j) -> unsigned long long {
-    const int rho = row0 + 16 * (NBH * r + j) + l16;
-    return rho < rows_b ? A.P.anc[s.o + rho / A.G] : 0ull;
-  };
-
-  f32x4 o[NBH][DBH];
-  float mrow[NBH], mseen[NBH], lsum[NBH];
-  bool ovf = false;
-#pragma unroll
-  for (int j = 0; j < NBH; ++j) mrow[j] = -INFINITY;
-
-  auto page_of = [&](int t) -> int {
-    return A.pt ? A.pt[(size_t)b * A.max_pages + (t >> 4)] : (t >> 4);
-  };
-  const size_t kv_head = (size_t)g;
-
-  // ---- full cache tile -> LDS stage, straight from HBM (global_load_lds);
-  // the same stage layout as the four-wave kernel
-  auto issue_tile = [&](int it, int stage) {
-    const int t0 = t_beg + it * TILE;
-    const int pg0 = page_of(t0), pg1 = page_of(t0 + 16);
-    _Float16 *Ks = lds + stage * Lds<D>::STAGE;
-    _Float16 *Vs = Ks + Lds<D>::K_HALVES;
-#pragma unroll
-    for (int k = 0; k < WAVE_CH; ++k) {
-      const int piece = w + 4 * k;
-      const int P = piece * 64 + lane;
-      const int rr = P / CPR, cpos = P % CPR;
-      const int cc = cpos ^ ksw(rr);
-      const int tau = key_of_krow(rr);
-      const int pg = tau < 16 ? pg0 : pg1;
-      const _Float16 *src = A.Kc + (((size_t)pg * A.Hkv + kv_head) * DDT_PAGE + (tau & 15)) * D + 8 * cc;
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Ks + piece * 512), 16, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < WAVE_CH; ++k) {
-      const int piece = w + 4 * k;
-      const int P = piece * 64 + lane;
-      const int d = P >> 2, slot = P & 3;
-      const int qg = slot ^ vsw(d);
-      const int pg = (qg >> 1) ? pg1 : pg0;
-      const _Float16 *src = A.Vc + (((size_t)pg * A.Hkv + kv_head) * D + d) * DDT_PAGE + 8 * (qg & 1);
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Vs + piece * 512), 16, 0, 0);
-    }
-  };
-  auto wait_tiles = [&](int later) {
-    static_assert(NSTAGE <= 5, "wait_tiles covers up to three later tiles");
-    if (later >= 3)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * WAVE_CH) : "memory");
-    else if (later == 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * WAVE_CH) : "memory");
-    else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-  // ragged cache tile or tree tile -> LDS stage through registers, keys past
-  // the end zero-filled (unwritten cache slots may hold NaN)
-  auto fill_tile = [&](bool tree, int kbase, int stage) {
-    _Float16 *Ks = lds + stage * Lds<D>::STAGE;
-    _Float16 *Vs = Ks + Lds<D>::K_HALVES;
-    for (int ci = tid; ci < TILE * CPR; ci += 256) {
-      const int tau = ci / CPR, cc = ci % CPR;
-      const int key = kbase + tau;
-      uint4 kx = make_uint4(0, 0, 0, 0);
-      half8 vx = half8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (tree) {
-        if (key < s.n) {
-          const size_t src = ((size_t)(s.o + key) * A.Hkv + kv_head) * D + 8 * cc;
-          kx = *reinterpret_cast<const uint4 *>(A.Kt + src);
-          vx = *reinterpret_cast<const half8 *>(A.Vt + src);
-        }
-      } else if (key < t_end) {
-        const size_t pg = (size_t)page_of(key) * A.Hkv + kv_head;
-        kx = *reinterpret_cast<const uint4 *>(A.Kc + (pg * DDT_PAGE + (key & 15)) * D + 8 * cc);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) vx[x] = A.Vc[(pg * D + 8 * cc + x) * DDT_PAGE + (key & 15)];
-      }
-      const int rr = krow_of(tau);
-      *reinterpret_cast<uint4 *>(Ks + rr * D + 8 * (cc ^ ksw(rr))) = kx;
-      const int qg = tau >> 3, e = tau & 7;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int d = 8 * cc + x;
-        Vs[d * 32 + 8 * (qg ^ vsw(d)) + e] = vx[x];
-      }
-    }
-  };
-
-  // K fragment of this wave's key half (k-step ks) and V fragment of its
-  // channel half (block n)
-  auto kfrag = [&](const _Float16 *Ks, int ks) -> half8 {
-    const int rr = 16 * c + l16;
-    const int cc = 4 * ks + lq;
-    return *reinterpret_cast<const half8 *>(Ks + rr * D + 8 * (cc ^ ksw(rr)));
-  };
-  auto vfrag = [&](const _Float16 *Vs, int n) -> half8 {
-    const int d = 16 * (DBH * c + n) + l16;
-    return *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ vsw(d)));
-  };
-  // scores of this wave's 16 keys of a tile for its row blocks; lane
-  // (l16, lq) gets keys 8*lq + 4*c + e (e < 4) of row l16 of each block
-  auto qk_half = [&](const _Float16 *Ks, f32x4 (&S)[NBH]) {
-#pragma unroll
-    for (int j = 0; j < NBH; ++j) S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const half8 kf = kfrag(Ks, ks);
-#pragma unroll
-      for (int j = 0; j < NBH; ++j)
-        S[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[j][ks], S[j], 0, 0, 0);
-    }
-  };
-  // row max over the lanes of a row (the four lane groups)
-  auto rowmax = [&](float t) {
-    t = fmaxf(t, __shfl_xor(t, 16));
-    return fmaxf(t, __shfl_xor(t, 32));
-  };
-  // this wave's four probabilities of row block j against the row's
-  // reference, as four halves; with `valid` a mask over the four keys
-  auto probs = [&](const f32x4 &S, int j, unsigned valid) -> u32x2 {
-    const float mc = mrow[j] == -INFINITY ? 0.f : mrow[j] * A.c;
-    float tmax = -INFINITY, ps = 0.f;
-    half4 h;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float sv = (valid >> e) & 1u ? S[e] : -INFINITY;
-      tmax = fmaxf(tmax, sv);
-      const float p = __builtin_amdgcn_exp2f(fmaf(sv, A.c, -mc));  // masked: exp2(-inf) = 0
-      ps += p;
-      h[e] = (_Float16)p;
-    }
-    mseen[j] = fmaxf(mseen[j], tmax);
-    ovf |= (tmax - mrow[j]) * A.c > 15.0f;  // fp16 P keeps 15 binades above 1
-    lsum[j] += ps;
-    return __builtin_bit_cast(u32x2, h);
-  };
-  // B operand of the value product per row block: keys 8*lq .. 8*lq + 7 of
-  // row l16; this wave's half in words 2c, 2c+1, the partner's in the others
-  u32x4 pfr[NBH];
-  auto set_own = [&](int j, u32x2 v) {
-    if constexpr (C == 0) {
-      pfr[j].x = v.x;
-      pfr[j].y = v.y;
-    } else {
-      pfr[j].z = v.x;
-      pfr[j].w = v.y;
-    }
-  };
-  auto set_oth = [&](int j, u32x2 v) {
-    if constexpr (C == 0) {
-      pfr[j].z = v.x;
-      pfr[j].w = v.y;
-    } else {
-      pfr[j].x = v.x;
-      pfr[j].y = v.y;
-    }
-  };
-
-  // One main-loop tile: value product of tile it (this wave's half of the
-  // probabilities already in pfr, the partner's read from the swap buffer)
-  // and, if MORE, scores and probabilities of tile it+1, whose half goes to
-  // the partner.  Fragments stream in NBAT batches, each read one batch
-  // ahead of the matrix instructions that use it (sched_barrier fences keep
-  // that order).
-  auto tile_step = [&](auto MORE, int it) {
-    constexpr bool more = decltype(MORE)::value;
-    const _Float16 *K1 = lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE;
-    const _Float16 *V0 = lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES;
-    const int par = it & 1;
-    half8 kf[2][KPB], vf[2][VPB];
-    f32x4 S[NBH];
-    auto load_batch = [&](int bi) {
-      if constexpr (more) {
-#pragma unroll
-        for (int x = 0; x < KPB; ++x) kf[bi & 1][x] = kfrag(K1, bi * KPB + x);
-      }
-#pragma unroll
-      for (int x = 0; x < VPB; ++x) vf[bi & 1][x] = vfrag(V0, bi * VPB + x);
-    };
-    auto mfma_batch = [&](int bi) {
-      if constexpr (more) {
-#pragma unroll
-        for (int x = 0; x < KPB; ++x)
-#pragma unroll
-          for (int j = 0; j < NBH; ++j)
-            S[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[bi & 1][x], qf[j][bi * KPB + x], S[j], 0, 0, 0);
-      }
-#pragma unroll
-      for (int x = 0; x < VPB; ++x)
-#pragma unroll
-        for (int j = 0; j < NBH; ++j)
-          o[j][bi * VPB + x] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              vf[bi & 1][x], __builtin_bit_cast(half8, pfr[j]), o[j][bi * VPB + x], 0, 0, 0);
-    };
-#pragma unroll
-    for (int j = 0; j < NBH; ++j) set_oth(j, pbuf[pi(par, wp, j)]);
-    load_batch(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (it + NSTAGE - 1 < n_full) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
-    __builtin_amdgcn_sched_barrier(0);
-    load_batch(1);
-    if constexpr (more) {
-#pragma unroll
-      for (int j = 0; j < NBH; ++j) S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int bi = 0; bi < NBAT; ++bi) {
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_batch(bi);
-      __builtin_amdgcn_sched_barrier(0);
-      if (bi + 2 < NBAT) load_batch(bi + 2);
-    }
-    if constexpr (more) {
-#pragma unroll
-      for (int j = 0; j < NBH; ++j) {
-        const u32x2 v = probs(S[j], j, 0xfu);
-        set_own(j, v);
-        pbuf[pi(par ^ 1, w, j)] = v;
-      }
-    }
-  };
-
-  // The split normally runs once.  If some score exceeded its row's
-  // reference by more than fp16 P can hold, it runs again with every
-  // reference set to the true maximum seen (both key halves).
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int j = 0; j < NBH; ++j) {
-      mseen[j] = -INFINITY;
-      lsum[j] = 0.f;
-#pragma unroll
-      for (int n = 0; n < DBH; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (n_full > 0) {
-#pragma unroll
-      for (int t = 0; t < NSTAGE - 1; ++t)
-        if (t < n_full) issue_tile(t, t);
-      wait_tiles(min(n_full, NSTAGE - 1) - 1);
-      __syncthreads();
-      f32x4 S[NBH];
-      qk_half(lds, S);
-      if (pass == 0) {
-        // the first full tile fixes every row's reference max
-        float t[NBH];
-#pragma unroll
-        for (int j = 0; j < NBH; ++j) {
-          t[j] = rowmax(fmaxf(fmaxf(S[j][0], S[j][1]), fmaxf(S[j][2], S[j][3])));
-          xch[xi(w, j)] = t[j];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < NBH; ++j) mrow[j] = fmaxf(t[j], xch[xi(wp, j)]);
-      }
-#pragma unroll
-      for (int j = 0; j < NBH; ++j) {
-        const u32x2 v = probs(S[j], j, 0xfu);
-        set_own(j, v);
-        pbuf[pi(0, w, j)] = v;
-      }
-      for (int it = 0; it + 1 < n_full; ++it) {
-        // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
-        wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
-        __syncthreads();  // tile it+1 landed, P(it) halves written; tile it-1 done
-        tile_step(std::true_type{}, it);
-      }
-      __syncthreads();  // P(n_full-1) halves written
-      tile_step(std::false_type{}, n_full - 1);
-    }
-    // ---- epilogue: ragged cache tile, then the tree tiles
-    const int n_ep = (has_part ? 1 : 0) + n_tree;
-    for (int e = 0; e < n_ep; ++e) {
-      const bool tree = !(has_part && e == 0);
-      const int kbase = tree ? (e - (has_part ? 1 : 0)) * TILE : t_beg + n_full * TILE;
-      __syncthreads();  // the stage, the swap buffers and xch are no longer read
-      fill_tile(tree, kbase, 0);
-      __syncthreads();
-      f32x4 S[NBH];
-      qk_half(lds, S);
-      unsigned valid[NBH];
-      float t[NBH];
-#pragma unroll
-      for (int j = 0; j < NBH; ++j) {
-        const unsigned long long am = tree ? anc_row(j) : 0ull;
-        valid[j] = 0u;
-        float m = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int key = kbase + 8 * lq + 4 * c + x;
-          const bool ok = tree ? (key < s.n && ((am >> key) & 1ull)) : (key < t_end);
-          if (ok) {
-            valid[j] |= 1u << x;
-            m = fmaxf(m, S[j][x]);
-          }
-        }
-        t[j] = rowmax(m);
-        xch[xi(w, j)] = t[j];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < NBH; ++j) {
-        // a row's first tile with valid keys fixes its reference max
-        if (mrow[j] == -INFINITY) mrow[j] = fmaxf(t[j], xch[xi(wp, j)]);
-        const u32x2 v = probs(S[j], j, valid[j]);
-        set_own(j, v);
-        pbuf[pi(0, w, j)] = v;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < NBH; ++j) set_oth(j, pbuf[pi(0, wp, j)]);
-      const _Float16 *Vs = lds + Lds<D>::K_HALVES;
-#pragma unroll
-      for (int n = 0; n < DBH; ++n) {
-        const half8 vf = vfrag(Vs, n);
-#pragma unroll
-        for (int j = 0; j < NBH; ++j)
-          o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, __builtin_bit_cast(half8, pfr[j]), o[j][n], 0, 0, 0);
-      }
-    }
-    // any overflow in the workgroup?  (a block-wide vote would take static
-    // LDS; the flags go through xch)
-    __syncthreads();
-    int *flag = reinterpret_cast<int *>(xch);
-    const bool wave_ovf = __ballot(ovf) != 0ull;  // every lane votes, outside the branch
-    if (lane == 0) flag[w] = wave_ovf;
-    __syncthreads();
-    const bool redo = (flag[0] | flag[1] | flag[2] | flag[3]) != 0;
-    __syncthreads();
-    if (!redo) break;
-    ovf = false;
-    float t[NBH];
-#pragma unroll
-    for (int j = 0; j < NBH; ++j) {
-      t[j] = rowmax(mseen[j]);
-      xch[xi(w, j)] = t[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NBH; ++j) mrow[j] = fmaxf(t[j], xch[xi(wp, j)]);
-    __syncthreads();  // xch read before the next pass writes it
-  }
-
-  // ---- partial results of this split: row sums of both key halves (added
-  // in key-half order, so both waves of a pair get the same value)
-  float lrow[NBH];
-#pragma unroll
-  for (int j = 0; j < NBH; ++j) {
-    float l = lsum[j];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    lrow[j] = l;
-    xch[xi(w, j)] = l;
-  }
-  __syncthreads();
-  const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits + split) * A.rows_wg;
-#pragma unroll
-  for (int j = 0; j < NBH; ++j) {
-    if (!blk_on[j]) continue;
-    const int rl = 16 * (NBH * r + j) + l16;  // row within the workgroup
-    if (row0 + rl >= rows_b) continue;
-    if (c == 0 && lq == 0) A.ML[base + rl] = make_float2(mrow[j], lrow[j] + xch[xi(wp, j)]);
-    float *op = A.Opart + (base + rl) * D + 16 * DBH * c + 4 * lq;
-#pragma unroll
-    for (int n = 0; n < DBH; ++n)
-      *reinterpret_cast<float4 *>(op + 16 * n) = make_float4(o[j][n][0], o[j][n][1], o[j][n][2], o[j][n][3]);
-  }
-}
-
-template <int D, int NBH>
-__global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs A) {
-  // the key / channel half is a compile-time property of each wave's code
-  if ((threadIdx.x >> 6) & 1)
-    attn_pair_wave<D, NBH, 1>(A);
-  else
-    attn_pair_wave<D, NBH, 0>(A);
 }
 
 // Merge the splits of one query row: one workgroup per row.  Every thread
@@ -1157,12 +709,8 @@ int check_plan(const ddt_plan *P);
 
 struct Cfg {
   bool mfma;
-  int nb;   // row blocks per wave (four-wave kernel), or 0
-  int nbh;  // row blocks per row half (paired-wave kernel), or 0
-  int rows_wg, n_rg, n_splits, chunk;
+  int nb, rows_wg, n_rg, n_splits, chunk;
 };
-// row blocks per row half that the paired-wave kernel's registers hold
-constexpr int PAIR_NBH_MAX = 5;
 
 static Cfg attn_cfg(const ddt_plan *P, int Hq, int Hkv, int D, int T_max, int n_splits, int dtype) {
   Cfg c{};
@@ -1171,14 +719,9 @@ static Cfg attn_cfg(const ddt_plan *P, int Hq, int Hkv, int D, int T_max, int n_
   if (!c.mfma) return c;
   const int rows = G * P->n_max;
   const int blocks = (rows + 15) / 16;
-  if (blocks <= 2 * PAIR_NBH_MAX) {
-    c.nbh = (blocks + 1) / 2;
-    c.rows_wg = 32 * c.nbh;
-  } else {
-    c.nb = (blocks + 3) / 4;
-    if (c.nb > 3) c.nb = 3;
-    c.rows_wg = 64 * c.nb;
-  }
+  c.nb = (blocks + 3) / 4;
+  if (c.nb > 3) c.nb = 3;
+  c.rows_wg = 64 * c.nb;
   c.n_rg = (rows + c.rows_wg - 1) / c.rows_wg;
   int tmax = T_max > 0 ? T_max : 1;
   if (n_splits <= 0) {
@@ -1270,9 +813,7 @@ extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, c
   A.ML = (float2 *)((char *)ws + rows * D * sizeof(float));
   A.out = out;
   dim3 grid(c.n_splits, Hkv, P->B * c.n_rg);
-  const size_t ring = (size_t)NSTAGE * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
-  // the paired kernel adds its probability swap buffers and row scalars
-  const size_t lds = c.nbh ? ring + (size_t)2 * 4 * c.nbh * 64 * 8 + (size_t)4 * c.nbh * 64 * 4 : ring;
+  const size_t lds = (size_t)NSTAGE * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
 #define DDT_ATTN(DD, NBB)                                                                       \
   do {                                                                                          \
     hipError_t e_ = hipFuncSetAttribute((const void *)attn_mfma_kernel<DD, NBB>,                \
@@ -1283,41 +824,11 @@ extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, c
     }                                                                                           \
     hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB>), grid, dim3(256), lds, st, A);               \
   } while (0)
-#define DDT_PAIR(DD, NBB)                                                                       \
-  do {                                                                                          \
-    hipError_t e_ = hipFuncSetAttribute((const void *)attn_pair_kernel<DD, NBB>,                \
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
-    if (e_ != hipSuccess) {                                                                     \
-      set_hip_error(e_);                                                                        \
-      return DDT_E_HIP;                                                                         \
-    }                                                                                           \
-    hipLaunchKernelGGL((attn_pair_kernel<DD, NBB>), grid, dim3(256), lds, st, A);               \
-  } while (0)
-  if (c.nbh) {
-    static_assert(PAIR_NBH_MAX == 5, "one instance per row-half size");
-    if (D == 256) {
-      switch (c.nbh) {
-        case 1: DDT_PAIR(256, 1); break;
-        case 2: DDT_PAIR(256, 2); break;
-        case 3: DDT_PAIR(256, 3); break;
-        case 4: DDT_PAIR(256, 4); break;
-        default: DDT_PAIR(256, 5); break;
-      }
-    } else {
-      switch (c.nbh) {
-        case 1: DDT_PAIR(128, 1); break;
-        case 2: DDT_PAIR(128, 2); break;
-        case 3: DDT_PAIR(128, 3); break;
-        case 4: DDT_PAIR(128, 4); break;
-        default: DDT_PAIR(128, 5); break;
-      }
-    }
-  } else if (D == 256) {
+  if (D == 256) {
     if (c.nb == 1) DDT_ATTN(256, 1); else if (c.nb == 2) DDT_ATTN(256, 2); else DDT_ATTN(256, 3);
   } else {
     if (c.nb == 1) DDT_ATTN(128, 1); else if (c.nb == 2) DDT_ATTN(128, 2); else DDT_ATTN(128, 3);
   }
-#undef DDT_PAIR
 #undef DDT_ATTN
   r = launch_status();
   if (r) return r;
