@@ -42,6 +42,8 @@
 //  - Each split writes unnormalised partial O^T, its reference max and the
 //    row sum; a combine kernel merges the splits in fixed order
 //    (deterministic, no atomics).
+#include <type_traits>
+
 #include "common.h"
 
 namespace ddt {
@@ -369,64 +371,71 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     return *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ vsw(d)));
   };
   // One full tile of the main loop: scores of the next tile (Ks1) while the
-  // probabilities and value product of this tile (S, Vs0) are formed.
-  // sched_barrier fences keep each batch of LDS reads one batch ahead of
-  // the MFMAs that consume it and put the softmax next to the score MFMAs.
-  auto tile_step = [&](const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
+  // probabilities and value product of this tile (S, Vs0) are formed, for
+  // the first NBA row blocks of this wave (the others are padding past the
+  // sequence's rows and are skipped).  sched_barrier fences keep each batch
+  // of LDS reads one batch ahead of the MFMAs that consume it and put the
+  // softmax next to the score MFMAs.
+  auto tile_step = [&](auto NBA_c, const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
                        f32x4 (&Sn)[2][NB], auto &&in_shadow) {
+    constexpr int NBA = decltype(NBA_c)::value;
     constexpr int KH = KS / 2;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) Sn[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NBA; ++j) Sn[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     half8 ka[2][KH], kb[2][KH], pf[NB];
+    if constexpr (NBA > 0) {
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
+      for (int ks = 0; ks < KH; ++ks)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) ka[tt][ks] = kfrag(Ks1, tt, ks);
+        for (int tt = 0; tt < 2; ++tt) ka[tt][ks] = kfrag(Ks1, tt, ks);
+    }
     __builtin_amdgcn_sched_barrier(0);
     in_shadow();  // work that needs no fragment, done while they arrive
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NBA > 0) {
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
+      for (int ks = 0; ks < KH; ++ks)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) kb[tt][ks] = kfrag(Ks1, tt, KH + ks);
+        for (int tt = 0; tt < 2; ++tt) kb[tt][ks] = kfrag(Ks1, tt, KH + ks);
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
+      for (int ks = 0; ks < KH; ++ks)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tt][ks], qf[j][ks], Sn[tt][j], 0, 0, 0);
-    softmax_blk(S, 0, pf[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    constexpr int VH = DB / 2;
-    half8 va[VH], vb[VH];
+          for (int j = 0; j < NBA; ++j)
+            Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tt][ks], qf[j][ks], Sn[tt][j], 0, 0, 0);
+      softmax_blk(S, 0, pf[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int VH = DB / 2;
+      half8 va[VH], vb[VH];
 #pragma unroll
-    for (int n = 0; n < VH; ++n) va[n] = vfrag(Vs0, n);
+      for (int n = 0; n < VH; ++n) va[n] = vfrag(Vs0, n);
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
+      for (int ks = 0; ks < KH; ++ks)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[tt][ks], qf[j][KH + ks], Sn[tt][j], 0, 0, 0);
+          for (int j = 0; j < NBA; ++j)
+            Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[tt][ks], qf[j][KH + ks], Sn[tt][j], 0, 0, 0);
 #pragma unroll
-    for (int j = 1; j < NB; ++j) softmax_blk(S, j, pf[j]);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 1; j < NBA; ++j) softmax_blk(S, j, pf[j]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < VH; ++n) vb[n] = vfrag(Vs0, VH + n);
+      for (int n = 0; n < VH; ++n) vb[n] = vfrag(Vs0, VH + n);
 #pragma unroll
-    for (int n = 0; n < VH; ++n)
+      for (int n = 0; n < VH; ++n)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[n], pf[j], o[j][n], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < NBA; ++j)
+          o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[n], pf[j], o[j][n], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < VH; ++n)
+      for (int n = 0; n < VH; ++n)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        o[j][VH + n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb[n], pf[j], o[j][VH + n], 0, 0, 0);
+        for (int j = 0; j < NBA; ++j)
+          o[j][VH + n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb[n], pf[j], o[j][VH + n], 0, 0, 0);
+    }
   };
 
   // ---- O^T += V^T P^T for one tile
@@ -476,25 +485,33 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
           mrow[j] = fmaxf(t, __shfl_xor(t, 32));
         }
       }
-      for (int it = 0; it < n_full; ++it) {
-        const int nt = it + NSTAGE - 1;  // tile issued in this iteration
-        const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
-        // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
-        if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
-        __syncthreads();  // tile it+1 landed; every wave is past tile it-1
-        // scores of tile it+1 (past the last tile they read a stale stage
-        // and are dropped), probabilities and value product of tile it; the
-        // loads of tile it+3 go out while the first K fragments arrive
-        f32x4 Sc[2][NB];
+      auto main_loop = [&](auto NBA_c) {
+        for (int it = 0; it < n_full; ++it) {
+          const int nt = it + NSTAGE - 1;  // tile issued in this iteration
+          const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
+          // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
+          if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
+          __syncthreads();  // tile it+1 landed; every wave is past tile it-1
+          // scores of tile it+1 (past the last tile they read a stale stage
+          // and are dropped), probabilities and value product of tile it; the
+          // loads of tile it+3 go out while the first K fragments arrive
+          f32x4 Sc[2][NB];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
-        tile_step(lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
-                  lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
-                    if (nt < n_full) issue_tile(nt, nt % NSTAGE, npg0, npg1);
-                  });
-      }
+            for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
+          tile_step(NBA_c, lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
+                    lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
+                      if (nt < n_full) issue_tile(nt, nt % NSTAGE, npg0, npg1);
+                    });
+        }
+      };
+      // row blocks are dealt round-robin, so a wave's active blocks are a
+      // prefix of its NB and number NB or NB - 1
+      if (blk_on[NB - 1])
+        main_loop(std::integral_constant<int, NB>{});
+      else
+        main_loop(std::integral_constant<int, NB - 1>{});
     }
     // ---- epilogue: ragged cache tile, then the tree tiles
     const int n_ep = (has_part ? 1 : 0) + n_tree;
