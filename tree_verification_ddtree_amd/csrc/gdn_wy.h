@@ -334,68 +334,76 @@ __device__ __forceinline__ int gdn_nlev(int n, unsigned long long a) {
 
 // ------------------------------------------------------------ register path solve
 // One lane per (node i, rows r0..r0+3): u of every node on i's root path,
-// root first, then i's outputs.  Requires every node's depth < GDN_PATH.
-template <bool WANT_O>
+// root first, then i's outputs.  Requires every node's depth < PMAX; the
+// loops are unrolled to PMAX levels (and predicated per lane), so the
+// caller picks the smallest PMAX that holds the tree.  The operations for
+// a node do not depend on PMAX.
+template <bool WANT_O, int PMAX>
 __device__ void gdn_path_solve(GdnView &V, int n, float scale) {
+  static_assert(PMAX <= GDN_PATH, "register path bound");
   const int i = threadIdx.x & 63, r0 = (threadIdx.x >> 6) * 4;
   if (i >= n || r0 >= GDN_R) return;
   const unsigned long long anc = V.anc[i] & ((2ull << i) - 1);
-  const int d = min(__popcll(anc) - 1, GDN_PATH - 1);
-  int p[GDN_PATH];
+  const int d = min(__popcll(anc) - 1, PMAX - 1);
+  // path root first; slots past the node hold the node itself, so every
+  // slot is a valid index and the loops below need no per-lane branches
+  // (their results past depth d are computed and never used)
+  int p[PMAX];
   {
     unsigned long long bits = anc;
 #pragma unroll
-    for (int k = 0; k < GDN_PATH; ++k) {
+    for (int k = 0; k < PMAX; ++k) {
       p[k] = bits ? __ffsll((long long)bits) - 1 : i;
       bits &= bits - 1;
     }
   }
-  float al[GDN_PATH], be[GDN_PATH];
-  gf32x4 Dk[GDN_PATH], vk[GDN_PATH];
+  float al[PMAX], be[PMAX], g[PMAX][PMAX];
+  gf32x4 Dk[PMAX], vk[PMAX];
 #pragma unroll
-  for (int k = 0; k < GDN_PATH; ++k)
-    if (k <= d) {
-      al[k] = V.al[p[k]];
-      be[k] = V.be[p[k]];
-      Dk[k] = *reinterpret_cast<const gf32x4 *>(V.D + p[k] * GDN_R + r0);
-      vk[k] = *reinterpret_cast<const gf32x4 *>(V.v + p[k] * GDN_R + r0);
+  for (int k = 0; k < PMAX; ++k) {
+    al[k] = V.al[p[k]];
+    be[k] = V.be[p[k]];
+    Dk[k] = *reinterpret_cast<const gf32x4 *>(V.D + p[k] * GDN_R + r0);
+    vk[k] = *reinterpret_cast<const gf32x4 *>(V.v + p[k] * GDN_R + r0);
+#pragma unroll
+    for (int j = 0; j < k; ++j) g[j][k] = V.Gm[p[j] * V.gs + 2 * p[k]];  // k_j . k_k
+  }
+  gf32x4 u[PMAX], ul = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < PMAX; ++k) {
+    const float ba = be[k] * al[k];
+    float w = 1.f;
+    gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = k - 1; j >= 0; --j) {  // ancestors nearest first
+      const float m = -(ba * (w * g[j][k]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(m, u[j][e], acc[e]);
+      w *= al[j];
     }
-  gf32x4 u[GDN_PATH], ul = {0.f, 0.f, 0.f, 0.f};
+    const float c1 = -(al[k] * w);
 #pragma unroll
-  for (int k = 0; k < GDN_PATH; ++k) {
-    if (k <= d) {
-      const float ba = be[k] * al[k];
-      float w = 1.f;
-      gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = k - 1; j >= 0; --j) {  // ancestors nearest first
-        const float m = -(ba * (w * V.Gm[p[j] * V.gs + 2 * p[k]]));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(m, u[j][e], acc[e]);
-        w *= al[j];
-      }
-      const float c1 = -(al[k] * w);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[k][e] = fmaf(be[k], fmaf(c1, Dk[k][e], vk[k][e]), acc[e]);
-      if (k == d) ul = u[k];
-    }
+    for (int e = 0; e < 4; ++e) u[k][e] = fmaf(be[k], fmaf(c1, Dk[k][e], vk[k][e]), acc[e]);
+    if (k == d) ul = u[k];
   }
   *reinterpret_cast<gf32x4 *>(V.U + i * GDN_R + r0) = ul;
   if (WANT_O) {
+    float hq[PMAX];
+#pragma unroll
+    for (int j = 0; j < PMAX; ++j) hq[j] = V.Gm[p[j] * V.gs + 2 * i + 1];  // k_j . q_i
+    const gf32x4 Fi = *reinterpret_cast<const gf32x4 *>(V.F + i * GDN_R + r0);
+    const float kqd = V.Gm[i * V.gs + 2 * i + 1];
     float w = 1.f, ai = 0.f;
     gf32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = GDN_PATH - 1; j >= 0; --j) {
+    for (int j = PMAX - 1; j >= 0; --j) {
       if (j == d) ai = al[j];
-      if (j < d) {
-        const float hh = w * V.Gm[p[j] * V.gs + 2 * i + 1];
+      const bool on = j < d;  // ancestors of i, nearest first
+      const float hh = w * hq[j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = fmaf(hh, u[j][e], y[e]);
-        w *= al[j];
-      }
+      for (int e = 0; e < 4; ++e) y[e] = on ? fmaf(hh, u[j][e], y[e]) : y[e];
+      w = on ? w * al[j] : w;
     }
-    const gf32x4 Fi = *reinterpret_cast<const gf32x4 *>(V.F + i * GDN_R + r0);
-    const float kqd = V.Gm[i * V.gs + 2 * i + 1];
     gf32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = scale * fmaf(ai, fmaf(w, Fi[e], y[e]), ul[e] * kqd);
@@ -573,8 +581,12 @@ __device__ void gdn_level_solve(GdnView &V, int n, float scale) {
 // (levels of the tree) must be the same in every thread.
 template <bool WANT_O>
 __device__ void gdn_scalar(GdnView &V, int n, int nlev, float scale) {
-  if (nlev <= GDN_PATH) {
-    gdn_path_solve<WANT_O>(V, n, scale);
+  if (nlev <= 4) {
+    gdn_path_solve<WANT_O, 4>(V, n, scale);
+  } else if (nlev <= 8) {
+    gdn_path_solve<WANT_O, 8>(V, n, scale);
+  } else if (nlev <= GDN_PATH) {
+    gdn_path_solve<WANT_O, GDN_PATH>(V, n, scale);
   } else {
     if (threadIdx.x < 64) gdn_levels(V, n, threadIdx.x < n ? V.anc[threadIdx.x] : 0ull);
     __syncthreads();
