@@ -21,6 +21,10 @@ What the step computes (sources)
 * Attention is full attention over the KV cache, optionally paged
   (codehub lucebox-hub@main, "Server flags", --fa-window default 0;
   Luce-Org/lucebox README, "Inference Engine Optimizations").
+* Ahead of the step (a widening of it): the draft model's top-K tokens and
+  log-sum-exp per draft position are read from the device logits (codehub
+  lucebox-hub@main, "GPU draft top-K & verify-argmax (DFlash)"), and
+  DDTree builds the budget-N tree from them (draft.py states the reading).
 
 The pages give names and roles, not formulas.  The recurrence is the
 standard gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta Networks",
@@ -32,7 +36,8 @@ sequence.  Readings of the pages' gaps are listed in each module.
 
 Parity status: every function is pinned by tests/test_oracle_*.py against
 closed forms, library routines (torch CPU conv1d / softmax attention,
-numpy argmax) or brute force on tiny inputs.
+numpy argmax and stable sort, scipy logsumexp), hand-worked golden cases or
+brute force on tiny inputs.
 """
 from .tree import validate_tree, depth, root_path, ancestor_mask, conv_window, TreeError  # noqa: F401
 from .conv import tree_conv  # noqa: F401
@@ -40,3 +45,4 @@ from .gdn import gdn_chain, tree_gdn, tree_gdn_recurrent  # noqa: F401
 from .attn import tree_attn, gather_cache  # noqa: F401
 from .walk import argmax_rows, accept_walk  # noqa: F401
 from .commit import commit_gdn_state, commit_conv_prefix, commit_kv  # noqa: F401
+from .draft import draft_topk, log_probs, build_tree, build_tree_brute  # noqa: F401

@@ -33,6 +33,7 @@ _T_Q, _T_K, _T_V, _T_A, _T_B, _T_S = 1, 2, 3, 4, 5, 6
 _T_X, _T_PRE, _T_W = 7, 8, 9
 _T_AQ, _T_KC, _T_VC, _T_KT, _T_VT, _T_PT = 10, 11, 12, 13, 14, 15
 _T_LOG, _T_TOK, _T_TREE, _T_T = 16, 17, 18, 19
+_T_DL, _T_DP = 20, 21
 
 
 def rng_for(seed: int, *key: int) -> np.random.Generator:
@@ -210,6 +211,23 @@ def logits_and_draft(seed, key, parent, V, dtype="bf16", p_match=0.8, plant=True
             used.add(t)
             tok[c] = t
     return store(lg, dtype), tok
+
+
+def draft_logits(seed, key, L, V, dtype="bf16"):
+    """Draft logits [L][V] for one block of L draft positions: N(0,1) with,
+    per position, 1 to 4 planted contenders raised by 4 to 9 (a confident
+    drafter has a few likely tokens per position; how many and how far ahead
+    is drawn at random), at distinct seeded tokens."""
+    lg = rng_for(seed, *key, _T_DL).standard_normal((L, V), dtype=np.float32)
+    r = rng_for(seed, *key, _T_DP)
+    for i in range(L):
+        m = int(r.integers(1, 5))
+        toks = r.choice(V, size=m, replace=False)
+        lg[i, toks] += r.uniform(4.0, 9.0, size=m).astype(np.float32)
+    return store(lg, dtype)
+
+
+DRAFT = dict(name="draft_tree_b8_l16_k8_n22", B=8, L=16, K=8, N=22)
 
 
 # ----------------------------------------------------------------------------
