@@ -287,6 +287,56 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
                      int32_t kv_dtype, const int32_t *page_table, int32_t max_pages, int32_t *T,
                      void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Ahead of the verify step: draft top-K / log-sum-exp and tree construction.
+ *
+ * ddt_draft_topk: the draft model's K most likely tokens (1 <= K <= 8) and
+ * the log-sum-exp of every draft position, read from the draft logits on
+ * the device (codehub lucebox-hub@main, "GPU draft top-K & verify-argmax
+ * (DFlash)").
+ *   logits      device, [B][L][V], DDT_BF16 or DDT_F32 (16-byte aligned rows
+ *               use vector reads; any other layout is read element-wise).
+ *   topk_idx    device out [B][L][K] int32: indices by descending logit,
+ *               ties to the lower index; -1 past the row's finite logits.
+ *   topk_logit  device out [B][L][K] float: their logits (-inf where -1).
+ *   lse         device out [B][L] float: log-sum-exp of the finite logits
+ *               (-inf if there are none).  NaN logits count as -inf.
+ *   workspace   device, at least ddt_draft_topk_workspace(B, L, V, K)
+ *               bytes, owned by the caller (0 for invalid sizes).
+ * Errors: DDT_E_ARG (null pointer), DDT_E_SHAPE (B, L outside [1, 65535],
+ * V < 1, K outside [1, 8]), DDT_E_DTYPE, DDT_E_WS; nothing is launched then.
+ *
+ * ddt_tree_build: DDTree's budget-N tree from those candidates (lucebox-hub
+ * README, "02 · DFlash DDtree", "Algorithms used"; the pages give no
+ * selection rule).  Reading: a node at depth d has as candidate children
+ * the top-K tokens of draft position d (0-based; the root, the last
+ * committed token, has depth 0); log p = logit - lse; a node's score is the
+ * sum of log p along its root path; the tree is the root plus the N-1 best
+ * nodes under (score descending, then the candidate ranks along the path
+ * lexicographically, a prefix before its extensions), numbered in that
+ * order, so every parent precedes its children.  Scores are summed in fp32
+ * root first.
+ *   topk_idx, topk_logit, lse   device, as written by ddt_draft_topk.
+ *   L           draft positions, 1..16;  K as above;  N budget 1..64.
+ *   root_token  device [B] int32: the root's token (the last committed one).
+ *   parent, tok device out [B][N] int32: tree b is rows b*N .. b*N+n-1, node
+ *               ids local to the tree, parent[root] = -1; with every
+ *               n_nodes[b] == N the arrays feed ddt_tree_plan directly with
+ *               tree_off[b] = b*N.
+ *   score       device out [B][N] float: node scores (0 for the root).
+ *   n_nodes     device out [B] int32: nodes built (< N only when fewer
+ *               candidates exist, e.g. K = 1 or positions without finite
+ *               logits).
+ * Errors: DDT_E_ARG, DDT_E_SHAPE; nothing is launched then.
+ */
+size_t ddt_draft_topk_workspace(int32_t B, int32_t L, int32_t V, int32_t K);
+int ddt_draft_topk(const void *logits, int32_t B, int32_t L, int32_t V, int32_t dtype, int32_t K,
+                   int32_t *topk_idx, float *topk_logit, float *lse, void *workspace, size_t ws_bytes,
+                   void *stream);
+int ddt_tree_build(const int32_t *topk_idx, const float *topk_logit, const float *lse, int32_t B, int32_t L,
+                   int32_t K, int32_t N, const int32_t *root_token, int32_t *parent, int32_t *tok, float *score,
+                   int32_t *n_nodes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

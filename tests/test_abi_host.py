@@ -144,5 +144,15 @@ def test_device_entry_points_validate_before_launch():
                               256, 1, None, 0, None, None) == -1
     assert L.ddt_commit_state(bp, one, one, 0, one, 1, 16, 30, 128, 128, 2, 8192, 2, None, 0, 4,
                               256, 1, None, 0, None, None) == -3
+    # draft top-K: K outside 1..8, dtype, workspace; tree build: L > 16, N > 64, null output
+    ws = ddt.ddt_draft_topk_workspace(1, 16, 151936, 8)
+    assert ws > 0 and ddt.ddt_draft_topk_workspace(1, 16, 151936, 9) == 0
+    assert L.ddt_draft_topk(one, 1, 16, 151936, 2, 9, one, one, one, one, 1 << 30, None) == -3
+    assert L.ddt_draft_topk(one, 1, 16, 151936, 1, 8, one, one, one, one, 1 << 30, None) == -4
+    assert L.ddt_draft_topk(one, 1, 16, 151936, 2, 8, one, one, one, one, ws - 1, None) == -6
+    assert L.ddt_draft_topk(None, 1, 16, 151936, 2, 8, one, one, one, one, ws, None) == -1
+    assert L.ddt_tree_build(one, one, one, 1, 17, 8, 22, one, one, one, one, one, None) == -3
+    assert L.ddt_tree_build(one, one, one, 1, 16, 8, 65, one, one, one, one, one, None) == -3
+    assert L.ddt_tree_build(one, one, one, 1, 16, 8, 22, one, one, one, one, None, None) == -1
     for c in (-1, -2, -3, -4, -5, -6, -7, 0):
         assert ddt.status_str(c)

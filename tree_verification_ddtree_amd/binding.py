@@ -60,6 +60,9 @@ _SIGS = {
                          _vp], _i32),
     "ddt_commit_state": ([ctypes.POINTER(Plan), _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp], _i32),
+    "ddt_draft_topk_workspace": ([_i32, _i32, _i32, _i32], _sz),
+    "ddt_draft_topk": ([_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "ddt_tree_build": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
 }
 
 _LIB = None
@@ -234,3 +237,23 @@ def ddt_commit_state(plan, path, L, mode, gdn_table, n_gdn, Hk, Hv, dk, dv, gdn_
                                   int(C), int(conv_dtype), _ptr(attn_table), int(n_attn),
                                   int(Hkv), int(D), int(kv_dtype), _ptr(page_table), max_pages,
                                   _ptr(T), _stream(stream)), "ddt_commit_state")
+
+
+def ddt_draft_topk_workspace(B, L, V, K):
+    return int(lib().ddt_draft_topk_workspace(int(B), int(L), int(V), int(K)))
+
+
+def ddt_draft_topk(logits, K, topk_idx, topk_logit, lse, ws, stream=None):
+    """logits [B][L][V] (bf16 or fp32 device tensor)."""
+    B, L, V = (int(x) for x in logits.shape)
+    wsb = ws.numel() * ws.element_size()
+    _check(lib().ddt_draft_topk(_ptr(logits), B, L, V, dtype_code(logits), int(K), _ptr(topk_idx),
+                                _ptr(topk_logit), _ptr(lse), _ptr(ws), wsb, _stream(stream)), "ddt_draft_topk")
+
+
+def ddt_tree_build(topk_idx, topk_logit, lse, N, root_token, parent, tok, score, n_nodes, stream=None):
+    """topk_* [B][L][K], lse [B][L]; outputs [B][N] and n_nodes [B]."""
+    B, L, K = (int(x) for x in topk_idx.shape)
+    _check(lib().ddt_tree_build(_ptr(topk_idx), _ptr(topk_logit), _ptr(lse), B, L, K, int(N),
+                                _ptr(root_token), _ptr(parent), _ptr(tok), _ptr(score), _ptr(n_nodes),
+                                _stream(stream)), "ddt_tree_build")
