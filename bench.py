@@ -202,6 +202,58 @@ class Stack:
         return sum(per[k] * v for k, v in b.items())
 
 
+def draft_bench(device, B, reps=5, calls=20, settle=0.3):
+    """Ahead of the verify step: draft top-K / log-sum-exp and the DDTree
+    build on L=16 draft positions of the full vocabulary (bf16 logits), K=8,
+    budget 22.  Timed as graph-replayed back-to-back batches (each call is a
+    few microseconds), the two entry points on their own and together, each
+    after `settle` seconds of untimed replays (the clock ramps under load)."""
+    import torch
+    import tree_verification_ddtree_amd as ddt
+    c = synth.DRAFT
+    L, K, N, V = c["L"], c["K"], c["N"], synth.VOCAB
+    lg = _dev(np.stack([synth.draft_logits(0, (40, b), L, V, "bf16") for b in range(B)]), device)
+    i32 = dict(dtype=torch.int32, device=device)
+    idx, lse = torch.empty(B, L, K, **i32), torch.empty(B, L, dtype=torch.float32, device=device)
+    val = torch.empty(B, L, K, dtype=torch.float32, device=device)
+    ws = torch.empty(ddt.ddt_draft_topk_workspace(B, L, V, K), dtype=torch.uint8, device=device)
+    roots = torch.arange(B, **i32)
+    parent, tok, n = torch.empty(B, N, **i32), torch.empty(B, N, **i32), torch.empty(B, **i32)
+    score = torch.empty(B, N, dtype=torch.float32, device=device)
+    topk = lambda: ddt.ddt_draft_topk(lg, K, idx, val, lse, ws)  # noqa: E731
+    tree = lambda: ddt.ddt_tree_build(idx, val, lse, N, roots, parent, tok, score, n)  # noqa: E731
+    res = {}
+    for name, fns in (("topk", [topk]), ("tree", [tree]), ("both", [topk, tree])):
+        for f in fns:
+            f()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                for f in fns:
+                    f()
+        g.replay()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                g.replay()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / (reps * calls)
+        del g
+    nbytes = B * L * V * 2 + B * L * (K * 8 + 4)
+    gbps = nbytes / (res["topk"] * 1e-6) / 1e9
+    return {"workload": f"draft_tree_b{B}_l{L}_k{K}_n{N}", "B": B, "L": L, "V": V, "K": K, "N": N,
+            "us_topk": res["topk"], "us_tree": res["tree"], "us_per_call": res["both"],
+            "topk_bytes": nbytes, "topk_GBps": gbps, "topk_frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+            "timed": "graph-replayed back-to-back batch", "bound": "hbm (top-K); latency (tree)"}
+
+
 def _traffic(kernel_src_sha):
     """HBM traffic of the attention call from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source; else None."""
@@ -284,6 +336,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the measurements of the widenings beside the step (draft tree build)")
     ap.add_argument("--kernel-reps", type=int, default=5, help="eager steps timed per attention call")
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed sustained steps before timing (the GPU clock ramps "
@@ -465,6 +519,10 @@ def main():
         "kernels": kernels,
         "cpu_baseline": None,
     }
+    if not args.no_next:
+        # widening ahead of the step (reported beside it, not part of `value`)
+        print("[bench] draft top-K + tree build", file=sys.stderr, flush=True)
+        out["next"] = {"draft_tree": [draft_bench(dev, 1), draft_bench(dev, 8)]}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(st, args.seed)

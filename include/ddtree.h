@@ -304,7 +304,8 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
  *   workspace   device, at least ddt_draft_topk_workspace(B, L, V, K)
  *               bytes, owned by the caller (0 for invalid sizes).
  * Errors: DDT_E_ARG (null pointer), DDT_E_SHAPE (B, L outside [1, 65535],
- * V < 1, K outside [1, 8]), DDT_E_DTYPE, DDT_E_WS; nothing is launched then.
+ * V outside [1, 1572864], K outside [1, 8]), DDT_E_DTYPE, DDT_E_WS; nothing
+ * is launched then.
  *
  * ddt_tree_build: DDTree's budget-N tree from those candidates (lucebox-hub
  * README, "02 · DFlash DDtree", "Algorithms used"; the pages give no
@@ -316,7 +317,9 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
  * lexicographically, a prefix before its extensions), numbered in that
  * order, so every parent precedes its children.  Scores are summed in fp32
  * root first.
- *   topk_idx, topk_logit, lse   device, as written by ddt_draft_topk.
+ *   topk_idx, topk_logit, lse   device, as written by ddt_draft_topk: each
+ *               row's entries by non-increasing logit, absent ones (-1)
+ *               last; rows in another order give an unspecified tree.
  *   L           draft positions, 1..16;  K as above;  N budget 1..64.
  *   root_token  device [B] int32: the root's token (the last committed one).
  *   parent, tok device out [B][N] int32: tree b is rows b*N .. b*N+n-1, node
