@@ -202,7 +202,7 @@ class Stack:
         return sum(per[k] * v for k, v in b.items())
 
 
-def draft_bench(device, B, reps=5, calls=20, settle=0.3):
+def draft_bench(device, B, reps=5, calls=20, settle=0.3, cpu_s=0.0):
     """Ahead of the verify step: draft top-K / log-sum-exp and the DDTree
     build on L=16 draft positions of the full vocabulary (bf16 logits), K=8,
     budget 22.  Timed as graph-replayed back-to-back batches (each call is a
@@ -248,10 +248,28 @@ def draft_bench(device, B, reps=5, calls=20, settle=0.3):
         del g
     nbytes = B * L * V * 2 + B * L * (K * 8 + 4)
     gbps = nbytes / (res["topk"] * 1e-6) / 1e9
-    return {"workload": f"draft_tree_b{B}_l{L}_k{K}_n{N}", "B": B, "L": L, "V": V, "K": K, "N": N,
-            "us_topk": res["topk"], "us_tree": res["tree"], "us_per_call": res["both"],
-            "topk_bytes": nbytes, "topk_GBps": gbps, "topk_frac_hbm_peak": gbps / HBM_PEAK_GBPS,
-            "timed": "graph-replayed back-to-back batch", "bound": "hbm (top-K); latency (tree)"}
+    out = {"workload": f"draft_tree_b{B}_l{L}_k{K}_n{N}", "B": B, "L": L, "V": V, "K": K, "N": N,
+           "us_topk": res["topk"], "us_tree": res["tree"], "us_per_call": res["both"],
+           "trees_per_s": B / (res["both"] * 1e-6),
+           "topk_bytes": nbytes, "topk_GBps": gbps, "topk_frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+           "timed": "graph-replayed back-to-back batch", "bound": "hbm (top-K); latency (tree)",
+           "cpu_baseline": None}
+    if cpu_s > 0:
+        # the oracle on sequence 0 of the same logits, repeated for about cpu_s seconds
+        import oracle
+        x = lg[0].float().cpu().numpy()
+        n, t0 = 0, time.perf_counter()
+        while True:
+            ti, tv, tl = oracle.draft_topk(x, K)
+            oracle.build_tree(ti, oracle.log_probs(tv, tl), N, 0)
+            n += 1
+            if time.perf_counter() - t0 >= cpu_s:
+                break
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / el, "unit": "trees/s", "cores": 1, "kind": "oracle",
+                               "sample": f"numpy fp64 oracle, {n} tree(s) from one sequence's "
+                                         f"[{L}][{V}] bf16 logits"}
+    return out
 
 
 def _traffic(kernel_src_sha):
@@ -342,6 +360,8 @@ def main():
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed sustained steps before timing (the GPU clock ramps "
                          "over a few hundred ms of load)")
+    ap.add_argument("--draft", type=int, default=0, metavar="B",
+                    help="only time the draft top-K and tree build for B sequences and print that line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel "
                          "that scales the HBM byte counters of a profiler run)")
@@ -367,6 +387,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "launches": 3}), flush=True)
+        return
+    if args.draft > 0:
+        print(json.dumps(draft_bench(dev, args.draft, settle=args.settle,
+                                     cpu_s=0.0 if args.no_cpu_baseline else 3.0)), flush=True)
         return
     print(f"[bench] building the 128K stack (seed {args.seed})", file=sys.stderr, flush=True)
     st = Stack(dev, seed=args.seed, headroom_steps=headroom(args.warmup, args.steps, args.kernel_reps))
@@ -522,7 +546,8 @@ def main():
     if not args.no_next:
         # widening ahead of the step (reported beside it, not part of `value`)
         print("[bench] draft top-K + tree build", file=sys.stderr, flush=True)
-        out["next"] = {"draft_tree": [draft_bench(dev, 1), draft_bench(dev, 8)]}
+        cs = 0.0 if args.no_cpu_baseline else 3.0
+        out["next"] = {"draft_tree": [draft_bench(dev, 1, cpu_s=cs), draft_bench(dev, 8)]}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(st, args.seed)
