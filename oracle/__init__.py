@@ -25,6 +25,11 @@ What the step computes (sources)
   log-sum-exp per draft position are read from the device logits (codehub
   lucebox-hub@main, "GPU draft top-K & verify-argmax (DFlash)"), and
   DDTree builds the budget-N tree from them (draft.py states the reading).
+* A second widening fuses a linear-attention layer's input stage into the
+  delta-net: tree conv, SiLU, split into q | k | v and L2 normalisation of
+  q and k (the Gated DeltaNet layer), the pages' idea being fewer launches
+  per forward (lucebox-hub README, "01 · Megakernel"); fused.py states the
+  readings.
 
 The pages give names and roles, not formulas.  The recurrence is the
 standard gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta Networks",
@@ -46,3 +51,4 @@ from .attn import tree_attn, gather_cache  # noqa: F401
 from .walk import argmax_rows, accept_walk  # noqa: F401
 from .commit import commit_gdn_state, commit_conv_prefix, commit_kv  # noqa: F401
 from .draft import draft_topk, log_probs, build_tree, build_tree_brute  # noqa: F401
+from .fused import qkv_split_norm, tree_conv_gdn, L2_EPS  # noqa: F401

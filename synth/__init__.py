@@ -135,6 +135,17 @@ def conv_inputs(seed, key, n, C, W, dtype="bf16", B=1):
     return dict(x=store(x, dtype), prefix=store(pre, dtype), w=store(w, dtype))
 
 
+def fused_inputs(seed, key, n, Hk, Hv, dk, dv, W, dtype="bf16", B=1):
+    """Inputs of the fused conv -> delta-net layer: conv x / prefix / w over
+    C = 2*Hk*dk + Hv*dv channels as conv_inputs draws them (stored in
+    ``dtype``), fp32 gates and the committed state as gdn_inputs draws them."""
+    C = 2 * Hk * dk + Hv * dv
+    d = conv_inputs(seed, key, n, C, W, dtype, B)
+    g = gdn_inputs(seed, key, n, Hk, Hv, dk, dv, "f32", B)
+    d.update(alpha=g["alpha"], beta=g["beta"], S_c=g["S_c"])
+    return d
+
+
 def page_layout(seed, key, T, n_nodes, page=PAGE, shuffle=True):
     """Page table for sequences with committed lengths ``T`` and room for
     ``n_nodes`` more tokens each (the commit appends up to that many).
