@@ -288,6 +288,43 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
                      void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Fused linear-attention layer: tree conv -> SiLU -> split -> L2 norm ->
+ * tree gated delta-net in one launch (the pages' single-dispatch forward,
+ * lucebox-hub README, "01 · Megakernel", applied to the verify layers of
+ * "02 · DFlash DDtree", "Implemented here"; the layer stage is the Gated
+ * DeltaNet one: short conv with SiLU, L2-normalised q and k).
+ *   y_n  = SiLU(tree conv of x over prefix ++ root path of n)   (as a2, act 1)
+ *   y_n  = [q (Hk*dk) | k (Hk*dk) | v (Hv*dv)], head-major
+ *   q, k <- x / sqrt(sum x^2 + 1e-6) per head;  v as is
+ *   out  = the a3 rule on (q, k, v, alpha, beta) from S_c
+ *   x         device [n_total][C], C = 2*Hk*dk + Hv*dv, dtype DDT_BF16 or
+ *             DDT_F32, rows and base 16-byte aligned
+ *   prefix    device [B][W-1][C] dtype, oldest first (read only; may be NULL
+ *             when plan->W == 1);  w device [C][W] dtype, tap W-1 = current
+ *   alpha, beta device [n_total][Hv] fp32 (gates)
+ *   S_c       device [B][Hv][dv][dk] fp32, read only
+ *   out       device [n_total][Hv][dv] fp32
+ *   q_out, k_out device [n_total][Hk][dk] fp32 or NULL: the normalised q, k
+ *             (the commit's UPDATE needs k; REPLAY needs q, k and v)
+ *   v_out     device [n_total][Hv][dv] fp32 or NULL: v after SiLU
+ *   node_states, node_u  as for ddt_tree_gdn (node_u: the saved u for UPDATE)
+ * A layer committed with DDT_COMMIT_UPDATE or SELECT takes k_out as its k,
+ * the fp32 gates, and gdn_dtype DDT_F32; UPDATE and SELECT then give
+ * bitwise the node state this call computes.  REPLAY (from q_out, k_out,
+ * v_out) forms its products in fp32 and agrees within rounding only.
+ * Same shape rules as ddt_tree_gdn; the workgroup's LDS,
+ * ddt_tree_conv_gdn_lds(n_max, dk) bytes, must fit in 160 KiB (it does for
+ * every n_max <= 64 at dk <= 128).
+ * Errors: DDT_E_ARG, DDT_E_SHAPE, DDT_E_DTYPE, plan errors; nothing is
+ * launched then.
+ */
+size_t ddt_tree_conv_gdn_lds(int32_t n_max, int32_t dk);
+int ddt_tree_conv_gdn(const ddt_plan *plan, const void *x, const void *prefix, const void *w, int32_t dtype,
+                      const float *alpha, const float *beta, const float *S_c, int32_t Hk, int32_t Hv,
+                      int32_t dk, int32_t dv, float scale, float *out, float *q_out, float *k_out,
+                      float *v_out, float *node_states, float *node_u, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Ahead of the verify step: draft top-K / log-sum-exp and tree construction.
  *
  * ddt_draft_topk: the draft model's K most likely tokens (1 <= K <= 8) and

@@ -154,5 +154,19 @@ def test_device_entry_points_validate_before_launch():
     assert L.ddt_tree_build(one, one, one, 1, 17, 8, 22, one, one, one, one, one, None) == -3
     assert L.ddt_tree_build(one, one, one, 1, 16, 8, 65, one, one, one, one, one, None) == -3
     assert L.ddt_tree_build(one, one, one, 1, 16, 8, 22, one, one, one, one, None, None) == -1
+    # fused conv -> delta-net: GQA mismatch, dk, dtype, null gate; LDS of the largest tree fits
+    f = L.ddt_tree_conv_gdn
+    assert f(bp, one, one, one, 2, one, one, one, 3, 4, 128, 128, 1.0, one, None, None, None, None, None,
+             None) == -3
+    assert f(bp, one, one, one, 2, one, one, one, 2, 4, 96, 128, 1.0, one, None, None, None, None, None,
+             None) == -3
+    assert f(bp, one, one, one, 2, one, one, one, 2, 4, 128, 120, 1.0, one, None, None, None, None, None,
+             None) == -3
+    assert f(bp, one, one, one, 3, one, one, one, 2, 4, 128, 128, 1.0, one, None, None, None, None, None,
+             None) == -4
+    assert f(bp, one, one, one, 2, None, one, one, 2, 4, 128, 128, 1.0, one, None, None, None, None, None,
+             None) == -1
+    assert 0 < ddt.ddt_tree_conv_gdn_lds(64, 128) <= 160 * 1024
+    assert ddt.ddt_tree_conv_gdn_lds(65, 128) == 0 and ddt.ddt_tree_conv_gdn_lds(22, 96) == 0
     for c in (-1, -2, -3, -4, -5, -6, -7, 0):
         assert ddt.status_str(c)

@@ -52,6 +52,9 @@ _SIGS = {
     "ddt_tree_conv": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
     "ddt_tree_gdn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                       _f32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "ddt_tree_conv_gdn_lds": ([_i32, _i32], _sz),
+    "ddt_tree_conv_gdn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                           _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "ddt_tree_attn_workspace": ([ctypes.POINTER(Plan), _i32, _i32, _i32, _i32, _i32], _sz),
     "ddt_tree_attn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
                        _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
@@ -186,6 +189,22 @@ def ddt_tree_gdn(plan, q, k, v, alpha, beta, S_c, scale, out, node_states=None, 
     _check(lib().ddt_tree_gdn(_plan(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                               _ptr(S_c), Hk, Hv, dk, dv, float(scale), dtype_code(q), _ptr(out),
                               _ptr(node_states), _ptr(node_u), _stream(stream)), "ddt_tree_gdn")
+
+
+def ddt_tree_conv_gdn_lds(n_max, dk):
+    return int(lib().ddt_tree_conv_gdn_lds(int(n_max), int(dk)))
+
+
+def ddt_tree_conv_gdn(plan, x, prefix, w, alpha, beta, S_c, Hk, dk, scale, out, q_out=None, k_out=None,
+                      v_out=None, node_states=None, node_u=None, stream=None):
+    """Fused layer: x [n][2*Hk*dk + Hv*dv] (bf16 or fp32), gates fp32 [n][Hv],
+    S_c [B][Hv][dv][dk]; out [n][Hv][dv]; optional q_out/k_out [n][Hk][dk],
+    v_out [n][Hv][dv], node_states, node_u."""
+    Hv, dv = int(out.shape[1]), int(out.shape[2])
+    _check(lib().ddt_tree_conv_gdn(_plan(plan), _ptr(x), _ptr(prefix), _ptr(w), dtype_code(x), _ptr(alpha),
+                                   _ptr(beta), _ptr(S_c), int(Hk), Hv, int(dk), dv, float(scale), _ptr(out),
+                                   _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(node_states), _ptr(node_u),
+                                   _stream(stream)), "ddt_tree_conv_gdn")
 
 
 def ddt_tree_attn_workspace(plan, Hq, Hkv, D, T_max, n_splits=0):

@@ -322,6 +322,143 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
   }
 }
 
+// bf16 bits of x rounded to nearest even (finite x)
+__device__ __forceinline__ unsigned bf16_rne(float x) {
+  const unsigned u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// Two-way split of 8 fp32 values into bf16 parts hi and lo, each rounded to
+// nearest: x - hi is exact in fp32 and |x - hi - lo| <= 2^-16 |x|.
+__device__ __forceinline__ void split2(gf32x4 x0, gf32x4 x1, gu32x4 (&o)[2]) {
+  unsigned short p[2][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = e < 4 ? x0[e] : x1[e - 4];
+    const unsigned hi = bf16_rne(x);
+    const float r1 = x - __uint_as_float(hi << 16);
+    p[0][e] = (unsigned short)hi;
+    p[1][e] = (unsigned short)bf16_rne(r1);
+  }
+#pragma unroll
+  for (int part = 0; part < 2; ++part)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[part][w] = (unsigned)p[part][2 * w] | ((unsigned)p[part][2 * w + 1] << 16);
+}
+
+// gdn_front for q and k that the workgroup computed itself (the fused
+// layer): they are fp32 rows in LDS (node j's row at qn + j * ldk, kn + j *
+// ldk), the tile's v rows are already in V.v, and the gates are fp32
+// [node][Hv] in global memory.  Same products and LDS outputs as
+// gdn_front; each 8-value slice of q or k is split into bf16 hi + lo, the
+// committed rows into their three exact parts.  D and F sum the part
+// products (row, column) lo*hi, mid*hi, hi*lo, hi*hi and the key products
+// lo*hi, hi*lo, hi*hi: every dropped term and the split residue stay below
+// about 2^-15 of |row| |column|.
+template <int DK, class Gid, class Anc>
+__device__ void gdn_front_lds(GdnView &V, int n, Gid gid, Anc anc_of, const float *qn, const float *kn, int ldk,
+                              const float *__restrict__ alpha, const float *__restrict__ beta,
+                              const float *__restrict__ Srows, int Hv, int h) {
+  constexpr int NS = (DK + 31) / 32;
+  constexpr int MAXRB = DDT_MAX_NODES / 16;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = nth >> 6;
+  const int lane = tid & 63, i16 = lane & 15, kk = lane >> 4;
+  const int nrb = (n + 15) / 16, ncb = (2 * n + 15) / 16;
+  const gu32x4 z = {0u, 0u, 0u, 0u};
+  const int jt = min(tid, n - 1);
+  const float a0 = alpha[(size_t)gid(jt) * Hv + h];
+  const float b0 = beta[(size_t)gid(jt) * Hv + h];
+  const unsigned long long m0 = anc_of(jt);
+  auto slice2 = [&](const float *row, int k0, gu32x4 (&o)[2]) {
+    if (k0 < DK) {
+      split2(*reinterpret_cast<const gf32x4 *>(row + k0), *reinterpret_cast<const gf32x4 *>(row + k0 + 4), o);
+    } else {
+      o[0] = z;
+      o[1] = z;
+    }
+  };
+  if (wave < ncb) {
+    gu32x4 sa[3][NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int k0 = 32 * s + 8 * kk;
+      gf32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+      if (k0 < DK) {
+        x0 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
+        x1 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
+      }
+      gu32x4 t3[3];
+      split3(x0, x1, t3);
+#pragma unroll
+      for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
+    }
+    for (int cb = wave; cb < ncb; cb += nw) {
+      const int c = 16 * cb + i16;
+      const bool con = c < 2 * n;
+      const int cn = min(c, 2 * n - 1) >> 1;
+      const float *brow = ((c & 1) ? qn : kn) + cn * ldk;
+      gu32x4 bv[NS][2];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        slice2(brow, 32 * s + 8 * kk, bv[s]);
+        if (!con) bv[s][0] = bv[s][1] = z;
+      }
+      gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[2][s]),
+                                                      __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[1][s]),
+                                                      __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
+                                                      __builtin_bit_cast(gbf16x8, bv[s][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
+                                                      __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+      }
+      if (con) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
+      }
+#pragma unroll
+      for (int m = 0; m < MAXRB; ++m) {
+        if (m < nrb) {
+          const int a = 16 * m + i16;
+          gf32x4 g4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            gu32x4 ka[2];
+            slice2(kn + min(a, n - 1) * ldk, 32 * s + 8 * kk, ka);
+            if (a >= n) ka[0] = ka[1] = z;
+            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[1]),
+                                                         __builtin_bit_cast(gbf16x8, bv[s][0]), g4, 0, 0, 0);
+            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[0]),
+                                                         __builtin_bit_cast(gbf16x8, bv[s][1]), g4, 0, 0, 0);
+            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[0]),
+                                                         __builtin_bit_cast(gbf16x8, bv[s][0]), g4, 0, 0, 0);
+          }
+          if (con) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * m + 4 * kk + e;
+              if (r < n) V.Gm[r * V.gs + c] = g4[e];
+            }
+          }
+        }
+      }
+    }
+  }
+  if (tid < n) {
+    V.al[tid] = a0;
+    V.be[tid] = b0;
+    V.anc[tid] = m0;
+  }
+  for (int j = tid + nth; j < n; j += nth) {
+    V.al[j] = alpha[(size_t)gid(j) * Hv + h];
+    V.be[j] = beta[(size_t)gid(j) * Hv + h];
+    V.anc[j] = anc_of(j);
+  }
+}
+
 // Levels of a tree (max depth + 1) from the masks, by one wavefront; the
 // result is the same in every lane.
 __device__ __forceinline__ int gdn_nlev(int n, unsigned long long a) {
