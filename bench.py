@@ -130,13 +130,43 @@ class Stack:
         b.record()
         self.timer[name].append((a, b))
 
-    def step(self, stream=None):
+    def setup_fused(self):
+        """Buffers of the fused variant of the step, where each conv + delta-net
+        pair is one ddt_tree_conv_gdn call on the conv's x (its channels are
+        the layer's q | k | v): fp32 gates, the normalised keys handed to the
+        commit, and the commit's layer table (fused layers commit as fp32)."""
+        import torch
+        ddt, c, N = self.ddt, self.c, self.c["N"]
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.fz, gl = [], []
+        for g, x, u in zip(self.gdn, self.conv, self.gdn_u):
+            f = dict(alpha=g["alpha"].float(), beta=g["beta"].float(),
+                     q=torch.zeros(N, c["Hk"], c["dk"], **f32), k=torch.zeros(N, c["Hk"], c["dk"], **f32),
+                     v=torch.zeros(N, c["Hv"], c["dv"], **f32))
+            self.fz.append(f)
+            gl.append(ddt.GdnLayer(q=f["q"].data_ptr(), k=f["k"].data_ptr(), v=f["v"].data_ptr(),
+                                   alpha=f["alpha"].data_ptr(), beta=f["beta"].data_ptr(),
+                                   S_c=g["S_c"].data_ptr(), node_u=u.data_ptr(), x=x["x"].data_ptr(),
+                                   prefix=x["prefix"].data_ptr()))
+        self.fused_table = ddt.layer_table(gl, self.device)
+
+    def fused_call(self, l, stream=None):
+        c, g, x, f = self.c, self.gdn[l], self.conv[l], self.fz[l]
+        self.ddt.ddt_tree_conv_gdn(self.tb, x["x"], x["prefix"], x["w"], f["alpha"], f["beta"], g["S_c"],
+                                   c["Hk"], c["dk"], 1.0, self.gdn_out[l], k_out=f["k"],
+                                   node_u=self.gdn_u[l], stream=stream)
+
+    def step(self, stream=None, fused=False):
         ddt, c = self.ddt, self.c
         self._timed("plan", lambda: ddt.ddt_tree_plan(self.tb, c["levels"], stream))
         gi = 0
         for a in range(c["n_attn"]):
             for _ in range(c["n_gdn"] // c["n_attn"]):
                 x, g, l = self.conv[gi], self.gdn[gi], gi
+                if fused:
+                    self._timed("fused", lambda: self.fused_call(l, stream))
+                    gi += 1
+                    continue
                 self._timed("conv", lambda: ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0,
                                                              self.conv_out[l], stream))
                 self._timed("gdn", lambda: ddt.ddt_tree_gdn(
@@ -151,9 +181,9 @@ class Stack:
                                                         self.path, self.L, self.bonus, self.walk_ws,
                                                         stream))
         self._timed("commit", lambda: ddt.ddt_commit_state(
-            self.tb, self.path, self.L, ddt.DDT_COMMIT_UPDATE, self.gdn_table, c["n_gdn"], c["Hk"],
-            c["Hv"], c["dk"], c["dv"], ddt.DDT_BF16, c["C"], ddt.DDT_BF16, self.attn_table, c["n_attn"],
-            c["Hkv"], c["D"], ddt.DDT_F16, None, self.T, stream))
+            self.tb, self.path, self.L, ddt.DDT_COMMIT_UPDATE, self.fused_table if fused else self.gdn_table,
+            c["n_gdn"], c["Hk"], c["Hv"], c["dk"], c["dv"], ddt.DDT_F32 if fused else ddt.DDT_BF16, c["C"],
+            ddt.DDT_BF16, self.attn_table, c["n_attn"], c["Hkv"], c["D"], ddt.DDT_F16, None, self.T, stream))
 
     def op_batches(self):
         """Idempotent calls of the short ops for batch timing: every layer's
@@ -270,6 +300,64 @@ def draft_bench(device, B, reps=5, calls=20, settle=0.3, cpu_s=0.0):
                                "sample": f"numpy fp64 oracle, {n} tree(s) from one sequence's "
                                          f"[{L}][{V}] bf16 logits"}
     return out
+
+
+def fused_stack_bench(st, T_set, steps, settle, reps=5):
+    """The same 128K step with each conv + delta-net pair replaced by one
+    fused ddt_tree_conv_gdn call (48 launches fewer), timed like the step:
+    eager warmup, one captured graph, settle replays with the committed
+    length put back, then `steps` timed replays from the configured
+    context.  The fused call alone is timed as a graph-replayed batch of
+    the 48 layers."""
+    import torch
+    st.setup_fused()
+    st.T.copy_(T_set)
+    for _ in range(2):
+        st.step(fused=True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step(fused=True)
+    t_end = time.perf_counter() + settle
+    while time.perf_counter() < t_end:
+        st.T.copy_(T_set)
+        for _ in range(SETTLE_BATCH):
+            g.replay()
+        torch.cuda.synchronize()
+    st.T.copy_(T_set)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    status = st.tb.status.cpu().numpy()
+    if status.any():
+        raise RuntimeError(f"device status {status}")
+    del g
+    calls = [lambda l=l: st.fused_call(l) for l in range(st.c["n_gdn"])]
+    for fn in calls:
+        fn()
+    gb = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gb):
+        for fn in calls:
+            fn()
+    gb.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        gb.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * len(calls))
+    del gb
+    st.T.copy_(T_set)
+    return {"workload": st.c["name"] + "_fused_conv_gdn", "ms_per_step": ms, "steps_per_s": 1000.0 / ms,
+            "fused_us_per_layer": us, "layers": st.c["n_gdn"],
+            "timed": "graph-replayed step after a settle phase; the fused call as a graph-replayed batch"}
 
 
 def _traffic(kernel_src_sha):
@@ -547,7 +635,13 @@ def main():
         # widening ahead of the step (reported beside it, not part of `value`)
         print("[bench] draft top-K + tree build", file=sys.stderr, flush=True)
         cs = 0.0 if args.no_cpu_baseline else 3.0
-        out["next"] = {"draft_tree": [draft_bench(dev, 1, cpu_s=cs), draft_bench(dev, 8)]}
+        print("[bench] fused conv -> delta-net step", file=sys.stderr, flush=True)
+        fz = fused_stack_bench(st, T_set, args.steps, args.settle)
+        fz["vs_unfused_step"] = ms / fz["ms_per_step"]
+        fz["unfused_conv_plus_gdn_us"] = kernels["conv"]["us_per_call"] + kernels["gdn"]["us_per_call"]
+        out["next"] = {"fused_stack": fz}
+        print("[bench] draft top-K + tree build", file=sys.stderr, flush=True)
+        out["next"]["draft_tree"] = [draft_bench(dev, 1, cpu_s=cs), draft_bench(dev, 8)]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(st, args.seed)

@@ -305,7 +305,9 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
  *   S_c       device [B][Hv][dv][dk] fp32, read only
  *   out       device [n_total][Hv][dv] fp32
  *   q_out, k_out device [n_total][Hk][dk] fp32 or NULL: the normalised q, k
- *             (the commit's UPDATE needs k; REPLAY needs q, k and v)
+ *             exactly as the kernel uses them (rounded to 16 significand
+ *             bits, within 2^-16 of the normalised values); the commit's
+ *             UPDATE needs k, REPLAY q, k and v
  *   v_out     device [n_total][Hv][dv] fp32 or NULL: v after SiLU
  *   node_states, node_u  as for ddt_tree_gdn (node_u: the saved u for UPDATE)
  * A layer committed with DDT_COMMIT_UPDATE or SELECT takes k_out as its k,

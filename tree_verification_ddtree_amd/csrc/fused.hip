@@ -13,13 +13,17 @@
 //
 // A workgroup owns 16 state rows of one value head, as the delta-net kernel
 // does.  Its prologue computes what those rows need: the q and k of its key
-// head (2*dk channels, with their norms) and its own 16 v channels, for
-// every node of the tree, from one round of global loads (x rows, taps,
-// prefix rows, conv windows).  The x slice is staged in LDS, where it
-// aliases the delta-net area that is only filled afterwards.  The
-// normalised q and k stay in LDS as fp32 rows and feed the matrix-core
-// products directly (gdn_front_lds); the rest is the delta-net kernel's
-// solve.  Sixteen workgroups share a key head and each computes its q and k
+// head (2*dk channels) and its own 16 v channels, for every node of the
+// tree, from one round of global loads (x rows, taps, prefix rows, conv
+// windows, and already the committed rows and gates the products need
+// later, so that their latency hides under the conv).  The x slice is
+// staged in LDS, where it aliases the delta-net area that is only filled
+// afterwards.  A thread convolves 8 channels of a node at a time; the lanes
+// holding one q or k row add their squares, normalise, and store the row as
+// packed bf16 pairs hi | lo << 16 (hi + lo is the layer's q or k, within
+// 2^-16 of the normalised value and exact in fp32), which feed the
+// matrix-core products directly (gdn_front_lds); the rest is the delta-net
+// kernel's solve.  Sixteen workgroups share a key head and each computes its q and k
 // itself: 2*dk*(n + W-1) extra reads from L2 per workgroup instead of a
 // second launch.
 #include "gdn_wy.h"
@@ -28,39 +32,28 @@ namespace ddt {
 
 constexpr float FUSED_EPS = 1e-6f;
 
-// LDS carve-up (bytes): the delta-net area first, with the x staging
-// [nmax][2 dk + 16] fp32 aliasing it during the prologue; then q and k rows
+// LDS carve-up (bytes): the delta-net area first, with the prologue's
+// staging aliasing it (prefix and node rows [W_max - 1 + nmax][2 dk + 16]
+// and the taps [W_max][2 dk + 16], fp32); then q and k rows
 // [nmax][dk + 4] fp32 (4 floats of padding keep the operand reads of 16
-// rows on distinct banks), per-node partial sums of squares [nmax][4], and
-// the conv windows [nmax][W_max - 1].
+// rows on distinct banks) and the conv windows as staged rows [nmax][W_max].
 struct FusedLds {
   GdnLds g;
   int ldk, xw;
-  size_t qn, kn, ssq, win, total;
+  size_t qn, kn, win, total;
   __host__ __device__ FusedLds(int nmax, int dk) : g(nmax) {
     auto up = [](size_t x) { return (x + 15) / 16 * 16; };
     ldk = dk + 4;
     xw = 2 * dk + GDN_R;
-    const size_t xs_bytes = (size_t)nmax * xw * 4;
+    const size_t xs_bytes = (size_t)(nmax + 2 * DDT_MAX_W - 1) * xw * 4;  // staged rows + tap rows
     qn = up(g.total > xs_bytes ? g.total : xs_bytes);
     kn = up(qn + (size_t)nmax * ldk * 4);
-    ssq = up(kn + (size_t)nmax * ldk * 4);
-    win = up(ssq + (size_t)nmax * 4 * 4);
-    total = up(win + (size_t)nmax * (DDT_MAX_W - 1) * 4);
+    win = up(kn + (size_t)nmax * ldk * 4);
+    total = up(win + (size_t)nmax * DDT_MAX_W * 4);
   }
 };
 
-// sum over aligned groups of G lanes (G up to 64); every lane of a group
-// gets bitwise the same sum (each step adds one pair in both partners)
-template <int G>
-__device__ __forceinline__ float group_sum64(float v) {
-  v = group_sum<(G < 16 ? G : 16)>(v);
-  if (G >= 32) v += __shfl_xor(v, 16);
-  if (G >= 64) v += __shfl_xor(v, 32);
-  return v;
-}
-
-template <typename T, int DK>
+template <typename T, int DK, int MW>
 __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__restrict__ x,
                                                        const T *__restrict__ prefix, const T *__restrict__ w,
                                                        const float *__restrict__ alpha,
@@ -70,154 +63,205 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
                                                        float *__restrict__ q_out, float *__restrict__ k_out,
                                                        float *__restrict__ v_out, float *__restrict__ node_states,
                                                        float *__restrict__ node_u) {
-  constexpr int MW = DDT_MAX_W;               // widest conv
+  // MW: conv width class (4 or 8); taps at or past W are zero
   constexpr int UE = 16 / (int)sizeof(T);     // elements per 16-byte piece
   constexpr int XW = 2 * DK + GDN_R;          // staged channels per node: q, k of the key head, v of the tile
   constexpr int PPN = XW / UE;                // pieces per node row
-  constexpr int G = DK < 64 ? DK : 64;        // lanes per norm group
   constexpr int LPR = DK / 8;                 // lanes per state row when storing states
   extern __shared__ float4 lds4[];
   char *base = reinterpret_cast<char *>(lds4);
   const FusedLds FL(P.n_max, DK);
   GdnView V(base, FL.g, P.n_max);
   float *xs = reinterpret_cast<float *>(base);  // prologue only
-  float *qn = reinterpret_cast<float *>(base + FL.qn);
+  float *qn = reinterpret_cast<float *>(base + FL.qn);  // raw fp32, then packed bf16 pairs in place
   float *kn = reinterpret_cast<float *>(base + FL.kn);
-  float *ssq = reinterpret_cast<float *>(base + FL.ssq);
   int *wins = reinterpret_cast<int *>(base + FL.win);
   const int ldk = FL.ldk;
   const int b = blockIdx.z, h = blockIdx.y, row0 = blockIdx.x * GDN_R;
   const int tid = threadIdx.x;
   const Seq s = seq_of(P, b);
-  const int n = s.n;
+  const int n = __builtin_amdgcn_readfirstlane(s.n);
   if (n == 0) return;
   const int g = h / (Hv / Hk);
   const int W = P.W, W1 = W - 1;
   const size_t C = (size_t)2 * Hk * DK + (size_t)Hv * dv;
-  // global channel of staged channel lc
-  auto gch = [&](int lc) -> size_t {
-    return lc < DK ? (size_t)g * DK + lc
-                   : lc < 2 * DK ? (size_t)Hk * DK + (size_t)g * DK + (lc - DK)
-                                 : (size_t)2 * Hk * DK + (size_t)h * dv + row0 + (lc - 2 * DK);
+  // global channel of staged channel lc (selects, no branches)
+  const int gq0 = g * DK, gk0 = Hk * DK + g * DK - DK, gv0 = 2 * Hk * DK + h * dv + row0 - 2 * DK;
+  auto gch = [&](int lc) -> int { return lc + (lc < DK ? gq0 : (lc < 2 * DK ? gk0 : gv0)); };
+  // ---- one round of loads.  Staged rows: the W-1 prefix rows (oldest
+  // first), then the n node rows, so that every conv window entry names a
+  // staged row.  Taps are staged too, tap-major (row j = j tokens back).
+  const int R = W1 + n;
+  float *tw = xs + (size_t)(W1 + P.n_max) * XW;
+  constexpr int NWE = (DDT_MAX_NODES * MW + 255) / 256;  // window entries per thread
+  constexpr int RPR = 256 / PPN;  // staged rows per pass of the workgroup (one piece column per thread)
+  constexpr int NRR = 4;          // passes of the first round
+  const int ne = n * MW, W1w = W1 > 0 ? W1 : 1;  // plan rows hold max(W-1, 1) entries
+  const int pc = tid % PPN, pr = tid / PPN;      // this thread's piece column and first row
+  const bool pon = pr < RPR;
+  const int gc = gch(pc * UE);
+  auto row_src = [&](int row) {
+    const bool pre = row < W1;
+    const size_t o = pre ? ((size_t)b * W1 + row) * C : (size_t)(s.o + row - W1) * C;
+    return (pre ? prefix : x) + o + gc;
   };
-  // ---- one round of loads
-  const bool qk = tid < 2 * DK;           // thread owns q/k channel tid
-  const int vc = tid & (GDN_R - 1);       // and v channel vc of nodes tid/16 + 16 r
-  float tq[MW], tv[MW], pq[MW - 1], pv[MW - 1];  // taps (index j = j tokens back), prefix slots
-  {
-    const size_t cq = gch(qk ? tid : 0), cv = gch(2 * DK + vc);
-#pragma unroll
-    for (int j = 0; j < MW; ++j) {
-      tq[j] = j < W ? load1(w + cq * W + (W - 1 - j)) : 0.f;
-      tv[j] = j < W ? load1(w + cv * W + (W - 1 - j)) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < MW - 1; ++j) {
-      pq[j] = j < W1 ? load1(prefix + ((size_t)b * W1 + j) * C + cq) : 0.f;
-      pv[j] = j < W1 ? load1(prefix + ((size_t)b * W1 + j) * C + cv) : 0.f;
-    }
-  }
-  for (int e = tid; e < n * W1; e += blockDim.x) wins[e] = P.win[(size_t)s.o * W1 + e];
-  {
-    const int np = n * PPN;
-    for (int p0 = tid; p0 < np; p0 += 4 * 256) {
-      gu32x4 r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int p = min(p0 + 256 * u, np - 1);
-        const int j = p / PPN, lc = (p % PPN) * UE;
-        r[u] = ld16(x + (size_t)(s.o + j) * C + gch(lc));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int p = p0 + 256 * u;
-        if (p < np) {
-          const int j = p / PPN, lc = (p % PPN) * UE;
-          float f[UE];
-          piece_f32<T>(r[u], f);
-          float *d = xs + j * XW + lc;
-          *reinterpret_cast<gf32x4 *>(d) = gf32x4{f[0], f[1], f[2], f[3]};
-          if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(d + 4) = gf32x4{f[4], f[5], f[6], f[7]};
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // conv + SiLU of staged channel lc at node i: y = act(sum_j tap_j tok_j(i)),
-  // tok_0 = the node itself, tok_j = its j-th previous token (window entry)
-  auto conv = [&](int i, int lc, const float (&tp)[MW], const float (&pr)[MW - 1]) {
-    float acc = tp[0] * xs[i * XW + lc];
-#pragma unroll
-    for (int j = 1; j < MW; ++j) {
-      if (j < W) {
-        const int src = wins[i * W1 + j - 1];
-        float v;
-        if (src >= 0) {
-          v = xs[min(src, n - 1) * XW + lc];
-        } else {
-          const int sl = min(-src - 1, W1 - 1);
-          v = 0.f;
-#pragma unroll
-          for (int jj = 0; jj < MW - 1; ++jj) v = jj == sl ? pr[jj] : v;
-        }
-        acc = fmaf(tp[j], v, acc);
-      }
-    }
-    return acc / (1.0f + __expf(-acc));
+  auto put_piece = [&](int row, gu32x4 v) {
+    float f[UE];
+    piece_f32<T>(v, f);
+    float *d = xs + row * XW + pc * UE;
+    *reinterpret_cast<gf32x4 *>(d) = gf32x4{f[0], f[1], f[2], f[3]};
+    if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(d + 4) = gf32x4{f[4], f[5], f[6], f[7]};
   };
-  // ---- pass 1: sums of squares of q and k per node (one partial per group
-  // of G lanes; a head is DK / G groups), and the v channels
-  if (tid < 2 * DK) {
-    for (int i = 0; i < n; ++i) {
-      const float y = conv(i, tid, tq, pq);
-      const float ss = group_sum64<G>(y * y);
-      if ((tid & (G - 1)) == 0) ssq[i * 4 + tid / G] = ss;
-    }
-  }
-  constexpr int VR = DDT_MAX_NODES * GDN_R / 256;  // v (node, channel) pairs per thread
-  float yv[VR];
+  // every first-round global load is issued before any store (a store
+  // waits for its value, and for everything issued before it): x / prefix
+  // pieces, taps, window entries, then the committed rows and this thread's
+  // gates and mask, which are needed only after the conv
+  gu32x4 r[NRR];
 #pragma unroll
-  for (int r = 0; r < VR; ++r) {
-    const int j = tid / GDN_R + (256 / GDN_R) * r;
-    yv[r] = j < n ? conv(j, 2 * DK + vc, tv, pv) : 0.f;
-  }
-  __syncthreads();
-  // ---- pass 2: the same conv values, normalised, into the q and k rows
-  if (tid < 2 * DK) {
-    const int hg = (tid / DK) * (DK / G);  // first group of this thread's head
-    for (int i = 0; i < n; ++i) {
-      const float y = conv(i, tid, tq, pq);
-      float nrm = ssq[i * 4 + hg];
-      if (DK / G == 2) nrm += ssq[i * 4 + hg + 1];
-      const float yn = y / sqrtf(nrm + FUSED_EPS);
-      if (tid < DK)
-        qn[i * ldk + tid] = yn;
-      else
-        kn[i * ldk + tid - DK] = yn;
-    }
-  }
-  __syncthreads();  // the x staging is dead from here on
+  for (int u = 0; u < NRR; ++u) r[u] = ld16(row_src(min(pr + RPR * u, R - 1)));
+  constexpr int NTC = (XW + 255) / 256;  // staged channels per thread for the taps
+  float tl[NTC][MW];
 #pragma unroll
-  for (int r = 0; r < VR; ++r) {
-    const int j = tid / GDN_R + (256 / GDN_R) * r;
-    if (j < n) {
-      V.v[j * GDN_R + vc] = yv[r];
-      if (v_out) v_out[((size_t)(s.o + j) * Hv + h) * dv + row0 + vc] = yv[r];
-    }
+  for (int q = 0; q < NTC; ++q) {
+    const T *wc = w + (size_t)gch(min(tid + 256 * q, XW - 1)) * W;
+#pragma unroll
+    for (int k = 0; k < MW; ++k) tl[q][k] = load1(wc + min(k, W - 1));
   }
-  // one workgroup per key head hands q and k out (for the commit)
-  if ((q_out || k_out) && blockIdx.x == 0 && h % (Hv / Hk) == 0) {
-    for (int e = tid; e < n * DK; e += blockDim.x) {
-      const int i = e / DK, c = e % DK;
-      const size_t o = ((size_t)(s.o + i) * Hk + g) * DK + c;
-      if (q_out) q_out[o] = qn[i * ldk + c];
-      if (k_out) k_out[o] = kn[i * ldk + c];
-    }
+  int wr[NWE];
+#pragma unroll
+  for (int k = 0; k < NWE; ++k) {
+    const int e = min(tid + 256 * k, ne - 1), i = e / MW, j = e % MW;
+    wr[k] = P.win[(size_t)(s.o + i) * W1w + min(max(j - 1, 0), W1w - 1)];
   }
   const float *Srows = S_c + (((size_t)b * Hv + h) * dv + row0) * DK;
-  auto gid = [&](int j) { return s.o + j; };
+  SrowOperand<DK> So;
+  if ((tid >> 6) < (2 * n + 15) / 16) So.load(Srows);
   auto anc_of = [&](int j) { return (P.anc[s.o + j] & ((2ull << j) - 1)) | (1ull << j); };
-  gdn_front_lds<DK>(V, n, gid, anc_of, qn, kn, ldk, alpha, beta, Srows, Hv, h);
+  const int jt = min(tid, n - 1);
+  const float a0 = alpha[(size_t)(s.o + jt) * Hv + h], b0 = beta[(size_t)(s.o + jt) * Hv + h];
+  const unsigned long long m0 = anc_of(jt);
+  // ---- stores into the staging area
+#pragma unroll
+  for (int u = 0; u < NRR; ++u)
+    if (pon && pr + RPR * u < R) put_piece(pr + RPR * u, r[u]);
+  for (int r0 = pr + RPR * NRR; r0 < R; r0 += RPR * NRR) {  // more rows than one round holds
+    if (!pon) break;
+    gu32x4 rr[NRR];
+#pragma unroll
+    for (int u = 0; u < NRR; ++u) rr[u] = ld16(row_src(min(r0 + RPR * u, R - 1)));
+#pragma unroll
+    for (int u = 0; u < NRR; ++u)
+      if (r0 + RPR * u < R) put_piece(r0 + RPR * u, rr[u]);
+  }
+  // taps, tap-major: row j = j tokens back (memory index W-1-j), zero past W
+#pragma unroll
+  for (int q = 0; q < NTC; ++q) {
+    const int c = tid + 256 * q;
+    if (c < XW) {
+#pragma unroll
+      for (int k = 0; k < MW; ++k) {
+        if (k < W) tw[(W - 1 - k) * XW + c] = tl[q][k];
+        if (k >= W) tw[k * XW + c] = 0.f;
+      }
+    }
+  }
+  // staged rows of every node's window, MW per node: the node itself, then
+  // its previous tokens (node j: row W-1+j; prefix slot s: row s); entries
+  // at or past W, whose taps are zero, repeat the node's own row
+#pragma unroll
+  for (int k = 0; k < NWE; ++k) {
+    const int e = tid + 256 * k;
+    if (e < ne) {
+      const int i = e / MW, j = e % MW, src = wr[k];
+      int rw = W1 + i;
+      if (j >= 1 && j < W) rw = src >= 0 ? W1 + min(src, n - 1) : min(-src - 1, W1 - 1);
+      wins[e] = rw;
+    }
+  }
+  __syncthreads();
+  // ---- the conv.  Task = 8 channels of one node.  Thread t owns q|k chunk
+  // t % QKC for nodes t / QKC + NG k, and (t < 2n) v chunk t % 2 of node t / 2.
+  constexpr int QKC = 2 * DK / 8;
+  constexpr int NG = 256 / QKC;
+  const int qc = tid % QKC, ng = tid / QKC, vch = tid & 1, iv = min(tid >> 1, n - 1);
+  float tq[MW][8], tvv[MW][8];
+#pragma unroll
+  for (int j = 0; j < MW; ++j) {
+    ld8f(tw + j * XW + 8 * qc, tq[j]);
+    ld8f(tw + j * XW + 2 * DK + 8 * vch, tvv[j]);
+  }
+  // y = SiLU(sum_j tap_j tok_j(i)) for 8 channels from lc0 (tok_0 = node i);
+  // no branches, so that all of a task's reads issue together
+  auto conv8 = [&](int i, int lc0, const float (&tp)[MW][8], float (&y)[8]) {
+    int rows[MW];
+#pragma unroll
+    for (int j = 0; j < MW; j += 4) {
+      const int4 r4 = *reinterpret_cast<const int4 *>(wins + i * MW + j);
+      rows[j] = r4.x;
+      rows[j + 1] = r4.y;
+      rows[j + 2] = r4.z;
+      rows[j + 3] = r4.w;
+    }
+    float xv[MW][8];
+#pragma unroll
+    for (int j = 0; j < MW; ++j) ld8f(xs + rows[j] * XW + lc0, xv[j]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = tp[0][e] * xv[0][e];
+#pragma unroll
+      for (int j = 1; j < MW; ++j) a = fmaf(tp[j][e], xv[j][e], a);
+      y[e] = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+    }
+  };
+  // q and k rows: the DK / 8 lanes that hold one row (aligned groups of
+  // adjacent lanes) add their squares, so every thread normalises its own
+  // 8 values and stores them as packed bf16 pairs (hi + lo is the layer's q
+  // or k, within 2^-16 of the normalised value); the workgroup that hands
+  // q and k out writes hi + lo as fp32
+  {
+    const int nk = (n + NG - 1) / NG;  // tasks of the busiest thread, the same in every thread
+    const bool isk = qc >= DK / 8;
+    const int c0 = 8 * (isk ? qc - DK / 8 : qc);
+    float *dst = (isk ? kn : qn) + c0;
+    float *ho = isk ? k_out : q_out;
+    const bool hand = ho && blockIdx.x == 0 && h % (Hv / Hk) == 0;
+    auto finish = [&](int i, const float (&y)[8]) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+      ss = group_sum<DK / 8>(ss);
+      const float inv = 1.0f / sqrtf(ss + FUSED_EPS);
+      const gu32x4 p0 = pack_hilo4(gf32x4{y[0], y[1], y[2], y[3]} * inv);
+      const gu32x4 p1 = pack_hilo4(gf32x4{y[4], y[5], y[6], y[7]} * inv);
+      if (i < n) {
+        *reinterpret_cast<gu32x4 *>(dst + i * ldk) = p0;
+        *reinterpret_cast<gu32x4 *>(dst + i * ldk + 4) = p1;
+        if (hand) {
+          float *o = ho + ((size_t)(s.o + i) * Hk + g) * DK + c0;
+          *reinterpret_cast<gf32x4 *>(o) =
+              gf32x4{unpack_hilo(p0[0]), unpack_hilo(p0[1]), unpack_hilo(p0[2]), unpack_hilo(p0[3])};
+          *reinterpret_cast<gf32x4 *>(o + 4) =
+              gf32x4{unpack_hilo(p1[0]), unpack_hilo(p1[1]), unpack_hilo(p1[2]), unpack_hilo(p1[3])};
+        }
+      }
+    };
+    for (int k = 0; k < nk; ++k) {
+      const int i = ng + NG * k;
+      float y[8];
+      conv8(min(i, n - 1), 8 * qc, tq, y);
+      finish(i, y);
+    }
+  }
+  float yv[8];
+  conv8(iv, 2 * DK + 8 * vch, tvv, yv);
+  __syncthreads();  // the x staging is dead from here on
+  if (tid < 2 * n) {
+    st8f(V.v + iv * GDN_R + 8 * vch, yv);
+    if (v_out) st8f(v_out + ((size_t)(s.o + iv) * Hv + h) * dv + row0 + 8 * vch, yv);
+  }
+  // (the front reads only the q and k rows; the barrier after it orders V.v)
+  const unsigned *qp = reinterpret_cast<const unsigned *>(qn), *kp = reinterpret_cast<const unsigned *>(kn);
+  gdn_front_lds<DK>(V, n, qp, kp, ldk, So, a0, b0, m0);
   __syncthreads();
   const int nlev = gdn_nlev(n, (tid & 63) < n ? V.anc[tid & 63] : 0ull);
   gdn_scalar<true>(V, n, nlev, scale);
@@ -232,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
   }
   if (node_states && tid < GDN_R * LPR) {
     const int lr = tid / LPR, c0 = (tid % LPR) * 8;
-    auto krow = [&](int a) { return kn + a * ldk; };
+    auto krow = [&](int a) { return PackedRow{kp + a * ldk}; };
     for (int i = 0; i < n; ++i) {
       float st[8];
       gdn_state(V, i, lr, c0, Srows + lr * DK, krow, st);
@@ -248,19 +292,27 @@ static void launch_fused(int dk, dim3 grid, size_t lds, hipStream_t st, const dd
                          const void *pre, const void *w, const float *al, const float *be, const float *S,
                          int Hk, int Hv, int dv, float scale, float *out, float *qo, float *ko, float *vo,
                          float *ns, float *nu) {
-#define DDT_FUSED(D)                                                                                   \
-  do {                                                                                                 \
-    (void)hipFuncSetAttribute((const void *)fused_kernel<T, D>,                                        \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                   \
-    hipLaunchKernelGGL((fused_kernel<T, D>), grid, dim3(256), lds, st, P, (const T *)x, (const T *)pre, \
-                       (const T *)w, al, be, S, Hk, Hv, dv, scale, out, qo, ko, vo, ns, nu);          \
+#define DDT_FUSED(D, M)                                                                                   \
+  do {                                                                                                    \
+    (void)hipFuncSetAttribute((const void *)fused_kernel<T, D, M>,                                        \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
+    hipLaunchKernelGGL((fused_kernel<T, D, M>), grid, dim3(256), lds, st, P, (const T *)x, (const T *)pre, \
+                       (const T *)w, al, be, S, Hk, Hv, dv, scale, out, qo, ko, vo, ns, nu);             \
+  } while (0)
+#define DDT_FUSED_W(D)        \
+  do {                        \
+    if (P.W <= 4)             \
+      DDT_FUSED(D, 4);        \
+    else                      \
+      DDT_FUSED(D, DDT_MAX_W); \
   } while (0)
   switch (dk) {
-    case 16: DDT_FUSED(16); break;
-    case 32: DDT_FUSED(32); break;
-    case 64: DDT_FUSED(64); break;
-    default: DDT_FUSED(128); break;
+    case 16: DDT_FUSED_W(16); break;
+    case 32: DDT_FUSED_W(32); break;
+    case 64: DDT_FUSED_W(64); break;
+    default: DDT_FUSED_W(128); break;
   }
+#undef DDT_FUSED_W
 #undef DDT_FUSED
 }
 

@@ -322,140 +322,186 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
   }
 }
 
-// bf16 bits of x rounded to nearest even (finite x)
-__device__ __forceinline__ unsigned bf16_rne(float x) {
-  const unsigned u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Packed words of two bf16 parts, hi | lo << 16, each rounded to nearest
+// even (x - hi is exact in fp32): hi + lo keeps 16 significand bits,
+// |x - (hi + lo)| <= 2^-16 |x|, and hi + lo is exact in fp32.
+// four values at once, with the packed fp32 -> bf16 conversion
+typedef __bf16 gbf16x2 __attribute__((ext_vector_type(2)));
+typedef float gf32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ gu32x4 pack_hilo4(gf32x4 v) {
+  const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector((gf32x2){v[0], v[1]}, gbf16x2));
+  const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector((gf32x2){v[2], v[3]}, gbf16x2));
+  const gf32x2 r01 = {v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u)};
+  const gf32x2 r23 = {v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u)};
+  const unsigned l01 = __builtin_bit_cast(unsigned, __builtin_convertvector(r01, gbf16x2));
+  const unsigned l23 = __builtin_bit_cast(unsigned, __builtin_convertvector(r23, gbf16x2));
+  return gu32x4{__builtin_amdgcn_perm(l01, h01, 0x05040100u), __builtin_amdgcn_perm(l01, h01, 0x07060302u),
+                __builtin_amdgcn_perm(l23, h23, 0x05040100u), __builtin_amdgcn_perm(l23, h23, 0x07060302u)};
 }
-// Two-way split of 8 fp32 values into bf16 parts hi and lo, each rounded to
-// nearest: x - hi is exact in fp32 and |x - hi - lo| <= 2^-16 |x|.
-__device__ __forceinline__ void split2(gf32x4 x0, gf32x4 x1, gu32x4 (&o)[2]) {
-  unsigned short p[2][8];
+__device__ __forceinline__ float unpack_hilo(unsigned w) {
+  return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+}
+// A row of packed words read as fp32 values hi + lo (for gdn_state).
+struct PackedRow {
+  const unsigned *p;
+  __device__ PackedRow operator+(int c) const { return {p + c}; }
+};
+__device__ __forceinline__ void load8(PackedRow r, float *f) {
+  const gu32x4 a = *reinterpret_cast<const gu32x4 *>(r.p), b = *reinterpret_cast<const gu32x4 *>(r.p + 4);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = e < 4 ? x0[e] : x1[e - 4];
-    const unsigned hi = bf16_rne(x);
-    const float r1 = x - __uint_as_float(hi << 16);
-    p[0][e] = (unsigned short)hi;
-    p[1][e] = (unsigned short)bf16_rne(r1);
+  for (int e = 0; e < 4; ++e) {
+    f[e] = unpack_hilo(a[e]);
+    f[e + 4] = unpack_hilo(b[e]);
   }
-#pragma unroll
-  for (int part = 0; part < 2; ++part)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o[part][w] = (unsigned)p[part][2 * w] | ((unsigned)p[part][2 * w + 1] << 16);
+}
+// 8 packed words at row + k0 -> the matrix-core operands of their hi and lo
+// parts (8 bf16 each)
+__device__ __forceinline__ void slice_hilo(const unsigned *row, int k0, gu32x4 (&o)[2]) {
+  const gu32x4 a = *reinterpret_cast<const gu32x4 *>(row + k0), b = *reinterpret_cast<const gu32x4 *>(row + k0 + 4);
+  o[0][0] = __builtin_amdgcn_perm(a[1], a[0], 0x05040100u);
+  o[0][1] = __builtin_amdgcn_perm(a[3], a[2], 0x05040100u);
+  o[0][2] = __builtin_amdgcn_perm(b[1], b[0], 0x05040100u);
+  o[0][3] = __builtin_amdgcn_perm(b[3], b[2], 0x05040100u);
+  o[1][0] = __builtin_amdgcn_perm(a[1], a[0], 0x07060302u);
+  o[1][1] = __builtin_amdgcn_perm(a[3], a[2], 0x07060302u);
+  o[1][2] = __builtin_amdgcn_perm(b[1], b[0], 0x07060302u);
+  o[1][3] = __builtin_amdgcn_perm(b[3], b[2], 0x07060302u);
 }
 
+// Committed-row operand of the products for this lane (row i16, the
+// lane's k-share of every 32-wide step), split exactly into three bf16
+// parts; a caller can load it early and split it later.
+template <int DK>
+struct SrowOperand {
+  static constexpr int NS = (DK + 31) / 32;
+  gf32x4 x[NS][2];
+  __device__ __forceinline__ void load(const float *__restrict__ Srows) {
+    const int lane = threadIdx.x & 63, i16 = lane & 15, kk = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int k0 = 32 * s + 8 * kk;
+      x[s][0] = x[s][1] = gf32x4{0.f, 0.f, 0.f, 0.f};
+      if (k0 < DK) {
+        x[s][0] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
+        x[s][1] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
+      }
+    }
+  }
+};
+
 // gdn_front for q and k that the workgroup computed itself (the fused
-// layer): they are fp32 rows in LDS (node j's row at qn + j * ldk, kn + j *
-// ldk), the tile's v rows are already in V.v, and the gates are fp32
-// [node][Hv] in global memory.  Same products and LDS outputs as
-// gdn_front; each 8-value slice of q or k is split into bf16 hi + lo, the
-// committed rows into their three exact parts.  D and F sum the part
-// products (row, column) lo*hi, mid*hi, hi*lo, hi*hi and the key products
-// lo*hi, hi*lo, hi*hi: every dropped term and the split residue stay below
-// about 2^-15 of |row| |column|.
-template <int DK, class Gid, class Anc>
-__device__ void gdn_front_lds(GdnView &V, int n, Gid gid, Anc anc_of, const float *qn, const float *kn, int ldk,
-                              const float *__restrict__ alpha, const float *__restrict__ beta,
-                              const float *__restrict__ Srows, int Hv, int h) {
-  constexpr int NS = (DK + 31) / 32;
-  constexpr int MAXRB = DDT_MAX_NODES / 16;
+// layer): they are rows of packed bf16 pairs in LDS (pack_hilo; node j's
+// row at qn + j * ldk, kn + j * ldk), whose values hi + lo are the q and k
+// of the layer; the tile's v rows are already in V.v, and this thread's
+// gates and mask (node tid, n <= blockDim) and its committed-row operand
+// were loaded by the caller.  Same products and LDS outputs as gdn_front;
+// the committed rows are split into their three exact parts.  D and F sum
+// the part products (row, column) lo*hi, mid*hi, hi*lo, hi*hi and the key
+// products lo*hi, hi*lo, hi*hi: every dropped term stays below about 2^-15
+// of |row| |column|.
+template <int DK, int NRB>
+__device__ void gdn_front_lds_rb(GdnView &V, int n, const unsigned *qn, const unsigned *kn, int ldk,
+                                 const SrowOperand<DK> &S) {
+  constexpr int NS = SrowOperand<DK>::NS;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = nth >> 6;
   const int lane = tid & 63, i16 = lane & 15, kk = lane >> 4;
-  const int nrb = (n + 15) / 16, ncb = (2 * n + 15) / 16;
+  const int ncb = (2 * n + 15) / 16;
   const gu32x4 z = {0u, 0u, 0u, 0u};
-  const int jt = min(tid, n - 1);
-  const float a0 = alpha[(size_t)gid(jt) * Hv + h];
-  const float b0 = beta[(size_t)gid(jt) * Hv + h];
-  const unsigned long long m0 = anc_of(jt);
-  auto slice2 = [&](const float *row, int k0, gu32x4 (&o)[2]) {
+  auto slice2 = [&](const unsigned *row, int k0, gu32x4 (&o)[2]) {
     if (k0 < DK) {
-      split2(*reinterpret_cast<const gf32x4 *>(row + k0), *reinterpret_cast<const gf32x4 *>(row + k0 + 4), o);
+      slice_hilo(row, k0, o);
     } else {
       o[0] = z;
       o[1] = z;
     }
   };
-  if (wave < ncb) {
-    gu32x4 sa[3][NS];
+  if (wave >= ncb) return;
+  gu32x4 sa[3][NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    gu32x4 t3[3];
+    split3(S.x[s][0], S.x[s][1], t3);
+#pragma unroll
+    for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
+  }
+  for (int cb = wave; cb < ncb; cb += nw) {
+    const int c = 16 * cb + i16;
+    const bool con = c < 2 * n;
+    const int cn = min(c, 2 * n - 1) >> 1;
+    const unsigned *brow = ((c & 1) ? qn : kn) + cn * ldk;
+    // every operand read of the column block before any product is stored
+    gu32x4 bv[NS][2], ka[NRB][NS][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int k0 = 32 * s + 8 * kk;
-      gf32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-      if (k0 < DK) {
-        x0 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
-        x1 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
-      }
-      gu32x4 t3[3];
-      split3(x0, x1, t3);
-#pragma unroll
-      for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
+      slice2(brow, 32 * s + 8 * kk, bv[s]);
+      if (!con) bv[s][0] = bv[s][1] = z;
     }
-    for (int cb = wave; cb < ncb; cb += nw) {
-      const int c = 16 * cb + i16;
-      const bool con = c < 2 * n;
-      const int cn = min(c, 2 * n - 1) >> 1;
-      const float *brow = ((c & 1) ? qn : kn) + cn * ldk;
-      gu32x4 bv[NS][2];
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) {
+      const int a = 16 * m + i16;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        slice2(brow, 32 * s + 8 * kk, bv[s]);
-        if (!con) bv[s][0] = bv[s][1] = z;
+        slice2(kn + min(a, n - 1) * ldk, 32 * s + 8 * kk, ka[m][s]);
+        if (a >= n) ka[m][s][0] = ka[m][s][1] = z;
       }
-      gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    }
+    gf32x4 acc = {0.f, 0.f, 0.f, 0.f}, g4[NRB];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[2][s]),
+                                                    __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[1][s]),
+                                                    __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
+                                                    __builtin_bit_cast(gbf16x8, bv[s][1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
+                                                    __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) {
+      g4[m] = gf32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[2][s]),
-                                                      __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[1][s]),
-                                                      __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
-                                                      __builtin_bit_cast(gbf16x8, bv[s][1]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
-                                                      __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
+        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][1]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
+        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][0]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s][1]), g4[m], 0, 0, 0);
+        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][0]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
       }
-      if (con) {
+    }
+    if (con) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
-      }
+      for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
 #pragma unroll
-      for (int m = 0; m < MAXRB; ++m) {
-        if (m < nrb) {
-          const int a = 16 * m + i16;
-          gf32x4 g4 = {0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < NRB; ++m)
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            gu32x4 ka[2];
-            slice2(kn + min(a, n - 1) * ldk, 32 * s + 8 * kk, ka);
-            if (a >= n) ka[0] = ka[1] = z;
-            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[1]),
-                                                         __builtin_bit_cast(gbf16x8, bv[s][0]), g4, 0, 0, 0);
-            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[0]),
-                                                         __builtin_bit_cast(gbf16x8, bv[s][1]), g4, 0, 0, 0);
-            g4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[0]),
-                                                         __builtin_bit_cast(gbf16x8, bv[s][0]), g4, 0, 0, 0);
-          }
-          if (con) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 16 * m + 4 * kk + e;
-              if (r < n) V.Gm[r * V.gs + c] = g4[e];
-            }
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * m + 4 * kk + e;
+          if (r < n) V.Gm[r * V.gs + c] = g4[m][e];
         }
-      }
     }
   }
+}
+
+// The row-block count (16 nodes each) picks the instantiation, so that all
+// of a column block's operand reads are unconditional and issue together.
+template <int DK>
+__device__ void gdn_front_lds(GdnView &V, int n, const unsigned *qn, const unsigned *kn, int ldk,
+                              const SrowOperand<DK> &S, float a0, float b0, unsigned long long m0) {
+  const int nrb = (n + 15) / 16;
+  if (nrb <= 1)
+    gdn_front_lds_rb<DK, 1>(V, n, qn, kn, ldk, S);
+  else if (nrb <= 2)
+    gdn_front_lds_rb<DK, 2>(V, n, qn, kn, ldk, S);
+  else
+    gdn_front_lds_rb<DK, DDT_MAX_NODES / 16>(V, n, qn, kn, ldk, S);
+  const int tid = threadIdx.x;
   if (tid < n) {
     V.al[tid] = a0;
     V.be[tid] = b0;
     V.anc[tid] = m0;
-  }
-  for (int j = tid + nth; j < n; j += nth) {
-    V.al[j] = alpha[(size_t)gid(j) * Hv + h];
-    V.be[j] = beta[(size_t)gid(j) * Hv + h];
-    V.anc[j] = anc_of(j);
   }
 }
 
