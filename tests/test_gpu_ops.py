@@ -246,6 +246,10 @@ ATTN_SHAPES = {
     "11_blocks": ([27], [3000], 24, 4, 256, True, True, 0),
     "d128_6_blocks": ([8, 12], [777, 1500], 16, 2, 128, True, False, 0),
     "d128_10_blocks": ([20], [2500], 16, 2, 128, True, True, 3),
+    # one sequence whose last round has 1 or 2 blocks: shared by pairs of waves
+    "5_blocks_shared": ([12], [1500], 24, 4, 256, False, False, 0),
+    "6_blocks_shared": ([16], [2222], 24, 4, 256, True, False, 0),
+    "9_blocks_shared_ragged": ([22], [4133], 24, 4, 256, True, True, 3),
 }
 
 
