@@ -30,6 +30,10 @@ What the step computes (sources)
   q and k (the Gated DeltaNet layer), the pages' idea being fewer launches
   per forward (lucebox-hub README, "01 · Megakernel"); fused.py states the
   readings.
+* Under sampling (temperature > 0, the model card's top_p and top_k when a
+  request gives none: codehub lucebox-hub@main, "Making requests") each
+  node's verify sample replaces its argmax in the walk; sample.py states
+  the reading of that acceptance rule, which the pages do not give.
 
 The pages give names and roles, not formulas.  The recurrence is the
 standard gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta Networks",
@@ -52,3 +56,4 @@ from .walk import argmax_rows, accept_walk  # noqa: F401
 from .commit import commit_gdn_state, commit_conv_prefix, commit_kv  # noqa: F401
 from .draft import draft_topk, log_probs, build_tree, build_tree_brute  # noqa: F401
 from .fused import qkv_split_norm, tree_conv_gdn, L2_EPS  # noqa: F401
+from .sample import filtered_dist, sample_row, sample_tokens  # noqa: F401

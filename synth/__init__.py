@@ -33,7 +33,7 @@ _T_Q, _T_K, _T_V, _T_A, _T_B, _T_S = 1, 2, 3, 4, 5, 6
 _T_X, _T_PRE, _T_W = 7, 8, 9
 _T_AQ, _T_KC, _T_VC, _T_KT, _T_VT, _T_PT = 10, 11, 12, 13, 14, 15
 _T_LOG, _T_TOK, _T_TREE, _T_T = 16, 17, 18, 19
-_T_DL, _T_DP = 20, 21
+_T_DL, _T_DP, _T_U = 20, 21, 22
 
 
 def rng_for(seed: int, *key: int) -> np.random.Generator:
@@ -144,6 +144,12 @@ def fused_inputs(seed, key, n, Hk, Hv, dk, dv, W, dtype="bf16", B=1):
     g = gdn_inputs(seed, key, n, Hk, Hv, dk, dv, "f32", B)
     d.update(alpha=g["alpha"], beta=g["beta"], S_c=g["S_c"])
     return d
+
+
+def uniforms(seed, key, n):
+    """One uniform in [0, 1) per tree node: the random draws of stochastic
+    acceptance, passed to both sides as inputs."""
+    return rng_for(seed, *key, _T_U).random(n).astype(np.float32)
 
 
 def page_layout(seed, key, T, n_nodes, page=PAGE, shuffle=True):
