@@ -360,6 +360,64 @@ def fused_stack_bench(st, T_set, steps, settle, reps=5):
             "timed": "graph-replayed step after a settle phase; the fused call as a graph-replayed batch"}
 
 
+def sample_bench(st, reps=5, calls=20, settle=0.3, cpu_s=0.0):
+    """Stochastic acceptance on the step's own verify logits and tree (22 x
+    151,936 bf16), the model card's sampling (temperature 1.0, top_k 20,
+    top_p 0.95), timed like the short ops: a graph of back-to-back calls,
+    replayed after a settle phase.  Reported beside the greedy walk."""
+    import torch
+    ddt, c, dev = st.ddt, st.c, st.device
+    N, V = c["N"], synth.VOCAB
+    T, k, p = 1.0, 20, 0.95
+    i32 = dict(dtype=torch.int32, device=dev)
+    u = _dev(synth.uniforms(0, (3, 4000), N), dev)
+    sample, path = torch.empty(N, **i32), torch.empty(1, st.tb.n_max, **i32)
+    L, bonus = torch.empty(1, **i32), torch.empty(1, **i32)
+    ws = torch.empty(ddt.ddt_accept_sample_workspace(st.tb, V, k), dtype=torch.uint8, device=dev)
+    call = lambda: ddt.ddt_accept_sample(st.tb, st.logits, st.tok, u, T, k, p, sample, path, L, bonus, ws)  # noqa: E731
+    call()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * calls)
+    del g
+    nbytes = N * V * 2
+    out = {"workload": "stack_t128k_n22 verify logits, temperature 1.0 top_k 20 top_p 0.95",
+           "us_per_call": us, "logits_bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+           "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+           "mean_accepted_L": float(L.float().mean().item()),
+           "timed": "graph-replayed back-to-back batch", "cpu_baseline": None}
+    if cpu_s > 0:
+        import oracle
+        lg = st.logits.float().cpu().numpy()
+        tok, uu = st.tok.cpu().numpy().astype(np.int64), u.cpu().numpy()
+        n, t0 = 0, time.perf_counter()
+        while True:
+            y, _ = oracle.sample_tokens(lg, uu, T, k, p)
+            oracle.accept_walk(st.parent, tok, y)
+            n += 1
+            if time.perf_counter() - t0 >= cpu_s:
+                break
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+                               "sample": f"numpy fp64 oracle, {n} full sampled acceptance(s) of the step"}
+    return out
+
+
 def _traffic(kernel_src_sha):
     """HBM traffic of the attention call from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source; else None."""
@@ -640,6 +698,10 @@ def main():
         fz["vs_unfused_step"] = ms / fz["ms_per_step"]
         fz["unfused_conv_plus_gdn_us"] = kernels["conv"]["us_per_call"] + kernels["gdn"]["us_per_call"]
         out["next"] = {"fused_stack": fz}
+        print("[bench] sampled acceptance", file=sys.stderr, flush=True)
+        sb = sample_bench(st, cpu_s=cs)
+        sb["greedy_walk_us"] = kernels["walk"]["us_per_call"]
+        out["next"]["sampled_walk"] = sb
         print("[bench] draft top-K + tree build", file=sys.stderr, flush=True)
         out["next"]["draft_tree"] = [draft_bench(dev, 1, cpu_s=cs), draft_bench(dev, 8)]
     if not args.no_cpu_baseline:

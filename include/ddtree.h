@@ -242,6 +242,38 @@ int ddt_accept_walk(const ddt_plan *plan, const void *logits, int32_t dtype, int
                     int32_t *bonus, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Stochastic acceptance (temperature > 0).  Requests without a temperature
+ * are sampled with the model card's settings (temperature 1.0, top_p 0.95,
+ * top_k 20; codehub lucebox-hub@main, "Making requests"); the pages give no
+ * rule for accepting a tree then.  Reading: every node's target
+ * distribution is its logits / T, cut to the top_k tokens (ties to the lower
+ * index, NaN and -inf never kept), softmaxed, cut to the smallest prefix in
+ * descending order with c_i >= top_p * total (inclusive cumulative masses),
+ * renormalised; the node's sample is the first kept token with
+ * c_i > u * R (R the kept mass, u the node's uniform).  The walk is the
+ * greedy walk with the samples in place of the argmax: every emitted token
+ * is a draw from the target, which is what recursive rejection sampling
+ * gives for deterministic candidates.
+ *   logits, dtype, V, draft_tok, path, L, bonus  as for ddt_accept_walk
+ *   uniforms  device [n_total] float in [0, 1): one draw per node (input;
+ *             the caller's random numbers)
+ *   temperature > 0 and finite; top_k 1..32; top_p in (0, 1]
+ *   sample    device out [n_total] int32: every node's sample (0 and
+ *             DDT_ST_ARGMAX for a row with no finite logit)
+ *   ws        device workspace of ddt_accept_sample_workspace() bytes.
+ * Samples are computed in fp32: a draw whose u * R lies within rounding
+ * distance of a cumulative mass may differ from an exact evaluation by the
+ * neighbouring token.
+ * Errors: DDT_E_ARG, DDT_E_SHAPE (V, top_k; V up to 393216), DDT_E_RANGE
+ * (temperature, top_p), DDT_E_DTYPE, DDT_E_WS; nothing is launched then.
+ */
+size_t ddt_accept_sample_workspace(const ddt_plan *plan, int32_t V, int32_t top_k);
+int ddt_accept_sample(const ddt_plan *plan, const void *logits, int32_t dtype, int32_t V,
+                      const int32_t *draft_tok, const float *uniforms, float temperature, int32_t top_k,
+                      float top_p, int32_t *sample, int32_t *path, int32_t *L, int32_t *bonus, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/*
  * a6. Commit of the accepted path ([P1] "Implemented here": tree-aware SSM
  * state rollback; "Why GGUF": the DDTree verify state).  In one launch, for
  * every sequence b with accepted local path p_0 = 0, ..., p_{L-1}:

@@ -168,5 +168,16 @@ def test_device_entry_points_validate_before_launch():
              None) == -1
     assert 0 < ddt.ddt_tree_conv_gdn_lds(64, 128) <= 160 * 1024
     assert ddt.ddt_tree_conv_gdn_lds(65, 128) == 0 and ddt.ddt_tree_conv_gdn_lds(22, 96) == 0
+    # sampled acceptance: temperature, top_k, top_p, dtype, workspace
+    sw = ddt.ddt_accept_sample_workspace(P, 151936, 20)
+    assert sw > 0 and ddt.ddt_accept_sample_workspace(P, 151936, 33) == 0
+    sa = L.ddt_accept_sample
+    assert sa(bp, one, 2, 151936, one, one, 0.0, 20, 0.95, one, one, one, one, one, sw, None) == -5
+    assert sa(bp, one, 2, 151936, one, one, 1.0, 33, 0.95, one, one, one, one, one, sw, None) == -3
+    assert sa(bp, one, 2, 151936, one, one, 1.0, 20, 1.5, one, one, one, one, one, sw, None) == -5
+    assert sa(bp, one, 2, 151936, one, one, 1.0, 20, 0.0, one, one, one, one, one, sw, None) == -5
+    assert sa(bp, one, 1, 151936, one, one, 1.0, 20, 0.95, one, one, one, one, one, sw, None) == -4
+    assert sa(bp, one, 2, 151936, one, one, 1.0, 20, 0.95, one, one, one, one, one, sw - 1, None) == -6
+    assert sa(bp, one, 2, 151936, one, None, 1.0, 20, 0.95, one, one, one, one, one, sw, None) == -1
     for c in (-1, -2, -3, -4, -5, -6, -7, 0):
         assert ddt.status_str(c)

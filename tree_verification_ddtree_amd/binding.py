@@ -55,6 +55,9 @@ _SIGS = {
     "ddt_tree_conv_gdn_lds": ([_i32, _i32], _sz),
     "ddt_tree_conv_gdn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                            _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "ddt_accept_sample_workspace": ([ctypes.POINTER(Plan), _i32, _i32], _sz),
+    "ddt_accept_sample": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _f32, _i32, _f32, _vp, _vp, _vp,
+                           _vp, _vp, _sz, _vp], _i32),
     "ddt_tree_attn_workspace": ([ctypes.POINTER(Plan), _i32, _i32, _i32, _i32, _i32], _sz),
     "ddt_tree_attn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
                        _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
@@ -205,6 +208,19 @@ def ddt_tree_conv_gdn(plan, x, prefix, w, alpha, beta, S_c, Hk, dk, scale, out, 
                                    _ptr(beta), _ptr(S_c), int(Hk), Hv, int(dk), dv, float(scale), _ptr(out),
                                    _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(node_states), _ptr(node_u),
                                    _stream(stream)), "ddt_tree_conv_gdn")
+
+
+def ddt_accept_sample_workspace(plan, V, top_k):
+    return int(lib().ddt_accept_sample_workspace(_plan(plan), int(V), int(top_k)))
+
+
+def ddt_accept_sample(plan, logits, draft_tok, uniforms, temperature, top_k, top_p, sample, path, L, bonus,
+                      ws, stream=None):
+    """Stochastic acceptance: logits [n][V] (bf16 or fp32), uniforms [n] fp32."""
+    _check(lib().ddt_accept_sample(_plan(plan), _ptr(logits), dtype_code(logits), int(logits.shape[-1]),
+                                   _ptr(draft_tok), _ptr(uniforms), float(temperature), int(top_k),
+                                   float(top_p), _ptr(sample), _ptr(path), _ptr(L), _ptr(bonus), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "ddt_accept_sample")
 
 
 def ddt_tree_attn_workspace(plan, Hq, Hkv, D, T_max, n_splits=0):

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libddtree.so")
-SOURCES = ["plan.hip", "conv.hip", "gdn.hip", "attn.hip", "walk.hip", "commit.hip", "draft.hip", "fused.hip"]
+SOURCES = ["plan.hip", "conv.hip", "gdn.hip", "attn.hip", "walk.hip", "commit.hip", "draft.hip", "fused.hip", "sample.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -106,6 +106,16 @@ __global__ __launch_bounds__(64) void walk_kernel(ddt_plan P, int V, int nchunk_
 
 int check_plan(const ddt_plan *P);
 
+// The walk over per-node tokens given as chunk keys (nchunk_used of them per
+// node, stride NCHUNK): used by the greedy walk and by the sampled one.
+int launch_walk(const ddt_plan *P, int V, int nchunk_used, const unsigned long long *part,
+                const int32_t *draft_tok, int32_t *tokens, int32_t *path, int32_t *L, int32_t *bonus,
+                hipStream_t st) {
+  hipLaunchKernelGGL(walk_kernel, dim3(P->B), dim3(64), 0, st, *P, V, nchunk_used, part, draft_tok, tokens,
+                     path, L, bonus);
+  return launch_status();
+}
+
 }  // namespace ddt
 
 using namespace ddt;
@@ -142,7 +152,5 @@ extern "C" int ddt_accept_walk(const ddt_plan *P, const void *logits, int32_t dt
     return DDT_E_DTYPE;
   r = launch_status();
   if (r) return r;
-  hipLaunchKernelGGL(walk_kernel, dim3(P->B), dim3(64), 0, st, *P, V, used, part, draft_tok,
-                     argmax, path, L, bonus);
-  return launch_status();
+  return launch_walk(P, V, used, part, draft_tok, argmax, path, L, bonus, st);
 }
