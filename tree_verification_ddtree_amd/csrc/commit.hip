@@ -47,27 +47,34 @@ struct UpdShape {
 // value head become the state of the last path node, rebuilt from the u
 // the tree kernel saved.  Per row, the same sequence of fp32 operations as
 // gdn_state (ancestors nearest first), so the result is bitwise the state
-// the tree kernel would persist.  The path's keys and gates are loaded once
-// for all rows of the workgroup; nothing goes through LDS.
+// the tree kernel would persist.  The path comes in with one load per lane
+// (lane r holds path node r) and is broadcast from registers, so that every
+// key, gate and u load of the path goes out in one batch instead of waiting
+// for a path entry each; nothing goes through LDS.
 template <typename T, int DK>
 __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay, const Seq &s, int b,
-                                   int h, int row0, int Lb, float *Shead) {
+                                   int h, int row0, int Lb, int pnode, float *Shead) {
   using SH = UpdShape<DK>;
-  const T *k = (const T *)lay.k, *al = (const T *)lay.alpha;
+  // global views of the record's pointers (see as_global)
+  const auto k = as_global((const T *)lay.k);
+  const auto al = as_global((const T *)lay.alpha);
+  const auto nu = as_global(lay.node_u);
+  const auto Sg = as_global_w(Shead);
   const int g = h / (A.Hv / A.Hk);
   const int tid = threadIdx.x, c0 = (tid % SH::LPR) * 8, rsub = tid / SH::LPR;
   auto uidx = [&](int gn, int row) { return ((size_t)gn * A.Hv + h) * A.dv + row; };
+  auto node = [&](int r) { return s.o + __builtin_amdgcn_readlane(pnode, r); };
   int rows[SH::PASSES];
   bool on[SH::PASSES];
   float acc[SH::PASSES][8], sc[SH::PASSES][8], ui[SH::PASSES];
-  const int gi = s.o + path_node(A, b, Lb - 1, s.n);
+  const int gi = node(Lb - 1);
 #pragma unroll
   for (int p = 0; p < SH::PASSES; ++p) {
     const int r = row0 + rsub + SH::RPP * p;
     on[p] = r < A.dv;
     rows[p] = on[p] ? r : row0;
-    ld8f(Shead + (size_t)rows[p] * DK + c0, sc[p]);
-    ui[p] = lay.node_u[uidx(gi, rows[p])];
+    load8(Sg + (size_t)rows[p] * DK + c0, sc[p]);
+    ui[p] = nu[uidx(gi, rows[p])];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
   }
@@ -75,14 +82,17 @@ __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay
   load8(k + ((size_t)gi * A.Hk + g) * DK + c0, ki);
   const float ai = load1(al + (size_t)gi * A.Hv + h);
   float w = 1.f;
-  for (int r0 = Lb - 2; r0 >= 0; r0 -= 8) {
-    float ka[8][8], aa[8];
-    int ga[8];
+  // ancestors r0, r0 - 1, .., r0 - 7 (nearest first); the first batch is
+  // straight-line code so that its loads go out with the state's
+  auto batch = [&](int r0) {
+    float ka[8][8], aa[8], ua[SH::PASSES][8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      ga[t] = s.o + path_node(A, b, max(r0 - t, 0), s.n);
-      load8(k + ((size_t)ga[t] * A.Hk + g) * DK + c0, ka[t]);
-      aa[t] = load1(al + (size_t)ga[t] * A.Hv + h);
+      const int ga = node(max(r0 - t, 0));
+      load8(k + ((size_t)ga * A.Hk + g) * DK + c0, ka[t]);
+      aa[t] = load1(al + (size_t)ga * A.Hv + h);
+#pragma unroll
+      for (int p = 0; p < SH::PASSES; ++p) ua[p][t] = nu[uidx(ga, rows[p])];
     }
     float cw[8];  // a_i w(a,i) of each ancestor, nearest first
 #pragma unroll
@@ -93,18 +103,17 @@ __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay
       }
 #pragma unroll
     for (int p = 0; p < SH::PASSES; ++p) {
-      float ua[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) ua[t] = lay.node_u[uidx(ga[t], rows[p])];
 #pragma unroll
       for (int t = 0; t < 8; ++t)
         if (r0 - t >= 0) {
-          const float c = cw[t] * ua[t];
+          const float c = cw[t] * ua[p][t];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[p][e] = fmaf(c, ka[t][e], acc[p][e]);
         }
     }
-  }
+  };
+  if (Lb >= 2) batch(Lb - 2);
+  for (int r0 = Lb - 10; r0 >= 0; r0 -= 8) batch(r0);
   const float cs = ai * w;
 #pragma unroll
   for (int p = 0; p < SH::PASSES; ++p) {
@@ -112,7 +121,7 @@ __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay
     float s8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s8[e] = fmaf(ui[p], ki[e], fmaf(cs, sc[p][e], acc[p][e]));
-    st8f(Shead + (size_t)rows[p] * DK + c0, s8);
+    st8f(Sg + (size_t)rows[p] * DK + c0, s8);
   }
 }
 
@@ -129,9 +138,14 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
   const bool lane_on = tid < GDN_R * LPR;
   const int lr = tid / LPR, c0 = (tid % LPR) * 8, row0 = tile * GDN_R;
   const Seq s = seq_of(A.P, b);
-  const int Lb = path_len(A, b, s.n);
-  if (Lb == 0) return;
   const ddt_gdn_layer lay = A.gl[layer];
+  int praw = 0;  // UPDATE: lane r's path entry r
+  if constexpr (MODE == DDT_COMMIT_UPDATE) praw = A.path[(size_t)b * A.P.n_max + min(tid & 63, A.P.n_max - 1)];
+  const int Lb = path_len(A, b, s.n);
+  // the layer record, the path and its length arrive in one round trip
+  // (without this the compiler moves each load behind the branch before it)
+  if constexpr (MODE == DDT_COMMIT_UPDATE) asm volatile("" ::"v"(praw), "v"(Lb), "v"(lay.node_u));
+  if (Lb == 0) return;
   float *Sbase = lay.S_c + (((size_t)b * A.Hv + h) * A.dv + row0) * DK;
   if (MODE == DDT_COMMIT_SELECT) {
     if (!lay.node_states) {
@@ -150,7 +164,8 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
       if (tid == 0) atomicOr((unsigned *)&A.P.status[b], DDT_ST_COMMIT);
       return;
     }
-    commit_update_rows<T, DK>(A, lay, s, b, h, tile * UpdShape<DK>::ROWS, Lb,
+    const int pnode = (praw >= 0 && praw < s.n) ? praw : 0;  // as path_node
+    commit_update_rows<T, DK>(A, lay, s, b, h, tile * UpdShape<DK>::ROWS, Lb, pnode,
                               lay.S_c + ((size_t)b * A.Hv + h) * A.dv * DK);
     return;
   }

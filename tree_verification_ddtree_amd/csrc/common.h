@@ -72,6 +72,46 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- global views
+// A pointer read from device memory (a field of a layer record) has the
+// generic address space, so its loads are flat loads, and a wait can only
+// drain flat loads all at once.  Through a global view they are global loads,
+// which a wait can take one by one (the others stay in flight).
+#define DDT_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const DDT_GLOBAL T *as_global(const T *p) {
+  return (const DDT_GLOBAL T *)p;
+}
+template <typename T>
+__device__ __forceinline__ DDT_GLOBAL T *as_global_w(T *p) {
+  return (DDT_GLOBAL T *)p;
+}
+typedef unsigned ddt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float ddt_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load8(const DDT_GLOBAL uint16_t *p, float *f) {
+  const ddt_u32x4 u = *(const DDT_GLOBAL ddt_u32x4 *)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const DDT_GLOBAL float *p, float *f) {
+  const ddt_f32x4 a = ((const DDT_GLOBAL ddt_f32x4 *)p)[0];
+  const ddt_f32x4 b = ((const DDT_GLOBAL ddt_f32x4 *)p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = a[i];
+    f[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ float load1(const DDT_GLOBAL uint16_t *p) { return bf16f(*p); }
+__device__ __forceinline__ float load1(const DDT_GLOBAL float *p) { return *p; }
+__device__ __forceinline__ void st8f(DDT_GLOBAL float *p, const float (&f)[8]) {
+  ((DDT_GLOBAL ddt_f32x4 *)p)[0] = ddt_f32x4{f[0], f[1], f[2], f[3]};
+  ((DDT_GLOBAL ddt_f32x4 *)p)[1] = ddt_f32x4{f[4], f[5], f[6], f[7]};
+}
+
 __device__ __forceinline__ void ld8f(const float *p, float (&f)[8]) {
   float4 a0 = reinterpret_cast<const float4 *>(p)[0];
   float4 a1 = reinterpret_cast<const float4 *>(p)[1];

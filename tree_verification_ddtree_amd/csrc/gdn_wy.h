@@ -167,15 +167,18 @@ __device__ __forceinline__ void split3(gf32x4 x0, gf32x4 x1, gu32x4 (&o)[3]) {
 // 4(l/16) .. 4(l/16)+3 of column l%16.  Column c of kq is k (even c) or q
 // (odd c) of node c/2; row block 0 is the committed tile, row block 1+m the
 // keys of nodes 16m .. 16m+15.  Wave w takes column blocks w, w+4, ...
-template <typename T, int DK, class Gid, class Anc>
-__device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__restrict__ q,
-                          const T *__restrict__ k, const T *__restrict__ v,
-                          const T *__restrict__ alpha, const T *__restrict__ beta,
-                          const float *__restrict__ Srows, int Hk, int Hv, int dv, int g, int h,
-                          int row0) {
+// NRB key row blocks are loaded whatever n is; rows and columns past the
+// tree are read clamped to its last node (unconditional loads, so that none
+// waits on another) and their products are never stored.
+template <typename T, int DK, int NRB, class Gid, class Anc>
+__device__ void gdn_front_rb(GdnView &V, int n, Gid gid, Anc anc_of, const T *__restrict__ q,
+                             const T *__restrict__ k, const T *__restrict__ v,
+                             const T *__restrict__ alpha, const T *__restrict__ beta,
+                             const float *__restrict__ Srows, int Hk, int Hv, int dv, int g, int h,
+                             int row0) {
   constexpr int UE = 16 / (int)sizeof(T);  // elements per 16-byte piece
   constexpr int VP = GDN_R / UE;           // pieces of one node's 16 v entries
-  constexpr int MAXRB = DDT_MAX_NODES / 16;
+  constexpr int MAXRB = NRB;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = nth >> 6;
   const int lane = tid & 63, i16 = lane & 15, kk = lane >> 4;
@@ -218,26 +221,35 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
     constexpr int NS = (DK + 31) / 32;
     gu32x4 sa[3][NS], ka[MAXRB][NS], bv[NS];
     if (wave < ncb) {
+      // the committed rows are split only after the key loads are out: a
+      // split right after its load would wait for it before they issue
+      gf32x4 sx[NS][2];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int k0 = 32 * s + 8 * kk;
-        gf32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-        if (k0 < DK) {
-          x0 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
-          x1 = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
+        sx[s][0] = sx[s][1] = gf32x4{0.f, 0.f, 0.f, 0.f};
+        if (DK >= 32 || k0 < DK) {
+          sx[s][0] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
+          sx[s][1] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
         }
-        gu32x4 t3[3];
-        split3(x0, x1, t3);
-#pragma unroll
-        for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
       }
 #pragma unroll
       for (int m = 0; m < MAXRB; ++m)
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int k0 = 32 * s + 8 * kk, a = 16 * m + i16;
-          ka[m][s] = (m < nrb && a < n && k0 < DK) ? ld16(k + ((size_t)gid(a) * Hk + g) * DK + k0) : z;
+          const int k0 = 32 * s + 8 * kk, a = min(16 * m + i16, n - 1);
+          if constexpr (DK >= 32)
+            ka[m][s] = ld16(k + ((size_t)gid(a) * Hk + g) * DK + k0);
+          else
+            ka[m][s] = k0 < DK ? ld16(k + ((size_t)gid(a) * Hk + g) * DK + k0) : z;
         }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        gu32x4 t3[3];
+        split3(sx[s][0], sx[s][1], t3);
+#pragma unroll
+        for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
+      }
     }
     for (int cb = wave; cb < ncb; cb += nw) {
       const int c = 16 * cb + i16;
@@ -245,7 +257,10 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int k0 = 32 * s + 8 * kk;
-        bv[s] = (c < 2 * n && k0 < DK) ? ld16(bsrc + k0) : z;
+        if constexpr (DK >= 32)
+          bv[s] = ld16(bsrc + k0);
+        else
+          bv[s] = k0 < DK ? ld16(bsrc + k0) : z;
       }
       if (cb == wave) put_vs(vb);
       gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -271,7 +286,6 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
   } else {
     constexpr int KS = DK / 4;  // channels per lane group
     constexpr int NP = KS / 4;  // float4 pieces per operand
-    const gf32x4 zf = {0.f, 0.f, 0.f, 0.f};
     gf32x4 sa[NP], ka[MAXRB][NP], bv[NP];
     if (wave < ncb) {
 #pragma unroll
@@ -280,10 +294,8 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
       for (int m = 0; m < MAXRB; ++m)
 #pragma unroll
         for (int s = 0; s < NP; ++s) {
-          const int a = 16 * m + i16;
-          ka[m][s] = (m < nrb && a < n)
-                         ? *reinterpret_cast<const gf32x4 *>(k + ((size_t)gid(a) * Hk + g) * DK + kk * KS + 4 * s)
-                         : zf;
+          const int a = min(16 * m + i16, n - 1);
+          ka[m][s] = *reinterpret_cast<const gf32x4 *>(k + ((size_t)gid(a) * Hk + g) * DK + kk * KS + 4 * s);
         }
     }
     auto prod = [&](const gf32x4 *A) {
@@ -302,7 +314,7 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
       const T *bsrc = kq_row(min(c, 2 * n - 1));
 #pragma unroll
       for (int s = 0; s < NP; ++s)
-        bv[s] = c < 2 * n ? *reinterpret_cast<const gf32x4 *>(bsrc + kk * KS + 4 * s) : zf;
+        bv[s] = *reinterpret_cast<const gf32x4 *>(bsrc + kk * KS + 4 * s);
       if (cb == wave) put_vs(vb);
       store_D(c, prod(sa));
 #pragma unroll
@@ -320,6 +332,21 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
     V.be[j] = load1(beta + (size_t)gid(j) * Hv + h);
     V.anc[j] = anc_of(j);
   }
+}
+
+template <typename T, int DK, class Gid, class Anc>
+__device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__restrict__ q,
+                          const T *__restrict__ k, const T *__restrict__ v,
+                          const T *__restrict__ alpha, const T *__restrict__ beta,
+                          const float *__restrict__ Srows, int Hk, int Hv, int dv, int g, int h,
+                          int row0) {
+  static_assert(DDT_MAX_NODES == 64, "key row blocks: 1, 2 or 4 of 16 nodes");
+  if (n <= 16)
+    gdn_front_rb<T, DK, 1>(V, n, gid, anc_of, q, k, v, alpha, beta, Srows, Hk, Hv, dv, g, h, row0);
+  else if (n <= 32)
+    gdn_front_rb<T, DK, 2>(V, n, gid, anc_of, q, k, v, alpha, beta, Srows, Hk, Hv, dv, g, h, row0);
+  else
+    gdn_front_rb<T, DK, 4>(V, n, gid, anc_of, q, k, v, alpha, beta, Srows, Hk, Hv, dv, g, h, row0);
 }
 
 // Packed words of two bf16 parts, hi | lo << 16, each rounded to nearest
