@@ -176,3 +176,59 @@ def test_step_is_deterministic_and_batch_independent(gpu):
     for a, b in zip(o1["attn"], o3["attn"]):
         assert torch.equal(a[o:e], b)
     assert r3["L"][0] == r1["L"][1]
+
+
+@pytest.mark.parametrize("W,cdt", [(8, "f32"), (2, "bf16"), (1, "bf16")])
+def test_commit_deep_path_and_conv_widths(gpu, W, cdt):
+    """UPDATE and SELECT over a 40-node accepted chain (several ancestor
+    batches of the UPDATE) and a short path in a second tree; conv prefixes of
+    width W over C = 2056 channels (column groups with a ragged tail): the two
+    modes bitwise equal, the oracle's state within tolerance, its prefix
+    exactly."""
+    banner(f"commit deep path, conv W={W} {cdt}")
+    C2, d2 = 2056, 64
+    trees = [synth.chain(40), synth.random_tree(synth.rng_for(7, 87), 12, 5)]
+    par, off = synth.concat_trees(trees)
+    n, B = len(par), len(trees)
+    tb = ddt.TreeBatch(par, off, W, gpu)
+    ddt.ddt_tree_plan(tb, 64)
+    paths = [oracle.root_path(t, int(np.argmax(oracle.depth(t)))) for t in trees]
+    assert len(paths[0]) == 40
+    ph = np.full((B, tb.n_max), -1, np.int32)
+    for b, p in enumerate(paths):
+        ph[b, :len(p)] = p
+    Lh = np.array([len(p) for p in paths], np.int32)
+    g = synth.gdn_inputs(7, (88,), n, Hk, Hv, d2, d2, "bf16", B=B)
+    c = synth.conv_inputs(7, (89,), n, C2, W, cdt, B=B)
+    res = {}
+    for mode in (ddt.DDT_COMMIT_UPDATE, ddt.DDT_COMMIT_SELECT):
+        dg = {k: dev(v) for k, v in g.items()}
+        dc = {k: dev(v) for k, v in c.items()}
+        o = torch.empty(n, Hv, d2, dtype=torch.float32, device=gpu)
+        ns = torch.empty(n, Hv, d2, d2, dtype=torch.float32, device=gpu) if mode == ddt.DDT_COMMIT_SELECT else None
+        nu = torch.empty(n, Hv, d2, dtype=torch.float32, device=gpu) if mode == ddt.DDT_COMMIT_UPDATE else None
+        ddt.ddt_tree_gdn(tb, dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"], dg["S_c"], 1.0, o, ns, nu)
+        gl = [ddt.GdnLayer(q=dg["q"].data_ptr(), k=dg["k"].data_ptr(), v=dg["v"].data_ptr(),
+                           alpha=dg["alpha"].data_ptr(), beta=dg["beta"].data_ptr(), S_c=dg["S_c"].data_ptr(),
+                           node_states=ns.data_ptr() if ns is not None else None,
+                           node_u=nu.data_ptr() if nu is not None else None, x=dc["x"].data_ptr(),
+                           prefix=dc["prefix"].data_ptr())]
+        T = dev(np.array([5, 5], np.int32))
+        ddt.ddt_commit_state(tb, dev(ph), dev(Lh), mode, ddt.layer_table(gl, gpu), 1, Hk, Hv, d2, d2,
+                             ddt.DDT_BF16, C2, ddt.DDT_F32 if cdt == "f32" else ddt.DDT_BF16, None, 0, 1, 64,
+                             ddt.DDT_F16, None, T)
+        torch.cuda.synchronize()
+        assert not host(tb.status).any()
+        res[mode] = (dg, dc)
+    (ug, uc), (sg, sc) = res[ddt.DDT_COMMIT_UPDATE], res[ddt.DDT_COMMIT_SELECT]
+    assert torch.equal(ug["S_c"], sg["S_c"])
+    assert torch.equal(uc["prefix"], sc["prefix"])
+    for b in range(B):
+        pg = [off[b] + j for j in paths[b]]
+        S_ref = oracle.commit_gdn_state(g["S_c"], g["q"], g["k"], g["v"], g["alpha"], g["beta"], pg, b)
+        assert rel_err(host(ug["S_c"])[b], S_ref, (0,)) < TOL
+        if W > 1:
+            pre = oracle.commit_conv_prefix(c["prefix"], c["x"], pg, b)
+            p = uc["prefix"]
+            got = host(p)[b] if cdt == "f32" else host(p.view(torch.int16)).view(np.uint16)[b]
+            assert np.array_equal(oracle.num.f64(got), pre)

@@ -23,7 +23,8 @@ struct CommitArgs {
   const int32_t *pt;
   int max_pages;
   int32_t *T;
-  int nA, nB;  // block counts of the state and prefix parts
+  int nA, nB, nC;  // block counts of the state, prefix and K/V parts
+  int ncg;         // prefix column groups (256 chunks of 16 bytes each)
 };
 
 __device__ __forceinline__ int path_len(const CommitArgs &A, int b, int n) {
@@ -39,8 +40,8 @@ __device__ __forceinline__ int path_node(const CommitArgs &A, int b, int r, int 
 // and passes per workgroup.
 template <int DK>
 struct UpdShape {
-  static constexpr int LPR = DK / 8, RPP = 256 / LPR, PASSES = 4, ROWS = RPP * PASSES;
-  static_assert(ROWS == (256 / (DK / 8)) * 4, "host computes the same row count");
+  static constexpr int LPR = DK / 8, RPP = 256 / LPR, PASSES = 2, ROWS = RPP * PASSES;
+  static_assert(ROWS == (256 / (DK / 8)) * 2, "host computes the same row count");
 };
 
 // UPDATE: the committed rows row0 .. row0 + ROWS - 1 (clipped to dv) of one
@@ -81,22 +82,23 @@ __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay
   float ki[8];
   load8(k + ((size_t)gi * A.Hk + g) * DK + c0, ki);
   const float ai = load1(al + (size_t)gi * A.Hv + h);
+  constexpr int NA = 4;  // ancestors per batch
   float w = 1.f;
-  // ancestors r0, r0 - 1, .., r0 - 7 (nearest first); the first batch is
+  // ancestors r0, r0 - 1, .., r0 - NA + 1 (nearest first); the first batch is
   // straight-line code so that its loads go out with the state's
   auto batch = [&](int r0) {
-    float ka[8][8], aa[8], ua[SH::PASSES][8];
+    float ka[NA][8], aa[NA], ua[SH::PASSES][NA];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NA; ++t) {
       const int ga = node(max(r0 - t, 0));
       load8(k + ((size_t)ga * A.Hk + g) * DK + c0, ka[t]);
       aa[t] = load1(al + (size_t)ga * A.Hv + h);
 #pragma unroll
       for (int p = 0; p < SH::PASSES; ++p) ua[p][t] = nu[uidx(ga, rows[p])];
     }
-    float cw[8];  // a_i w(a,i) of each ancestor, nearest first
+    float cw[NA];  // a_i w(a,i) of each ancestor, nearest first
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < NA; ++t)
       if (r0 - t >= 0) {
         cw[t] = ai * w;
         w *= aa[t];
@@ -104,7 +106,7 @@ __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay
 #pragma unroll
     for (int p = 0; p < SH::PASSES; ++p) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < NA; ++t)
         if (r0 - t >= 0) {
           const float c = cw[t] * ua[p][t];
 #pragma unroll
@@ -113,7 +115,7 @@ __device__ void commit_update_rows(const CommitArgs &A, const ddt_gdn_layer &lay
     }
   };
   if (Lb >= 2) batch(Lb - 2);
-  for (int r0 = Lb - 10; r0 >= 0; r0 -= 8) batch(r0);
+  for (int r0 = Lb - 2 - NA; r0 >= 0; r0 -= NA) batch(r0);
   const float cs = ai * w;
 #pragma unroll
   for (int p = 0; p < SH::PASSES; ++p) {
@@ -197,26 +199,37 @@ struct Chunk {
   static constexpr int N = 16 / sizeof(E);
 };
 
+// One unit = one (layer, sequence, group of 256 16-byte column chunks).
+// Every slot's source is loaded before any slot is written: new slot j reads
+// position Lb + j of prefix ++ x[path], and a thread's columns are its own.
 template <typename E>
 __device__ void commit_prefix(const CommitArgs &A, int unit) {
+  constexpr int NE = Chunk<E>::N;
+  const int cg = unit % A.ncg;
+  unit /= A.ncg;
   const int b = unit % A.P.B, layer = unit / A.P.B;
   const ddt_gdn_layer lay = A.gl[layer];
   if (!lay.x || !lay.prefix) return;
   const Seq s = seq_of(A.P, b);
   const int Lb = path_len(A, b, s.n), W1 = A.P.W - 1;
   if (Lb == 0 || W1 == 0) return;
-  constexpr int NE = Chunk<E>::N;
+  const int c = (cg * 256 + (int)threadIdx.x) * NE;
+  if (c >= A.C) return;
   E *pre = (E *)lay.prefix + (size_t)b * W1 * A.C;
   const E *x = (const E *)lay.x;
-  for (int c = threadIdx.x * NE; c < A.C; c += blockDim.x * NE) {
-    // new slot j = position Lb + j of prefix ++ x[path]; reads run ahead of writes
-    for (int j = 0; j < W1; ++j) {
+  uint4 v[DDT_MAX_W - 1];
+#pragma unroll
+  for (int j = 0; j < DDT_MAX_W - 1; ++j) {
+    if (j < W1) {
       const int pos = Lb + j;
       const E *src = pos < W1 ? pre + (size_t)pos * A.C + c
                               : x + (size_t)(s.o + path_node(A, b, pos - W1, s.n)) * A.C + c;
-      *reinterpret_cast<uint4 *>(pre + (size_t)j * A.C + c) = *reinterpret_cast<const uint4 *>(src);
+      v[j] = *reinterpret_cast<const uint4 *>(src);
     }
   }
+#pragma unroll
+  for (int j = 0; j < DDT_MAX_W - 1; ++j)
+    if (j < W1) *reinterpret_cast<uint4 *>(pre + (size_t)j * A.C + c) = v[j];
 }
 
 __device__ __forceinline__ bool kv_fits(const CommitArgs &A, int b, int T0, int Lb) {
@@ -265,15 +278,20 @@ __global__ void commit_len_kernel(CommitArgs A) {
 
 // One instantiation per mode, so that the replay's register demand does not
 // lower the occupancy of the streaming modes.
+// The short K/V and prefix units come first in the grid, so that they run
+// beside the state tiles instead of after them.
 template <typename T, int DK, int MODE>
 __global__ __launch_bounds__(256) void commit_kernel(CommitArgs A) {
   extern __shared__ float4 commit_lds[];
   int u = blockIdx.x;
-  if (u < A.nA) {
-    commit_state_tile<T, DK, MODE>(A, u, reinterpret_cast<char *>(commit_lds));
+  if (u < A.nC) {
+    if (A.kvdt == DDT_F16)
+      commit_kv<uint16_t>(A, u);
+    else
+      commit_kv<float>(A, u);
     return;
   }
-  u -= A.nA;
+  u -= A.nC;
   if (u < A.nB) {
     if (A.cdt == DDT_BF16)
       commit_prefix<uint16_t>(A, u);
@@ -282,10 +300,7 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs A) {
     return;
   }
   u -= A.nB;
-  if (A.kvdt == DDT_F16)
-    commit_kv<uint16_t>(A, u);
-  else
-    commit_kv<float>(A, u);
+  commit_state_tile<T, DK, MODE>(A, u, reinterpret_cast<char *>(commit_lds));
 }
 
 int check_plan(const ddt_plan *P);
@@ -330,16 +345,16 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
     if (C < 0 || C % 8) return DDT_E_SHAPE;
     A.Hk = Hk; A.Hv = Hv; A.dk = dk; A.dv = dv; A.gdt = gdn_dtype; A.C = C; A.cdt = conv_dtype;
     if (mode == DDT_COMMIT_UPDATE) {
-      const int rows = (256 / (dk / 8)) * 4;  // UpdShape<dk>::ROWS
+      const int rows = (256 / (dk / 8)) * 2;  // UpdShape<dk>::ROWS
       A.tiles = (dv + rows - 1) / rows;
     } else {
       A.tiles = dv / GDN_R;
     }
     A.nA = n_gdn * P->B * Hv * A.tiles;
-    A.nB = (C > 0) ? n_gdn * P->B : 0;
+    A.ncg = (C / (conv_dtype == DDT_BF16 ? 8 : 4) + 255) / 256;
+    A.nB = (C > 0) ? n_gdn * P->B * A.ncg : 0;
     dkc = dk;
   }
-  int nC = 0;
   if (n_attn > 0) {
     if (!attn_layers || !T) return DDT_E_ARG;
     if (Hkv < 1 || D < 1) return DDT_E_SHAPE;
@@ -349,9 +364,9 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
     const int ne = kv_dtype == DDT_F16 ? 8 : 4;
     if (D % ne) return DDT_E_SHAPE;
     A.Hkv = Hkv; A.D = D; A.kvdt = kv_dtype;
-    nC = n_attn * P->B;
+    A.nC = n_attn * P->B;
   }
-  const int blocks = A.nA + A.nB + nC;
+  const int blocks = A.nA + A.nB + A.nC;
   if (blocks == 0) return DDT_OK;
   hipStream_t st = (hipStream_t)stream;
   const bool bf = (n_gdn == 0) || gdn_dtype == DDT_BF16;
