@@ -245,11 +245,23 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
         }
       }
     };
-    for (int k = 0; k < nk; ++k) {
-      const int i = ng + NG * k;
-      float y[8];
-      conv8(min(i, n - 1), 8 * qc, tq, y);
-      finish(i, y);
+    constexpr int NKU = 3;  // tasks unrolled together (n <= 24 at DK = 128)
+    if (nk <= NKU) {
+      // independent tasks side by side: the window and row reads of all of
+      // them issue together, and the SiLU of one hides the latency of another
+      float y[NKU][8];
+#pragma unroll
+      for (int k = 0; k < NKU; ++k) conv8(min(ng + NG * k, n - 1), 8 * qc, tq, y[k]);
+#pragma unroll
+      for (int k = 0; k < NKU; ++k)
+        if (k < nk) finish(ng + NG * k, y[k]);
+    } else {
+      for (int k = 0; k < nk; ++k) {
+        const int i = ng + NG * k;
+        float y[8];
+        conv8(min(i, n - 1), 8 * qc, tq, y);
+        finish(i, y);
+      }
     }
   }
   float yv[8];

@@ -543,15 +543,19 @@ __device__ __forceinline__ int gdn_nlev(int n, unsigned long long a) {
 }
 
 // ------------------------------------------------------------ register path solve
-// One lane per (node i, rows r0..r0+3): u of every node on i's root path,
+// One lane per (node i, rows r0..r0+RW-1): u of every node on i's root path,
 // root first, then i's outputs.  Requires every node's depth < PMAX; the
 // loops are unrolled to PMAX levels (and predicated per lane), so the
 // caller picks the smallest PMAX that holds the tree.  The operations for
-// a node do not depend on PMAX.
-template <bool WANT_O, int PMAX>
+// an element do not depend on PMAX or RW: RW = 2 (trees of up to 32 nodes)
+// puts two lanes on a node, so a wavefront issues half the row arithmetic.
+template <bool WANT_O, int PMAX, int RW>
 __device__ void gdn_path_solve(GdnView &V, int n, float scale) {
   static_assert(PMAX <= GDN_PATH, "register path bound");
-  const int i = threadIdx.x & 63, r0 = (threadIdx.x >> 6) * 4;
+  static_assert(RW == 2 || RW == 4, "rows per lane");
+  typedef float vec __attribute__((ext_vector_type(RW)));
+  constexpr int NL = 256 * RW / GDN_R;  // node lanes: 64 (RW 4) or 32 (RW 2)
+  const int i = threadIdx.x % NL, r0 = (threadIdx.x / NL) * RW;
   if (i >= n || r0 >= GDN_R) return;
   const unsigned long long anc = V.anc[i] & ((2ull << i) - 1);
   const int d = min(__popcll(anc) - 1, PMAX - 1);
@@ -568,57 +572,65 @@ __device__ void gdn_path_solve(GdnView &V, int n, float scale) {
     }
   }
   float al[PMAX], be[PMAX], g[PMAX][PMAX];
-  gf32x4 Dk[PMAX], vk[PMAX];
+  vec Dk[PMAX], vk[PMAX];
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     al[k] = V.al[p[k]];
     be[k] = V.be[p[k]];
-    Dk[k] = *reinterpret_cast<const gf32x4 *>(V.D + p[k] * GDN_R + r0);
-    vk[k] = *reinterpret_cast<const gf32x4 *>(V.v + p[k] * GDN_R + r0);
+    Dk[k] = *reinterpret_cast<const vec *>(V.D + p[k] * GDN_R + r0);
+    vk[k] = *reinterpret_cast<const vec *>(V.v + p[k] * GDN_R + r0);
 #pragma unroll
     for (int j = 0; j < k; ++j) g[j][k] = V.Gm[p[j] * V.gs + 2 * p[k]];  // k_j . k_k
   }
-  gf32x4 u[PMAX], ul = {0.f, 0.f, 0.f, 0.f};
+  vec u[PMAX], ul = (vec)(0.f);
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     const float ba = be[k] * al[k];
     float w = 1.f;
-    gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    vec acc = (vec)(0.f);
 #pragma unroll
     for (int j = k - 1; j >= 0; --j) {  // ancestors nearest first
       const float m = -(ba * (w * g[j][k]));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(m, u[j][e], acc[e]);
+      for (int e = 0; e < RW; ++e) acc[e] = fmaf(m, u[j][e], acc[e]);
       w *= al[j];
     }
     const float c1 = -(al[k] * w);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[k][e] = fmaf(be[k], fmaf(c1, Dk[k][e], vk[k][e]), acc[e]);
+    for (int e = 0; e < RW; ++e) u[k][e] = fmaf(be[k], fmaf(c1, Dk[k][e], vk[k][e]), acc[e]);
     if (k == d) ul = u[k];
   }
-  *reinterpret_cast<gf32x4 *>(V.U + i * GDN_R + r0) = ul;
+  *reinterpret_cast<vec *>(V.U + i * GDN_R + r0) = ul;
   if (WANT_O) {
     float hq[PMAX];
 #pragma unroll
     for (int j = 0; j < PMAX; ++j) hq[j] = V.Gm[p[j] * V.gs + 2 * i + 1];  // k_j . q_i
-    const gf32x4 Fi = *reinterpret_cast<const gf32x4 *>(V.F + i * GDN_R + r0);
+    const vec Fi = *reinterpret_cast<const vec *>(V.F + i * GDN_R + r0);
     const float kqd = V.Gm[i * V.gs + 2 * i + 1];
     float w = 1.f, ai = 0.f;
-    gf32x4 y = {0.f, 0.f, 0.f, 0.f};
+    vec y = (vec)(0.f);
 #pragma unroll
     for (int j = PMAX - 1; j >= 0; --j) {
       if (j == d) ai = al[j];
       const bool on = j < d;  // ancestors of i, nearest first
       const float hh = w * hq[j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = on ? fmaf(hh, u[j][e], y[e]) : y[e];
+      for (int e = 0; e < RW; ++e) y[e] = on ? fmaf(hh, u[j][e], y[e]) : y[e];
       w = on ? w * al[j] : w;
     }
-    gf32x4 o;
+    vec o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = scale * fmaf(ai, fmaf(w, Fi[e], y[e]), ul[e] * kqd);
-    *reinterpret_cast<gf32x4 *>(V.O + i * GDN_R + r0) = o;
+    for (int e = 0; e < RW; ++e) o[e] = scale * fmaf(ai, fmaf(w, Fi[e], y[e]), ul[e] * kqd);
+    *reinterpret_cast<vec *>(V.O + i * GDN_R + r0) = o;
   }
+}
+
+template <bool WANT_O, int PMAX>
+__device__ void gdn_path_solve(GdnView &V, int n, float scale) {
+  if (n <= 32)
+    gdn_path_solve<WANT_O, PMAX, 2>(V, n, scale);
+  else
+    gdn_path_solve<WANT_O, PMAX, 4>(V, n, scale);
 }
 
 // ------------------------------------------------------------ deep-tree solve
