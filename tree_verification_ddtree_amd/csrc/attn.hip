@@ -584,25 +584,34 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
   const int rho = rg * A.rows_wg + rl;
   if (rho >= A.G * s.n) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int nsp = n_active_splits(A, ctx_len(A, b, nullptr));
   const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
   const int dc = tid % TPR, sg = tid / TPR;
   const float *src = A.Opart + base * D + 4 * dc;
   const size_t sstride = (size_t)A.rows_wg * D;
+  // Every load that depends on no other goes out first: the context length,
+  // wave 0's split statistics and each thread's first BATCH partials.  Split
+  // indices are clamped to the workspace's n_splits, which bounds the active
+  // count; a split that turns out inactive is skipped after its load and never
+  // multiplied, since its slot may hold anything.
+  const int nw = A.n_splits;
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (tid < 64) ml0 = A.ML[base + (size_t)min(lane, nw - 1) * A.rows_wg];
   float4 v[BATCH];
 #pragma unroll
-  for (int t = 0; t < BATCH; ++t) {
-    const int sp = sg + t * SG;
-    v[t] = sp < nsp ? *reinterpret_cast<const float4 *>(src + sp * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int t = 0; t < BATCH; ++t)
+    v[t] = *reinterpret_cast<const float4 *>(src + min(sg + t * SG, nw - 1) * sstride);
+  // the context length is read after the partials are requested (left to
+  // itself the scheduler clamps it first and so waits for it before them)
+  __builtin_amdgcn_sched_barrier(0);
+  const int nsp = n_active_splits(A, ctx_len(A, b, nullptr));
   if (tid < 64) {
-    float m = -INFINITY;
-    for (int sp = lane; sp < nsp; sp += 64) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
+    float m = lane < nsp ? fmaxf(-INFINITY, ml0.x) : -INFINITY;
+    for (int sp = lane + 64; sp < nsp; sp += 64) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     float l = 0.f;
     for (int sp = lane; sp < nsp; sp += 64) {
-      const float2 ml = A.ML[base + (size_t)sp * A.rows_wg];
+      const float2 ml = sp == lane ? ml0 : A.ML[base + (size_t)sp * A.rows_wg];
       const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f((ml.x - m) * A.c);
       wts[sp] = wgt;
       l = fmaf(ml.y, wgt, l);
