@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix peak
 METRIC = "tree-verify steps/sec (budget 22) + achieved HBM GB/s vs peak, 1 GPU"
 
 
@@ -649,6 +650,13 @@ def main():
                        else "graph-replayed back-to-back batch"}
     attn_ms = kernels["attn"]["us_per_call"] * 1e-3
     attn_bytes = ob["attn"]
+    # the attention tiles' matrix work: Q K^T and P V over the cache, 2 flops
+    # per multiply-add, every real query row (q-heads x nodes), fp16 dense peak
+    attn_flops = 2.0 * 2.0 * st.c["Hq"] * st.c["N"] * T_mid * st.c["D"]
+    kernels["attn"]["mfma"] = {
+        "flops_per_call": attn_flops, "TFLOPs": attn_flops / (attn_ms * 1e-3) / 1e12,
+        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": attn_flops / (attn_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     src = open(os.path.join(ROOT, "tree_verification_ddtree_amd", "csrc", "attn.hip"), "rb").read()
     traffic = _traffic(hashlib.sha256(src).hexdigest())
