@@ -176,7 +176,9 @@ def attn_case(gpu, trees, T, Hq, Hkv, D, dt, seed, paged=True, nan_fill=False, n
     Td = dev(T.astype(np.int32))
     T_max = int(T.max())
     ws_bytes = ddt.ddt_tree_attn_workspace(tb, Hq, Hkv, D, T_max, n_splits)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=gpu)
+    # all-ones bytes (NaN floats): slots of splits a sequence leaves unused must never be read
+    # into its result
+    ws = torch.full((max(ws_bytes, 1),), 255, dtype=torch.uint8, device=gpu)
     out = torch.full((n, Hq, D), np.nan, dtype=torch.float32, device=gpu)
     ddt.ddt_tree_attn(tb, dev(a["q"]), dev(K), dev(V), ptd, Td, T_max, dev(a["Kt"]), dev(a["Vt"]),
                       out, ws, n_splits=n_splits)
@@ -250,6 +252,9 @@ ATTN_SHAPES = {
     "5_blocks_shared": ([12], [1500], 24, 4, 256, False, False, 0),
     "6_blocks_shared": ([16], [2222], 24, 4, 256, True, False, 0),
     "9_blocks_shared_ragged": ([22], [4133], 24, 4, 256, True, True, 3),
+    # more splits than one combine batch holds (64), some of them left empty
+    "many_splits": ([22], [40000], 6, 1, 256, False, False, 100),
+    "many_splits_batch": ([22, 7], [30000, 900], 12, 2, 256, True, True, 90),
 }
 
 
