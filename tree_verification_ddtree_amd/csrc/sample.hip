@@ -175,21 +175,37 @@ __global__ __launch_bounds__(256) void samp_chunk_kernel(const T *__restrict__ l
         key[8 * j + e] = i < hi ? samp_key(load1(p + min(i, V - 1))) : 0u;
       }
   }
-  // ---- a lower bound first: the K-th largest thread maximum (at least K
-  // elements are >= it, so every element of the chunk's top K is), which
-  // leaves only a few elements for the exact selection on ordinary rows
-  unsigned tmx[1] = {0u};
+  // ---- a lower bound first.  Each wavefront takes the m-th largest of its
+  // 64 thread maxima, m = ceil(K / 4), by m rounds of a wavefront maximum
+  // that retires one holder each; the smallest of the four is the bar.  At
+  // least m elements of every wavefront are >= it, so at least K elements of
+  // the chunk are, and with them its whole top K.  It costs one workgroup
+  // barrier, and on ordinary rows leaves only a few elements above it.
+  const int lane = tid & 63, w = tid >> 6;
+  unsigned tm = 0u;
 #pragma unroll
-  for (int x = 0; x < E; ++x) tmx[0] = max(tmx[0], key[x]);
-  unsigned need = (unsigned)K;
+  for (int x = 0; x < E; ++x) tm = max(tm, key[x]);
+  unsigned wk = 0u;
+  for (int r = 0; r < (K + 3) / 4; ++r) {
+    unsigned mx = tm;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
+    wk = mx;
+    const unsigned long long holders = __ballot(tm == mx);
+    if (lane == __ffsll((long long)holders) - 1) tm = 0u;  // retire one holder
+  }
+  if (lane == 0) wsum[w] = wk;
+  __syncthreads();
+  unsigned bar = min(min(wsum[0], wsum[1]), min(wsum[2], wsum[3]));
+  // 0: some wavefront has fewer than m thread maxima above padding, NaN and
+  // -inf, so the bound is void and every finite logit qualifies
+  if (bar == 0u) bar = 1u;
+  unsigned need;
   bool all;
-  unsigned bar = radix_kth<1>(tmx, 1u, need, all, hist, wsum, sh);
-  if (all) bar = 1u;  // fewer than K threads hold a finite logit: every finite one qualifies
 
   // ---- ordinary rows leave only a few elements >= bar: they are compacted
   // into LDS (branch-free stores; elements below the bar go to a
   // per-thread dummy slot) and their ranks counted directly
-  const int lane = tid & 63, w = tid >> 6;
   float2 *dst = cand + ((size_t)row * C + ck) * K;
   {
     int c = 0;
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(256) void samp_chunk_kernel(const T *__restrict__ l
       const int up = __shfl_up(incl, o);
       if (lane >= o) incl += up;
     }
-    __syncthreads();  // wsum was last read by the searches
+    __syncthreads();  // wsum was last read for the bar
     if (lane == 63) wsum[w] = (unsigned)incl;
     __syncthreads();
     int slot = incl - c, total = 0;
