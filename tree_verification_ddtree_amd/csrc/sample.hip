@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void samp_chunk_kernel(const T *__restrict__ l
   __shared__ unsigned sh[4];
   __shared__ unsigned ckey[SAMP_KMAX];
   __shared__ int cidx[SAMP_KMAX];
-  __shared__ unsigned fkey[SAMP_FAST + 256];  // compacted candidates (+ one dummy slot per thread)
-  __shared__ int fidx[SAMP_FAST + 256];
+  // compacted candidates as (key << 32 | ~index) (+ one dummy slot per thread)
+  __shared__ unsigned long long fk[SAMP_FAST + 256];
   const int ck = blockIdx.x, row = blockIdx.y, C = gridDim.x, tid = threadIdx.x;
   const int lo = ck * chunk, hi = min(V, lo + chunk);
   const T *p = logits + (size_t)row * V;
@@ -237,19 +237,19 @@ __global__ __launch_bounds__(256) void samp_chunk_kernel(const T *__restrict__ l
           for (int e = 0; e < 8; ++e) {
             const bool q = key[8 * j + e] >= bar;
             const int d = q ? slot : SAMP_FAST + tid;
-            fkey[d] = key[8 * j + e];
-            fidx[d] = lo + 8 * (tid + 256 * j) + e;
+            fk[d] = ((unsigned long long)key[8 * j + e] << 32) | (0xffffffffu - (unsigned)(lo + 8 * (tid + 256 * j) + e));
             slot += q ? 1 : 0;
           }
         }
       }
       __syncthreads();
       if (tid < total) {
-        const unsigned long long mine = ((unsigned long long)fkey[tid] << 32) | (0xffffffffu - (unsigned)fidx[tid]);
+        const unsigned long long mine = fk[tid];
         int rank = 0;
-        for (int j = 0; j < total; ++j)
-          rank += (((unsigned long long)fkey[j] << 32) | (0xffffffffu - (unsigned)fidx[j])) > mine;
-        if (rank < K) dst[rank] = make_float2(samp_val(fkey[tid]), __int_as_float(fidx[tid]));
+#pragma unroll 4
+        for (int j = 0; j < total; ++j) rank += fk[j] > mine;
+        if (rank < K)
+          dst[rank] = make_float2(samp_val((unsigned)(mine >> 32)), __int_as_float((int)(0xffffffffu - (unsigned)mine)));
       }
       if (tid >= total && tid < K) dst[tid] = make_float2(-INFINITY, __int_as_float(-1));
       return;
