@@ -45,6 +45,24 @@ __device__ __forceinline__ float samp_val(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Wavefront maximum of unsigned keys, in every lane: DPP row shifts leave
+// each row's maximum in its lane 15, row broadcasts carry it into lane 63
+// (0 is the identity: lanes without a source keep theirs).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned samp_dpp_umax(unsigned a) {
+  const unsigned o = (unsigned)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, ROWS, 0xF, false);
+  return o > a ? o : a;
+}
+__device__ __forceinline__ unsigned samp_wave_umax(unsigned a) {
+  a = samp_dpp_umax<0x111, 0xF>(a);  // row_shr:1
+  a = samp_dpp_umax<0x112, 0xF>(a);  // row_shr:2
+  a = samp_dpp_umax<0x114, 0xF>(a);  // row_shr:4
+  a = samp_dpp_umax<0x118, 0xF>(a);  // row_shr:8
+  a = samp_dpp_umax<0x142, 0xA>(a);  // row_bcast:15 into rows 1 and 3
+  a = samp_dpp_umax<0x143, 0xC>(a);  // row_bcast:31 into rows 2 and 3
+  return (unsigned)__builtin_amdgcn_readlane((int)a, 63);
+}
+
 // Block-wide search in hist[0..nb) (LDS): the bin where, counting from the
 // top bin down (or from bin 0 up when !top), the running count reaches
 // `need`.  Publishes the bin and the count strictly before it through
@@ -187,9 +205,7 @@ __global__ __launch_bounds__(256) void samp_chunk_kernel(const T *__restrict__ l
   for (int x = 0; x < E; ++x) tm = max(tm, key[x]);
   unsigned wk = 0u;
   for (int r = 0; r < (K + 3) / 4; ++r) {
-    unsigned mx = tm;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
+    const unsigned mx = samp_wave_umax(tm);
     wk = mx;
     const unsigned long long holders = __ballot(tm == mx);
     if (lane == __ffsll((long long)holders) - 1) tm = 0u;  // retire one holder
