@@ -51,11 +51,13 @@ static int plan_fields_ok(const ddt_plan *P) {
 int check_plan(const ddt_plan *P) { return plan_fields_ok(P); }
 
 // ------------------------------------------------------------------ device plan
+// One wavefront per sequence, lane c = node c.  After the parents are in LDS
+// and each lane has chased its own root path, every table is built from
+// loops over the nodes whose index is the same in all lanes, reading the
+// other nodes' values out of their lanes (readlane) or as ballots, so no
+// step waits on an LDS read.
 __global__ __launch_bounds__(64) void plan_kernel(ddt_plan P, int max_levels) {
   __shared__ int par[64];
-  __shared__ unsigned long long ancs[64];
-  __shared__ int sz[64];
-  __shared__ int heavy[64];
   const int b = blockIdx.x, c = threadIdx.x;
   unsigned st = 0;
   int o = P.tree_off[b], e = P.tree_off[b + 1];
@@ -72,7 +74,8 @@ __global__ __launch_bounds__(64) void plan_kernel(ddt_plan P, int max_levels) {
   bool ok = (c == 0) ? (p == -1) : (p >= 0 && p < c);
   if (c < n && !ok) p = (c == 0) ? -1 : 0;  // safe stand-in: hang it off the root
   if (__ballot(c < n && !ok)) st |= DDT_ST_TREE;
-  par[c] = (c == 0) ? -1 : p;
+  const int pc = (c == 0) ? -1 : p;  // this node's parent
+  par[c] = pc;
   __syncthreads();
 
   int d = 0;
@@ -85,42 +88,49 @@ __global__ __launch_bounds__(64) void plan_kernel(ddt_plan P, int max_levels) {
       ++d;
     }
   }
-  ancs[c] = a;
   int dmax = d;
   for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
   if (dmax + 1 > max_levels) st |= DDT_ST_LEVELS;
-  __syncthreads();
 
+  // subtree sizes: the nodes whose root path holds x, one ballot per x
   int size = 0;
-  for (int j = 0; j < n; ++j) size += (int)((ancs[j] >> c) & 1ull);
-  sz[c] = size;
-  __syncthreads();
-  // heaviest child = the one visited last: largest (size, index)
-  int hv = -1;
-  for (int j = 1; j < n; ++j)
-    if (par[j] == c && (hv < 0 || sz[j] > sz[hv] || (sz[j] == sz[hv] && j > hv))) hv = j;
-  heavy[c] = hv;
-  __syncthreads();
+  for (int x = 0; x < n; ++x) {
+    const unsigned long long m = __ballot(c < n && ((a >> x) & 1ull));
+    if (c == x) size = __popcll(m);
+  }
+  // heaviest child = the one visited last: largest (size, index); and the
+  // summed sizes of the siblings visited before this node (smaller (size,
+  // index) under the same parent)
+  int hv = -1, hvs = 0, sb = 0;
+  for (int j = 1; j < n; ++j) {
+    const int pj = __builtin_amdgcn_readlane(pc, j), sj = __builtin_amdgcn_readlane(size, j);
+    if (pj == c && (hv < 0 || sj >= hvs)) {
+      hv = j;
+      hvs = sj;
+    }
+    if (pj == pc && j != c && (sj < size || (sj == size && j < c))) sb += sj;
+  }
+  // a node is light if it is not its parent's heaviest child
+  int hpar = -1;
+  for (int y = 0; y < n; ++y) {
+    const int hy = __builtin_amdgcn_readlane(hv, y);
+    if (y == pc) hpar = hy;
+  }
+  const int light1 = (c > 0 && hpar != c) ? 1 : 0;
 
   if (c < n) {
     const int g = o + c;
-    // preorder position: nodes that precede c
-    int pos = 0;
-    for (int j = 0; j < n; ++j) {
-      if (j == c) continue;
-      if ((a >> j) & 1ull) {
-        ++pos;  // a proper ancestor
-      } else if (!((ancs[j] >> c) & 1ull)) {  // not a descendant: compare branches at the LCA
-        unsigned long long common = ancs[j] & a;
-        int bj = __ffsll((long long)(ancs[j] & ~common)) - 1;
-        int bc = __ffsll((long long)(a & ~common)) - 1;
-        if (sz[bj] < sz[bc] || (sz[bj] == sz[bc] && bj < bc)) ++pos;
+    // preorder position: the proper ancestors, plus for every node x on the
+    // root path (root excluded) the subtrees of the siblings visited before x
+    int pos = d, light = 0;
+    for (int x = 1; x < n; ++x) {
+      const int sbx = __builtin_amdgcn_readlane(sb, x), lx = __builtin_amdgcn_readlane(light1, x);
+      if ((a >> x) & 1ull) {
+        pos += sbx;
+        light += lx;
       }
     }
     P.order[o + pos] = c;
-    int light = 0;
-    for (int x = c; x > 0; x = par[x])
-      if (heavy[par[x]] != x) ++light;
     P.slot[g] = light;
     P.depth[g] = d;
     P.anc[g] = a;
