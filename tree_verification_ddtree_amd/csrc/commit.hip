@@ -5,9 +5,9 @@
 // (lucebox-hub README, "02 · DFlash DDtree", "Implemented here") -- the
 // conv prefix advances over the accepted tokens, and their K/V enter the
 // cache.  One launch covers every layer: a flat grid whose first blocks
-// replay (or select) delta-net state tiles, then conv prefixes, then one
-// block per sequence appending K/V for all attention layers and finally
-// advancing T.
+// append the accepted K/V (one per attention layer and sequence), then
+// advance the conv prefixes, then update (or select, or replay) the
+// delta-net state tiles; a second, tiny launch advances T.
 #include "gdn_wy.h"
 
 namespace ddt {
