@@ -204,9 +204,12 @@ int ddt_tree_gdn(const ddt_plan *plan, const void *q, const void *k, const void 
  *   q          device [n_total][Hq][D];  Kt, Vt device [n_total][Hkv][D]
  *              (the tree's draft keys/values, not yet in the cache)
  *   out        device [n_total][Hq][D] fp32
- *   ws         device workspace of ddt_tree_attn_workspace() bytes.
- * dtype: DDT_F16 (D in {64, 128, 256} use matrix cores; D <= 64 also
- * accepted) or DDT_F32 (D <= 64).  Hq % Hkv == 0.  n_splits: number of
+ *   ws         device workspace of ddt_tree_attn_workspace() bytes (split
+ *              partials; its contents need not be initialised: a call reads
+ *              only the slots it has written).  The workspace query returns
+ *              0 when the small path runs, which needs none.
+ * dtype: DDT_F16 (D in {128, 256} on matrix cores; D in {16, 32, 64} on the
+ * small path) or DDT_F32 (D in {16, 32, 64}).  Hq % Hkv == 0.  n_splits: number of
  * context splits per (sequence, KV head), 0 = automatic.  A sequence whose
  * T[b] exceeds T_max or its page table is flagged DDT_ST_CTX and only its
  * first T_max tokens are read.
