@@ -515,8 +515,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verify step of one batch runs on a single MI355X; "
-              "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
-              file=sys.stderr)
+              "runs over several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
     import tree_verification_ddtree_amd as ddt
