@@ -361,6 +361,66 @@ def fused_stack_bench(st, T_set, steps, settle, reps=5):
             "timed": "graph-replayed step after a settle phase; the fused call as a graph-replayed batch"}
 
 
+def q8_attn_bench(st, reps=5, settle=0.4, pools=4):
+    """One attention layer of the step over an 8-bit cache of the same shape
+    (codes and per-token scales drawn on the device), against the same call
+    over the step's fp16 caches, both as graphs of back-to-back calls that
+    cycle through `pools` caches (more bytes than the last-level cache holds),
+    replayed after a settle phase."""
+    import torch
+    ddt, c, dev = st.ddt, st.c, st.device
+    Hkv, D = c["Hkv"], c["D"]
+    npages = st.kv[0][0].shape[0]
+    g = torch.Generator(device=dev)
+    g.manual_seed(8)
+    q8 = []
+    for _ in range(pools):
+        Kq = torch.randint(-127, 128, (npages, Hkv, synth.PAGE, D), generator=g, device=dev, dtype=torch.int8)
+        Vq = torch.randint(-127, 128, (npages, Hkv, D, synth.PAGE), generator=g, device=dev, dtype=torch.int8)
+        Ks = (torch.rand((npages, Hkv, synth.PAGE), generator=g, device=dev) * 0.01 + 0.005).half()
+        Vs = (torch.rand((npages, Hkv, synth.PAGE), generator=g, device=dev) * 0.01 + 0.005).half()
+        q8.append((Kq, Ks, Vq, Vs))
+    at, out = st.attn[0], st.attn_out[0]
+
+    def timed(call):
+        call(0)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(4 * pools):
+                call(i)
+        gr.replay()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle
+        while time.perf_counter() < t_end:
+            gr.replay()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * 4 * pools)
+
+    def call_q8(i):
+        Kq, Ks, Vq, Vs = q8[i % pools]
+        ddt.ddt_tree_attn_q8(st.tb, at["q"], Kq, Ks, Vq, Vs, None, st.T, st.T_max, at["Kt"], at["Vt"], out,
+                             st.attn_ws)
+
+    def call_f16(i):
+        K, V = st.kv[i % min(pools, len(st.kv))]
+        ddt.ddt_tree_attn(st.tb, at["q"], K, V, None, st.T, st.T_max, at["Kt"], at["Vt"], out, st.attn_ws)
+    us_q8, us_f16 = timed(call_q8), timed(call_f16)
+    T = int(st.T.item())
+    nbytes = st.attn_bytes(T) - T * Hkv * D * 2 * 2 + T * Hkv * (D * 2 + 2 * 2)
+    del q8
+    return {"workload": "tree_attn_t128k_n22_q8 (one layer, 8-bit K/V codes, one fp16 scale per token)",
+            "us_per_call": us_q8, "fp16_us_per_call": us_f16, "speedup_vs_fp16": us_f16 / us_q8,
+            "bytes_per_call": nbytes, "GBps": nbytes / (us_q8 * 1e-6) / 1e9,
+            "frac_hbm_peak": nbytes / (us_q8 * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "timed": "graph of back-to-back calls over 4 caches, after a settle phase"}
+
+
 def sample_bench(st, reps=5, calls=20, settle=0.3, cpu_s=0.0):
     """Stochastic acceptance on the step's own verify logits and tree (22 x
     151,936 bf16), the model card's sampling (temperature 1.0, top_k 20,
@@ -705,6 +765,8 @@ def main():
         fz["vs_unfused_step"] = ms / fz["ms_per_step"]
         fz["unfused_conv_plus_gdn_us"] = kernels["conv"]["us_per_call"] + kernels["gdn"]["us_per_call"]
         out["next"] = {"fused_stack": fz}
+        print("[bench] 8-bit KV attention", file=sys.stderr, flush=True)
+        out["next"]["q8_attention"] = q8_attn_bench(st)
         print("[bench] sampled acceptance", file=sys.stderr, flush=True)
         sb = sample_bench(st, cpu_s=cs)
         sb["greedy_walk_us"] = kernels["walk"]["us_per_call"]

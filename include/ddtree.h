@@ -223,6 +223,25 @@ int ddt_tree_attn(const ddt_plan *plan, const void *q, const void *Kc, const voi
                   void *stream);
 
 /*
+ * Variant of a4: tree-masked attention over an 8-bit KV cache ([P1] keeps its
+ * cache quantized to fit long contexts).  Same operation, layouts of pages
+ * and arguments as ddt_tree_attn, with the cache stored as
+ *   Kq  device [P][Hkv][DDT_PAGE][D] int8     Vq  device [P][Hkv][D][DDT_PAGE] int8
+ *   Ksc device [P][Hkv][DDT_PAGE] fp16        Vsc device [P][Hkv][DDT_PAGE] fp16
+ * one scale per token and KV head for K and for V.  The cache value of an
+ * entry q with scale s is fp16(q * s): the exact product rounded once to
+ * fp16 (round to nearest even); attention is over those values exactly as
+ * over an fp16 cache.  q, Kt, Vt fp16; D in {128, 256}; the workspace is
+ * ddt_tree_attn_workspace() bytes.  Errors as ddt_tree_attn; DDT_E_SHAPE for
+ * another D.
+ */
+int ddt_tree_attn_q8(const ddt_plan *plan, const void *q, const int8_t *Kq, const void *Ksc,
+                     const int8_t *Vq, const void *Vsc, const int32_t *page_table, int32_t max_pages,
+                     const int32_t *T, int32_t T_max, const void *Kt, const void *Vt, int32_t Hq,
+                     int32_t Hkv, int32_t D, float scale, int32_t n_splits, float *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
  * a5. Verify argmax and greedy acceptance walk ([P2] "Making requests":
  * greedy decoding; "GPU draft top-K & verify-argmax": the argmax is read in
  * place from the device logits and validated).

@@ -51,7 +51,7 @@ brute force on tiny inputs.
 from .tree import validate_tree, depth, root_path, ancestor_mask, conv_window, TreeError  # noqa: F401
 from .conv import tree_conv  # noqa: F401
 from .gdn import gdn_chain, tree_gdn, tree_gdn_recurrent  # noqa: F401
-from .attn import tree_attn, gather_cache  # noqa: F401
+from .attn import tree_attn, gather_cache, dequant_q8  # noqa: F401
 from .walk import argmax_rows, accept_walk  # noqa: F401
 from .commit import commit_gdn_state, commit_conv_prefix, commit_kv  # noqa: F401
 from .draft import draft_topk, log_probs, build_tree, build_tree_brute  # noqa: F401

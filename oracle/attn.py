@@ -34,6 +34,17 @@ def gather_cache(Kp, Vp, page_table, b, g, T):
     return K, V
 
 
+def dequant_q8(Kq, Ksc, Vq, Vsc):
+    """The fp16 cache an 8-bit cache stands for: each code times its token's
+    scale, the exact product rounded once to fp16 (the int8 code and the fp16
+    scale multiply exactly in fp32, 8 + 11 significant bits).  Kq [P][Hkv][16][D],
+    Vq [P][Hkv][D][16] int8; Ksc, Vsc [P][Hkv][16] fp16 (one per token).  Returns
+    the (K, V) pages in ``tree_attn``'s fp16 layouts."""
+    K = (np.asarray(Kq, np.float32) * np.asarray(Ksc, np.float32)[..., :, None]).astype(np.float16)
+    V = (np.asarray(Vq, np.float32) * np.asarray(Vsc, np.float32)[..., None, :]).astype(np.float16)
+    return K, V
+
+
 def tree_attn(parent, q, Kp, Vp, T, Kt, Vt, page_table=None, tree_off=None, scale=None,
               rows=None):
     """o[i][h] = softmax(scale * keys q_ih) values, keys/values =

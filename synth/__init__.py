@@ -34,6 +34,7 @@ _T_X, _T_PRE, _T_W = 7, 8, 9
 _T_AQ, _T_KC, _T_VC, _T_KT, _T_VT, _T_PT = 10, 11, 12, 13, 14, 15
 _T_LOG, _T_TOK, _T_TREE, _T_T = 16, 17, 18, 19
 _T_DL, _T_DP, _T_U = 20, 21, 22
+_T_KQ, _T_KS, _T_VQ, _T_VS = 23, 24, 25, 26
 
 
 def rng_for(seed: int, *key: int) -> np.random.Generator:
@@ -179,6 +180,21 @@ def kv_pool(seed, key, n_pages, Hkv, D, dtype="f16", page=PAGE):
     K = rng_for(seed, *key, _T_KC).standard_normal((n_pages, Hkv, page, D), dtype=np.float32)
     V = rng_for(seed, *key, _T_VC).standard_normal((n_pages, Hkv, D, page), dtype=np.float32)
     return store(K, dtype), store(V, dtype)
+
+
+def kv_pool_q8(seed, key, n_pages, Hkv, D, page=PAGE):
+    """Paged 8-bit KV pool (the layouts of ``kv_pool``, int8) and one fp16 scale
+    per token and KV head: Kq [n_pages][Hkv][page][D], Vq [n_pages][Hkv][D][page],
+    Ksc and Vsc [n_pages][Hkv][page].  Codes are N(0, 40) rounded and clipped to
+    +-127, scales uniform in [0.015, 0.035], so code * scale is about N(0, 1)."""
+    def codes(tag, shape):
+        x = np.rint(rng_for(seed, *key, tag).normal(0.0, 40.0, shape))
+        return np.clip(x, -127, 127).astype(np.int8)
+
+    def scales(tag):
+        return rng_for(seed, *key, tag).uniform(0.015, 0.035, (n_pages, Hkv, page)).astype(np.float16)
+    return dict(Kq=codes(_T_KQ, (n_pages, Hkv, page, D)), Ksc=scales(_T_KS),
+                Vq=codes(_T_VQ, (n_pages, Hkv, D, page)), Vsc=scales(_T_VS))
 
 
 def attn_inputs(seed, key, n, Hq, Hkv, D, dtype="f16"):

@@ -268,6 +268,51 @@ def test_attn_mfma_shapes(gpu, case):
     assert err < TOL
 
 
+# ---- 8-bit cache: the same attention over fp16(code * token scale)
+def attn_q8_case(gpu, trees, T, Hq, Hkv, D, seed, paged=True, n_splits=0):
+    tb, par, off = make_batch(trees, 4, gpu)
+    n, B = len(par), len(trees)
+    T = np.asarray(T)
+    pt, P = synth.page_layout(seed, (70,), T, [len(t) for t in trees], shuffle=paged)
+    c = synth.kv_pool_q8(seed, (70,), P, Hkv, D)
+    a = synth.attn_inputs(seed, (71,), n, Hq, Hkv, D, "f16")
+    use_pt = paged or B > 1
+    T_max = int(T.max())
+    ws = torch.full((max(ddt.ddt_tree_attn_workspace(tb, Hq, Hkv, D, T_max, n_splits), 1),), 255,
+                    dtype=torch.uint8, device=gpu)
+    out = torch.full((n, Hq, D), np.nan, dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_attn_q8(tb, dev(a["q"]), dev(c["Kq"]), dev(c["Ksc"]), dev(c["Vq"]), dev(c["Vsc"]),
+                         dev(pt) if use_pt else None, dev(T.astype(np.int32)), T_max, dev(a["Kt"]),
+                         dev(a["Vt"]), out, ws, n_splits=n_splits)
+    torch.cuda.synchronize()
+    K, V = oracle.dequant_q8(c["Kq"], c["Ksc"], c["Vq"], c["Vsc"])
+    ref = oracle.tree_attn(par, a["q"], K, V, T, a["Kt"], a["Vt"], page_table=pt if use_pt else None,
+                           tree_off=off)
+    got = host(out)
+    assert np.isfinite(got).all()
+    return rel_err(got, ref, (0, 1))
+
+
+ATTN_Q8 = {
+    #  name: (tree sizes, T, Hq, Hkv, D, paged, n_splits)
+    "tree_only": ([22], [0], 24, 4, 256, False, 0),
+    "one_tile": ([22], [32], 24, 4, 256, False, 0),
+    "three_tiles": ([22], [100], 24, 4, 256, False, 0),
+    "ragged_4133": ([22], [4133], 24, 4, 256, False, 0),
+    "batch_paged": ([22, 8, 64], [1500, 37, 3001], 24, 4, 256, True, 0),
+    "d128": ([16, 32], [777, 2048], 16, 2, 128, True, 3),
+    "many_splits": ([22], [40000], 6, 1, 256, False, 100),
+}
+
+
+@pytest.mark.parametrize("case", list(ATTN_Q8))
+def test_attn_q8(gpu, case):
+    sizes, T, Hq, Hkv, D, paged, ns = ATTN_Q8[case]
+    banner(f"attn q8 {case}: sizes {sizes} T {T} Hq {Hq} Hkv {Hkv} D {D} splits {ns}")
+    trees = [synth.random_tree(synth.rng_for(16, 72, b), n, 10) for b, n in enumerate(sizes)]
+    assert attn_q8_case(gpu, trees, T, Hq, Hkv, D, 16, paged=paged, n_splits=ns) < TOL
+
+
 def _plant_cache(t):
     """Key at cache position t of sequence 0, KV head 0 := 4 q of node 0,
     q head 0: that row's score there is ~4|q|^2, about 90 binades (at scale

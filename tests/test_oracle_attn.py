@@ -128,3 +128,34 @@ def test_row_subset():
     sub = oracle.tree_attn(par, a["q"], K, V, [T], a["Kt"], a["Vt"], page_table=pt, rows=rows)
     for i, h in rows:
         np.testing.assert_allclose(sub[i, h], full[i, h], rtol=1e-13)
+
+
+# ---- 8-bit cache (dequantisation in front of the same attention)
+def test_q8_dequant_hand_values():
+    """Codes times a power-of-two scale are exact; 3 * fp16(0.1) lies exactly
+    halfway between two fp16 neighbours and rounds to the even one."""
+    Kq = np.array([-127, -1, 0, 1, 127], np.int8).reshape(1, 1, 1, 5)
+    Ksc = np.array([0.5], np.float16).reshape(1, 1, 1)
+    Vq = np.array([3], np.int8).reshape(1, 1, 1, 1)
+    Vsc = np.array([0.1], np.float16).reshape(1, 1, 1)  # 0.0999755859375
+    K, V = oracle.dequant_q8(Kq, Ksc, Vq, Vsc)
+    assert K.dtype == np.float16 and V.dtype == np.float16
+    assert K.ravel().tolist() == [-63.5, -0.5, 0.0, 0.5, 63.5]
+    # 3 * 0.0999755859375 = 0.2999267578125 = 1228.5 * 2**-12: ties to 1228 * 2**-12
+    assert float(V.ravel()[0]) == 1228 * 2.0 ** -12
+
+
+def test_q8_dequant_scales_follow_tokens():
+    """One scale per token: K row t and V column t of a page take token t's
+    scale (distinct powers of two, so every product is exact)."""
+    P, H, D = 2, 2, 4
+    Kq = np.arange(P * H * 16 * D).reshape(P, H, 16, D).astype(np.int64) % 7 - 3
+    Vq = np.arange(P * H * D * 16).reshape(P, H, D, 16).astype(np.int64) % 5 - 2
+    Ksc = (2.0 ** -(np.arange(P * H * 16).reshape(P, H, 16) % 8)).astype(np.float16)
+    Vsc = (2.0 ** -((np.arange(P * H * 16).reshape(P, H, 16) + 3) % 8)).astype(np.float16)
+    K, V = oracle.dequant_q8(Kq.astype(np.int8), Ksc, Vq.astype(np.int8), Vsc)
+    for p in range(P):
+        for h in range(H):
+            for t in range(16):
+                assert (K[p, h, t, :].astype(np.float64) == Kq[p, h, t, :] * float(Ksc[p, h, t])).all()
+                assert (V[p, h, :, t].astype(np.float64) == Vq[p, h, :, t] * float(Vsc[p, h, t])).all()

@@ -59,6 +59,8 @@ _SIGS = {
     "ddt_accept_sample": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _f32, _i32, _f32, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp], _i32),
     "ddt_tree_attn_workspace": ([ctypes.POINTER(Plan), _i32, _i32, _i32, _i32, _i32], _sz),
+    "ddt_tree_attn_q8": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp,
+                          _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp], _i32),
     "ddt_tree_attn": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
                        _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
     "ddt_accept_walk_workspace": ([ctypes.POINTER(Plan), _i32], _sz),
@@ -239,6 +241,20 @@ def ddt_tree_attn(plan, q, Kc, Vc, page_table, T, T_max, Kt, Vt, out, ws, scale=
                                max_pages, _ptr(T), int(T_max), _ptr(Kt), _ptr(Vt), Hq, Hkv, D,
                                scale, dtype_code(q), int(n_splits), _ptr(out), _ptr(ws), wsb,
                                _stream(stream)), "ddt_tree_attn")
+
+
+def ddt_tree_attn_q8(plan, q, Kq, Ksc, Vq, Vsc, page_table, T, T_max, Kt, Vt, out, ws, scale=None,
+                     n_splits=0, stream=None):
+    """8-bit cache: Kq [P][Hkv][16][D], Vq [P][Hkv][D][16] int8; Ksc, Vsc [P][Hkv][16] fp16."""
+    Hq, D = int(q.shape[1]), int(q.shape[2])
+    Hkv = int(Kt.shape[1])
+    max_pages = int(page_table.shape[1]) if page_table is not None else 0
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(D))
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().ddt_tree_attn_q8(_plan(plan), _ptr(q), _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc),
+                                  _ptr(page_table), max_pages, _ptr(T), int(T_max), _ptr(Kt), _ptr(Vt),
+                                  Hq, Hkv, D, scale, int(n_splits), _ptr(out), _ptr(ws), wsb,
+                                  _stream(stream)), "ddt_tree_attn_q8")
 
 
 def ddt_accept_walk_workspace(plan, V):

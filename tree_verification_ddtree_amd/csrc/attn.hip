@@ -57,6 +57,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 struct AttnArgs {
   ddt_plan P;
   const _Float16 *q, *Kc, *Vc, *Kt, *Vt;
+  // 8-bit cache (Q8 path): Kq [P][Hkv][16][D], Vq [P][Hkv][D][16] int8 and one
+  // fp16 scale per token, Ksc / Vsc [P][Hkv][16]; a value is fp16(q * scale)
+  const int8_t *Kq, *Vq;
+  const _Float16 *Ksc, *Vsc;
   const int32_t *pt;
   int max_pages;
   const int32_t *T;
@@ -123,6 +127,20 @@ struct Lds {
 };
 constexpr int NSTAGE = 4;  // LDS ring depth: NSTAGE - 1 tiles in flight
 
+// Q8 path: the 8-bit tiles land in their own 4-stage ring (K [32 tokens][D],
+// V [2 pages][D][16], then the tile's 32 K and 32 V scales), and one pass per
+// tile, between two workgroup barriers, turns the next tile into the fp16
+// stage layout above, in a 2-stage fp16 ring.
+template <int D>
+struct LdsQ8 {
+  static constexpr int K_BYTES = TILE * D, V_BYTES = TILE * D, S_BYTES = 4 * TILE;
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + S_BYTES;
+  static constexpr int Q_STAGES = 4;   // 8-bit ring: up to three tiles in flight
+  static constexpr int FP_STAGES = 2;  // fp16 ring: K of the next tile, V of this one
+  static constexpr int FP_BYTES = FP_STAGES * Lds<D>::STAGE * 2;  // fp16 ring, bytes
+  static constexpr int TOTAL = FP_BYTES + Q_STAGES * STAGE_BYTES;
+};
+
 // K rows are whole bank periods (256 B) long, so rows r and r + 8 collide
 // without the low four row bits in the swizzle; V channel rows are a quarter
 // period, so channels d and d + 4 share banks unless bits 2-3 of d enter.
@@ -140,10 +158,14 @@ __device__ __forceinline__ int key_of_krow(int r) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int NB>
+template <int D, int NB, bool Q8>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
   constexpr int WAVE_CH = (TILE * CPR) / 256;  // direct loads per wave, per tensor and tile
+  // direct loads per wave and tile: fp16 K and V; or 8-bit K and V (1 KB
+  // pieces, D / 128 each per wave) plus one load of the tile's scales
+  constexpr int LPT = Q8 ? 2 * (D / 128) + 1 : 2 * WAVE_CH;
+  constexpr int FPS = Q8 ? LdsQ8<D>::FP_STAGES : NSTAGE;  // fp16 stages the matrix cores read
   constexpr int KS = D / 32;               // k-steps of the score product
   constexpr int DB = D / 16;               // channel blocks of the value product
   extern __shared__ half8 lds_raw[];
@@ -239,16 +261,79 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     }
   };
 
+  // ---- Q8: 8-bit tile -> its staging stage, straight from HBM.  A page of
+  // one KV head is 16 * D contiguous bytes of K (token-major) and of V
+  // (channel-major); the stage holds both pages of each back to back, so
+  // wave w copies 1 KB pieces w, w + 4 of each, and then the 32-byte scale
+  // run w (K page 0, K page 1, V page 0, V page 1) with eight lanes.
+  char *const qbase = reinterpret_cast<char *>(lds) + (Q8 ? LdsQ8<D>::FP_BYTES : 0);
+  auto issue_q8 = [&](int stage, int pg0, int pg1) {
+    char *St = qbase + stage * LdsQ8<D>::STAGE_BYTES;
+    constexpr int PPP = 16 * D / 1024;  // 1 KB pieces per page
+#pragma unroll
+    for (int k = 0; k < D / 128; ++k) {
+      const int piece = w + 4 * k, half = piece / PPP, off = (piece % PPP) * 1024 + 16 * lane;
+      const size_t pb = ((size_t)(half ? pg1 : pg0) * A.Hkv + kv_head) * 16 * D;
+      __builtin_amdgcn_global_load_lds((const void *)(A.Kq + pb + off), (lds_void *)(St + piece * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < D / 128; ++k) {
+      const int piece = w + 4 * k, half = piece / PPP, off = (piece % PPP) * 1024 + 16 * lane;
+      const size_t pb = ((size_t)(half ? pg1 : pg0) * A.Hkv + kv_head) * 16 * D;
+      __builtin_amdgcn_global_load_lds((const void *)(A.Vq + pb + off),
+                                       (lds_void *)(St + LdsQ8<D>::K_BYTES + piece * 1024), 16, 0, 0);
+    }
+    const _Float16 *sc = (w < 2 ? A.Ksc : A.Vsc) + ((size_t)((w & 1) ? pg1 : pg0) * A.Hkv + kv_head) * 16;
+    if (lane < 8)
+      __builtin_amdgcn_global_load_lds((const void *)(sc + 2 * lane),
+                                       (lds_void *)(St + LdsQ8<D>::K_BYTES + LdsQ8<D>::V_BYTES + 32 * w), 4, 0, 0);
+  };
+  // Q8: one pass turns a staged 8-bit tile into the fp16 stage layout (the
+  // same rows, chunks and swizzles as a direct fp16 tile).  A value is
+  // fp16(q * scale): q becomes fp16 exactly (0x6400 | (q + 128) is 1024 + q
+  // + 128), and the product is rounded once, by the fp16 multiply.
+  auto convert_q8 = [&](int qstage, int fstage) {
+    const char *St = qbase + qstage * LdsQ8<D>::STAGE_BYTES;
+    const _Float16 *Sc = reinterpret_cast<const _Float16 *>(St + LdsQ8<D>::K_BYTES + LdsQ8<D>::V_BYTES);
+    _Float16 *Kf = lds + fstage * Lds<D>::STAGE;
+    _Float16 *Vf = Kf + Lds<D>::K_HALVES;
+    auto dq8 = [](uint2 q, half8 sc8) -> half8 {
+      const unsigned x0 = q.x ^ 0x80808080u, x1 = q.y ^ 0x80808080u;
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 hb = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
+                        __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
+                        __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
+                        __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
+      const half8 v = __builtin_bit_cast(half8, hb) - (half8)(_Float16)1152.0f;
+      return v * sc8;
+    };
+#pragma unroll 2
+    for (int k = 0; k < (TILE * CPR) / 256; ++k) {  // K: token tau, chunk cc
+      const int idx = threadIdx.x + 256 * k, tau = idx / CPR, cc = idx % CPR;
+      const uint2 q = *reinterpret_cast<const uint2 *>(St + tau * D + 8 * cc);
+      const half8 v = dq8(q, (half8)Sc[tau]);
+      const int r = krow_of(tau);
+      *reinterpret_cast<half8 *>(Kf + r * D + 8 * (cc ^ ksw(r))) = v;
+    }
+#pragma unroll 2
+    for (int k = 0; k < (4 * D) / 256; ++k) {  // V: channel d, keys 8 qg .. 8 qg + 7
+      const int idx = threadIdx.x + 256 * k, d = idx >> 2, qg = idx & 3;
+      const uint2 q = *reinterpret_cast<const uint2 *>(St + LdsQ8<D>::K_BYTES + (qg >> 1) * 16 * D + 16 * d + 8 * (qg & 1));
+      const half8 sv = *reinterpret_cast<const half8 *>(Sc + TILE + 8 * qg);
+      *reinterpret_cast<half8 *>(Vf + d * 32 + 8 * (qg ^ vsw(d))) = dq8(q, sv);
+    }
+  };
+
   // wait until at most `later` tiles' direct loads are outstanding (each
-  // tile is 2 * WAVE_CH loads per wave); the counts are immediates
+  // tile is LPT loads per wave); the counts are immediates
   auto wait_tiles = [&](int later) {
     static_assert(NSTAGE <= 5, "wait_tiles covers up to three later tiles");
     if (later >= 3)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * WAVE_CH) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPT) : "memory");
     else if (later == 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * WAVE_CH) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory");
     else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WAVE_CH) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
@@ -271,9 +356,21 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         }
       } else if (key < t_end) {
         const size_t pg = (size_t)page_of(key) * A.Hkv + kv_head;
-        kx = *reinterpret_cast<const uint4 *>(A.Kc + (pg * DDT_PAGE + (key & 15)) * D + 8 * cc);
+        if constexpr (Q8) {  // fp16(q * scale), the product rounded once
+          const float ks = (float)A.Ksc[pg * DDT_PAGE + (key & 15)], vs = (float)A.Vsc[pg * DDT_PAGE + (key & 15)];
+          const int8_t *kq = A.Kq + (pg * DDT_PAGE + (key & 15)) * D + 8 * cc;
+          half8 kh;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) vx[x] = A.Vc[(pg * D + 8 * cc + x) * DDT_PAGE + (key & 15)];
+          for (int x = 0; x < 8; ++x) kh[x] = (_Float16)((float)kq[x] * ks);
+          kx = __builtin_bit_cast(uint4, kh);
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            vx[x] = (_Float16)((float)A.Vq[(pg * D + 8 * cc + x) * DDT_PAGE + (key & 15)] * vs);
+        } else {
+          kx = *reinterpret_cast<const uint4 *>(A.Kc + (pg * DDT_PAGE + (key & 15)) * D + 8 * cc);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) vx[x] = A.Vc[(pg * D + 8 * cc + x) * DDT_PAGE + (key & 15)];
+        }
       }
       const int r = krow_of(tau);
       *reinterpret_cast<uint4 *>(Ks + r * D + 8 * (cc ^ ksw(r))) = kx;
@@ -466,52 +563,90 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     // NSTAGE - 1 tiles in flight; the scores of tile it+1 are formed while the
     // probabilities and value product of tile it are worked on.
     if (n_full > 0) {
-#pragma unroll
-      for (int t = 0; t < NSTAGE - 1; ++t)
-        if (t < n_full) issue_tile(t, t, tile_page(t, 0), tile_page(t, 1));
-      // wait for tile 0: the loads of the later tiles may stay outstanding
-      wait_tiles(min(n_full, NSTAGE - 1) - 1);
-      __syncthreads();
-      f32x4 Sn[2][NB];
-      qk(0, Sn);
-      // the first full tile fixes every row's reference max (pass 0 only)
-      if (__ballot(mrow[0] == -INFINITY)) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          float t = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) t = fmaxf(t, Sn[e >> 2][j][e & 3]);
-          t = fmaxf(t, __shfl_xor(t, 16));
-          mrow[j] = fmaxf(t, __shfl_xor(t, 32));
-        }
-      }
-      auto main_loop = [&](auto NBA_c) {
-        for (int it = 0; it < n_full; ++it) {
-          const int nt = it + NSTAGE - 1;  // tile issued in this iteration
-          const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
-          // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
-          if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
-          __syncthreads();  // tile it+1 landed; every wave is past tile it-1
-          // scores of tile it+1 (past the last tile they read a stale stage
-          // and are dropped), probabilities and value product of tile it; the
-          // loads of tile it+3 go out while the first K fragments arrive
-          f32x4 Sc[2][NB];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
-          tile_step(NBA_c, lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
-                    lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
-                      if (nt < n_full) issue_tile(nt, nt % NSTAGE, npg0, npg1);
-                    });
-        }
-      };
       // row blocks are dealt round-robin, so a wave's active blocks are a
       // prefix of its NB and number NB or NB - 1
-      if (blk_on[NB - 1])
-        main_loop(std::integral_constant<int, NB>{});
-      else
-        main_loop(std::integral_constant<int, NB - 1>{});
+      f32x4 Sn[2][NB];
+      auto fix_refs = [&]() {  // the first full tile fixes every row's reference max (pass 0 only)
+        if (__ballot(mrow[0] == -INFINITY)) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            float t = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t = fmaxf(t, Sn[e >> 2][j][e & 3]);
+            t = fmaxf(t, __shfl_xor(t, 16));
+            mrow[j] = fmaxf(t, __shfl_xor(t, 32));
+          }
+        }
+      };
+      auto copy_S = [&](f32x4 (&Sc)[2][NB]) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
+      };
+      if constexpr (!Q8) {
+#pragma unroll
+        for (int t = 0; t < NSTAGE - 1; ++t)
+          if (t < n_full) issue_tile(t, t, tile_page(t, 0), tile_page(t, 1));
+        // wait for tile 0: the loads of the later tiles may stay outstanding
+        wait_tiles(min(n_full, NSTAGE - 1) - 1);
+        __syncthreads();
+        qk(0, Sn);
+        fix_refs();
+        auto main_loop = [&](auto NBA_c) {
+          for (int it = 0; it < n_full; ++it) {
+            const int nt = it + NSTAGE - 1;  // tile issued in this iteration
+            const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
+            // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
+            if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
+            __syncthreads();  // tile it+1 landed; every wave is past tile it-1
+            // scores of tile it+1 (past the last tile they read a stale stage
+            // and are dropped), probabilities and value product of tile it; the
+            // loads of tile it+3 go out while the first K fragments arrive
+            f32x4 Sc[2][NB];
+            copy_S(Sc);
+            tile_step(NBA_c, lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
+                      lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
+                        if (nt < n_full) issue_tile(nt, nt % NSTAGE, npg0, npg1);
+                      });
+          }
+        };
+        if (blk_on[NB - 1])
+          main_loop(std::integral_constant<int, NB>{});
+        else
+          main_loop(std::integral_constant<int, NB - 1>{});
+      } else {
+        constexpr int QS = LdsQ8<D>::Q_STAGES, FS = LdsQ8<D>::FP_STAGES;
+#pragma unroll
+        for (int t = 0; t < QS - 1; ++t)
+          if (t < n_full) issue_q8(t, tile_page(t, 0), tile_page(t, 1));
+        wait_tiles(min(n_full, QS - 1) - 1);
+        __syncthreads();
+        convert_q8(0, 0);
+        __syncthreads();
+        qk(0, Sn);
+        fix_refs();
+        auto main_loop = [&](auto NBA_c) {
+          for (int it = 0; it < n_full; ++it) {
+            const int nt = it + QS - 1;  // 8-bit tile issued in this iteration
+            const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
+            if (it + 1 < n_full) wait_tiles(min(n_full, it + QS - 1) - (it + 2));
+            __syncthreads();  // tile it+1 landed; every wave is past tile it-1
+            if (it + 1 < n_full) convert_q8((it + 1) % QS, (it + 1) % FS);  // into tile it-1's fp16 stage
+            __syncthreads();
+            f32x4 Sc[2][NB];
+            copy_S(Sc);
+            tile_step(NBA_c, lds + ((it + 1) % FS) * Lds<D>::STAGE,
+                      lds + (it % FS) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
+                        if (nt < n_full) issue_q8(nt % QS, npg0, npg1);
+                      });
+          }
+        };
+        if (blk_on[NB - 1])
+          main_loop(std::integral_constant<int, NB>{});
+        else
+          main_loop(std::integral_constant<int, NB - 1>{});
+      }
     }
     // ---- epilogue: ragged cache tile, then the tree tiles
     const int n_ep = (has_part ? 1 : 0) + n_tree;
@@ -771,6 +906,64 @@ static Cfg attn_cfg(const ddt_plan *P, int Hq, int Hkv, int D, int T_max, int n_
   return c;
 }
 
+static AttnArgs attn_args(const ddt_plan *P, const void *q, const int32_t *page_table, int32_t max_pages,
+                          const int32_t *T, int32_t T_max, const void *Kt, const void *Vt, int32_t Hq,
+                          int32_t Hkv, int32_t D, float scale, const Cfg &c, float *out, void *ws) {
+  AttnArgs A{};
+  A.P = *P;
+  A.q = (const _Float16 *)q;
+  A.Kt = (const _Float16 *)Kt;
+  A.Vt = (const _Float16 *)Vt;
+  A.pt = page_table;
+  A.max_pages = max_pages;
+  A.T = T;
+  A.T_max = T_max;
+  A.Hq = Hq;
+  A.Hkv = Hkv;
+  A.G = Hq / Hkv;
+  A.c = scale * LOG2E;
+  A.n_splits = c.n_splits;
+  A.n_rg = c.n_rg;
+  A.rows_wg = c.rows_wg;
+  const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
+  A.Opart = (float *)ws;
+  A.ML = (float2 *)((char *)ws + rows * D * sizeof(float));
+  A.out = out;
+  return A;
+}
+
+// The matrix-core path: the split kernel, then the combine.
+template <bool Q8>
+static int launch_attn_mfma(const ddt_plan &P, const AttnArgs &A, const Cfg &c, int D, hipStream_t st) {
+  dim3 grid(c.n_splits, A.Hkv, P.B * c.n_rg);
+  const size_t lds = Q8 ? (size_t)(D == 256 ? LdsQ8<256>::TOTAL : LdsQ8<128>::TOTAL)
+                        : (size_t)NSTAGE * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
+#define DDT_ATTN(DD, NBB)                                                                       \
+  do {                                                                                          \
+    hipError_t e_ = hipFuncSetAttribute((const void *)attn_mfma_kernel<DD, NBB, Q8>,            \
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+    if (e_ != hipSuccess) {                                                                     \
+      set_hip_error(e_);                                                                        \
+      return DDT_E_HIP;                                                                         \
+    }                                                                                           \
+    hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB, Q8>), grid, dim3(256), lds, st, A);           \
+  } while (0)
+  if (D == 256) {
+    if (c.nb == 1) DDT_ATTN(256, 1); else if (c.nb == 2) DDT_ATTN(256, 2); else DDT_ATTN(256, 3);
+  } else {
+    if (c.nb == 1) DDT_ATTN(128, 1); else if (c.nb == 2) DDT_ATTN(128, 2); else DDT_ATTN(128, 3);
+  }
+#undef DDT_ATTN
+  const int r = launch_status();
+  if (r) return r;
+  dim3 cgrid(c.rows_wg, A.Hkv, P.B * c.n_rg);
+  if (D == 256)
+    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, dim3(256), 0, st, A);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, A);
+  return launch_status();
+}
+
 }  // namespace ddt
 
 using namespace ddt;
@@ -816,52 +1009,31 @@ extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, c
     return launch_status();
   }
   if (!ws || ws_bytes < ddt_tree_attn_workspace(P, Hq, Hkv, D, T_max, n_splits)) return DDT_E_WS;
-  AttnArgs A{};
-  A.P = *P;
-  A.q = (const _Float16 *)q;
+  AttnArgs A = attn_args(P, q, page_table, max_pages, T, T_max, Kt, Vt, Hq, Hkv, D, scale, c, out, ws);
   A.Kc = (const _Float16 *)Kc;
   A.Vc = (const _Float16 *)Vc;
-  A.Kt = (const _Float16 *)Kt;
-  A.Vt = (const _Float16 *)Vt;
-  A.pt = page_table;
-  A.max_pages = max_pages;
-  A.T = T;
-  A.T_max = T_max;
-  A.Hq = Hq;
-  A.Hkv = Hkv;
-  A.G = Hq / Hkv;
-  A.c = scale * LOG2E;
-  A.n_splits = c.n_splits;
-  A.n_rg = c.n_rg;
-  A.rows_wg = c.rows_wg;
-  const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
-  A.Opart = (float *)ws;
-  A.ML = (float2 *)((char *)ws + rows * D * sizeof(float));
-  A.out = out;
-  dim3 grid(c.n_splits, Hkv, P->B * c.n_rg);
-  const size_t lds = (size_t)NSTAGE * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
-#define DDT_ATTN(DD, NBB)                                                                       \
-  do {                                                                                          \
-    hipError_t e_ = hipFuncSetAttribute((const void *)attn_mfma_kernel<DD, NBB>,                \
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
-    if (e_ != hipSuccess) {                                                                     \
-      set_hip_error(e_);                                                                        \
-      return DDT_E_HIP;                                                                         \
-    }                                                                                           \
-    hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB>), grid, dim3(256), lds, st, A);               \
-  } while (0)
-  if (D == 256) {
-    if (c.nb == 1) DDT_ATTN(256, 1); else if (c.nb == 2) DDT_ATTN(256, 2); else DDT_ATTN(256, 3);
-  } else {
-    if (c.nb == 1) DDT_ATTN(128, 1); else if (c.nb == 2) DDT_ATTN(128, 2); else DDT_ATTN(128, 3);
-  }
-#undef DDT_ATTN
-  r = launch_status();
+  return launch_attn_mfma<false>(*P, A, c, D, st);
+}
+
+extern "C" int ddt_tree_attn_q8(const ddt_plan *P, const void *q, const int8_t *Kq, const void *Ksc,
+                                const int8_t *Vq, const void *Vsc, const int32_t *page_table,
+                                int32_t max_pages, const int32_t *T, int32_t T_max, const void *Kt,
+                                const void *Vt, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                int32_t n_splits, float *out, void *ws, size_t ws_bytes, void *stream) {
+  int r = check_plan(P);
   if (r) return r;
-  dim3 cgrid(c.rows_wg, Hkv, P->B * c.n_rg);
-  if (D == 256)
-    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, dim3(256), 0, st, A);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, A);
-  return launch_status();
+  if (!q || !Kq || !Ksc || !Vq || !Vsc || !T || !Kt || !Vt || !out) return DDT_E_ARG;
+  if (!page_table && P->B != 1) return DDT_E_ARG;
+  if (page_table && max_pages < 1) return DDT_E_SHAPE;
+  if (Hkv < 1 || Hq < Hkv || Hq % Hkv) return DDT_E_SHAPE;
+  if (D != 128 && D != 256) return DDT_E_SHAPE;
+  if (T_max < 0 || n_splits < 0) return DDT_E_RANGE;
+  const Cfg c = attn_cfg(P, Hq, Hkv, D, T_max, n_splits, DDT_F16);
+  if (!ws || ws_bytes < ddt_tree_attn_workspace(P, Hq, Hkv, D, T_max, n_splits)) return DDT_E_WS;
+  AttnArgs A = attn_args(P, q, page_table, max_pages, T, T_max, Kt, Vt, Hq, Hkv, D, scale, c, out, ws);
+  A.Kq = Kq;
+  A.Vq = Vq;
+  A.Ksc = (const _Float16 *)Ksc;
+  A.Vsc = (const _Float16 *)Vsc;
+  return launch_attn_mfma<true>(*P, A, c, D, (hipStream_t)stream);
 }
