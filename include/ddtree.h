@@ -123,7 +123,7 @@ const char *ddt_status_str(int code);
 int ddt_plan_slots(int32_t n_max);
 
 /*
- * a1. Tree plan on the host: same outputs as ddt_tree_plan, all pointers in
+ * Tree plan on the host: same outputs as ddt_tree_plan, all pointers in
  * `plan` are host pointers.  Returns DDT_E_TREE on a malformed tree (any
  * parent[0] != -1, parent[i] outside [0, i), tree size outside
  * [1, DDT_MAX_NODES] or above n_max) and DDT_E_RANGE when a tree has more
@@ -133,7 +133,7 @@ int ddt_plan_slots(int32_t n_max);
 int ddt_tree_plan_host(const ddt_plan *plan, int32_t max_levels);
 
 /*
- * a1. Tree plan on the device (one wavefront per sequence).  Reads
+ * Tree plan on the device (one wavefront per sequence).  Reads
  * plan->tree_off and plan->parent, writes depth, anc, win, order, slot and
  * resets status[b] to the sequence's DDT_ST_TREE / DDT_ST_LEVELS bits.  A
  * malformed tree is flagged and replaced by a safe plan (invalid parents
@@ -143,7 +143,7 @@ int ddt_tree_plan_host(const ddt_plan *plan, int32_t max_levels);
 int ddt_tree_plan(const ddt_plan *plan, int32_t max_levels, void *stream);
 
 /*
- * a2. Tree-aware causal depthwise conv1d ([P1] "Implemented here",
+ * Tree-aware causal depthwise conv1d ([P1] "Implemented here",
  * ssm_conv_tree).  For every node i and channel c:
  *   y[i][c] = act( sum_{t=0}^{W-1} w[c][W-1-t] * tok_t(i)[c] )
  * where tok_0 = x[i] and tok_j (j >= 1) is window entry j-1 of the plan
@@ -158,7 +158,7 @@ int ddt_tree_conv(const ddt_plan *plan, const void *x, const void *prefix, const
                   int32_t C, int32_t act, int32_t dtype, float *y, void *stream);
 
 /*
- * a3. Tree gated delta-net ([P1] "Implemented here", gated_delta_net_tree
+ * Tree gated delta-net ([P1] "Implemented here", gated_delta_net_tree
  * and its _persist variant).  For value head h (key head g = h / (Hv/Hk)),
  * every node n starts from its parent's state (the root from S_c[b][h]):
  *   S_n = alpha_n S_p (I - beta_n k_n k_n^T) + beta_n v_n k_n^T
@@ -189,7 +189,7 @@ int ddt_tree_gdn(const ddt_plan *plan, const void *q, const void *k, const void 
                  float *node_states, float *node_u, void *stream);
 
 /*
- * a4. Tree-masked attention over the committed KV cache.  Node i, query
+ * Tree-masked attention over the committed KV cache.  Node i, query
  * head h (KV head g = h / (Hq/Hkv)) attends to all T[b] committed tokens of
  * its sequence plus the draft tokens on its own root path, itself included
  * (plan->anc); full attention, no window ([P2] --fa-window 0):
@@ -223,7 +223,7 @@ int ddt_tree_attn(const ddt_plan *plan, const void *q, const void *Kc, const voi
                   void *stream);
 
 /*
- * Variant of a4: tree-masked attention over an 8-bit KV cache ([P1] keeps its
+ * Variant of ddt_tree_attn: tree-masked attention over an 8-bit KV cache ([P1] keeps its
  * cache quantized to fit long contexts).  Same operation, layouts of pages
  * and arguments as ddt_tree_attn, with the cache stored as
  *   Kq  device [P][Hkv][DDT_PAGE][D] int8     Vq  device [P][Hkv][D][DDT_PAGE] int8
@@ -242,7 +242,7 @@ int ddt_tree_attn_q8(const ddt_plan *plan, const void *q, const int8_t *Kq, cons
                      size_t ws_bytes, void *stream);
 
 /*
- * a5. Verify argmax and greedy acceptance walk ([P2] "Making requests":
+ * Verify argmax and greedy acceptance walk ([P2] "Making requests":
  * greedy decoding; "GPU draft top-K & verify-argmax": the argmax is read in
  * place from the device logits and validated).
  *   argmax[i] = smallest v maximising logits[i][v] (NaN never wins)
@@ -296,7 +296,7 @@ int ddt_accept_sample(const ddt_plan *plan, const void *logits, int32_t dtype, i
                       size_t ws_bytes, void *stream);
 
 /*
- * a6. Commit of the accepted path ([P1] "Implemented here": tree-aware SSM
+ * Commit of the accepted path ([P1] "Implemented here": tree-aware SSM
  * state rollback; "Why GGUF": the DDTree verify state).  In one launch, for
  * every sequence b with accepted local path p_0 = 0, ..., p_{L-1}:
  *  - each gated delta-net layer: S_c[b] <- state of node p_{L-1}.

@@ -1,4 +1,4 @@
-// a4: tree-masked attention over a paged fp16 KV cache.
+// Tree-masked attention over a paged fp16 or 8-bit KV cache.
 //
 // Each tree node attends to all committed tokens of its sequence and to the
 // draft tokens on its own root path (the whole tree is verified in one pass:

@@ -1,4 +1,4 @@
-// a6: commit of the accepted path.
+// Commit of the accepted path.
 //
 // After the walk the accepted node's linear-attention state becomes the
 // committed state -- the pages' "tree-aware SSM state rollback"

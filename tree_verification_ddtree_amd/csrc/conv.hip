@@ -1,4 +1,4 @@
-// a2: tree-aware causal depthwise conv1d.
+// Tree-aware causal depthwise conv1d.
 //
 // The pages name a tree-mode conv among the kernels for tree-aware SSM
 // state rollback (lucebox-hub README, "02 · DFlash DDtree", "Implemented

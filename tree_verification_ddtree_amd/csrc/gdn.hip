@@ -1,4 +1,4 @@
-// a3: tree gated delta-net with optional state persistence.
+// Tree gated delta-net with optional state persistence.
 //
 // The pages name tree-aware gated delta-net kernels, one of which persists
 // per-node state so the accepted node's state can be restored (lucebox-hub

@@ -1,4 +1,4 @@
-// a1: tree plan (host and device) and library-wide bits.
+// Tree plan (host and device) and library-wide bits.
 //
 // The plan turns a parent-pointer draft tree (lucebox-hub README,
 // "02 · DFlash DDtree", "Algorithms used": DDTree verifies a tree of draft

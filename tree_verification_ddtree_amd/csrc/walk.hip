@@ -1,4 +1,4 @@
-// a5: verify argmax and greedy acceptance walk.
+// Verify argmax and greedy acceptance walk.
 //
 // The verify argmax is read in place from the device logits and its result
 // is validated (codehub lucebox-hub@main, "GPU draft top-K & verify-argmax
