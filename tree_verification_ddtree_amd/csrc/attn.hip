@@ -48,6 +48,11 @@
 
 namespace ddt {
 
+// Cache policy of the loads of cache pages: non-temporal (the nt bit).  Each
+// K/V byte is read once per call; with the hint the 128K, 22-node call measured
+// 115.0 us against 121.8 us with the default policy.
+constexpr int KV_STREAM_CPOL = 2;
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       const int tau = key_of_krow(r);
       const int pg = tau < 16 ? pg0 : pg1;
       const _Float16 *src = A.Kc + (((size_t)pg * A.Hkv + kv_head) * DDT_PAGE + (tau & 15)) * D + 8 * cc;
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Ks + piece * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Ks + piece * 512), 16, 0, KV_STREAM_CPOL);
     }
 #pragma unroll
     for (int k = 0; k < WAVE_CH; ++k) {
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       const int qg = slot ^ vsw(d);
       const int pg = (qg >> 1) ? pg1 : pg0;
       const _Float16 *src = A.Vc + (((size_t)pg * A.Hkv + kv_head) * D + d) * DDT_PAGE + 8 * (qg & 1);
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Vs + piece * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Vs + piece * 512), 16, 0, KV_STREAM_CPOL);
     }
   };
 
@@ -274,14 +279,14 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     for (int k = 0; k < D / 128; ++k) {
       const int piece = w + 4 * k, half = piece / PPP, off = (piece % PPP) * 1024 + 16 * lane;
       const size_t pb = ((size_t)(half ? pg1 : pg0) * A.Hkv + kv_head) * 16 * D;
-      __builtin_amdgcn_global_load_lds((const void *)(A.Kq + pb + off), (lds_void *)(St + piece * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(A.Kq + pb + off), (lds_void *)(St + piece * 1024), 16, 0, KV_STREAM_CPOL);
     }
 #pragma unroll
     for (int k = 0; k < D / 128; ++k) {
       const int piece = w + 4 * k, half = piece / PPP, off = (piece % PPP) * 1024 + 16 * lane;
       const size_t pb = ((size_t)(half ? pg1 : pg0) * A.Hkv + kv_head) * 16 * D;
       __builtin_amdgcn_global_load_lds((const void *)(A.Vq + pb + off),
-                                       (lds_void *)(St + LdsQ8<D>::K_BYTES + piece * 1024), 16, 0, 0);
+                                       (lds_void *)(St + LdsQ8<D>::K_BYTES + piece * 1024), 16, 0, KV_STREAM_CPOL);
     }
     const _Float16 *sc = (w < 2 ? A.Ksc : A.Vsc) + ((size_t)((w & 1) ? pg1 : pg0) * A.Hkv + kv_head) * 16;
     if (lane < 8)
