@@ -133,6 +133,14 @@ def test_device_entry_points_validate_before_launch():
     assert L.ddt_tree_attn(ctypes.byref(P2), one, one, one, None, 0, one, 100, one, one, 24, 4, 256,
                            0.1, 1, 0, one, one, 1 << 30, None) == -1
     assert ddt.ddt_tree_attn_workspace(P, 24, 4, 256, 131072) > 0
+    # 8-bit cache attention: head size outside {128, 256}, null scales, small workspace
+    q8 = L.ddt_tree_attn_q8
+    assert q8(bp, one, one, one, one, one, None, 0, one, 100, one, one, 24, 4, 64, 0.1, 0, one, one,
+              1 << 30, None) == -3
+    assert q8(bp, one, one, None, one, one, None, 0, one, 100, one, one, 24, 4, 256, 0.1, 0, one, one,
+              1 << 30, None) == -1
+    assert q8(bp, one, one, one, one, one, None, 0, one, 100, one, one, 24, 4, 256, 0.1, 0, one, one,
+              16, None) == -6
     # walk: workspace, dtype
     assert L.ddt_accept_walk(bp, one, 2, 1000, one, one, one, one, one, one, 0, None) == -6
     assert L.ddt_accept_walk(bp, one, 1, 1000, one, one, one, one, one, one, 1 << 20, None) == -4
@@ -181,3 +189,19 @@ def test_device_entry_points_validate_before_launch():
     assert sa(bp, one, 2, 151936, one, None, 1.0, 20, 0.95, one, one, one, one, one, sw, None) == -1
     for c in (-1, -2, -3, -4, -5, -6, -7, 0):
         assert ddt.status_str(c)
+
+
+def test_q8_binding_rejects_wrong_dtypes():
+    import torch
+    P = _dummy_plan()
+    h = lambda *s, dt=torch.float16: torch.zeros(s, dtype=dt)
+    q, Kt, Vt, out = h(1, 24, 128), h(1, 4, 128), h(1, 4, 128), h(1, 24, 128, dt=torch.float32)
+    Kq, Vq = h(1, 4, 16, 128, dt=torch.int8), h(1, 4, 128, 16, dt=torch.int8)
+    Ks, Vs = h(1, 4, 16), h(1, 4, 16)
+    T = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        ddt.ddt_tree_attn_q8(P, q, Kq.half(), Ks, Vq, Vs, None, T, 16, Kt, Vt, out, None)
+    with pytest.raises(TypeError):
+        ddt.ddt_tree_attn_q8(P, q, Kq, Ks.float(), Vq, Vs, None, T, 16, Kt, Vt, out, None)
+    with pytest.raises(TypeError):
+        ddt.ddt_tree_attn_q8(P, q, Kq, Ks, Vq, Vs, None, T, 16, Kt, Vt, out.half(), None)

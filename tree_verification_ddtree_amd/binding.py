@@ -246,6 +246,11 @@ def ddt_tree_attn(plan, q, Kc, Vc, page_table, T, T_max, Kt, Vt, out, ws, scale=
 def ddt_tree_attn_q8(plan, q, Kq, Ksc, Vq, Vsc, page_table, T, T_max, Kt, Vt, out, ws, scale=None,
                      n_splits=0, stream=None):
     """8-bit cache: Kq [P][Hkv][16][D], Vq [P][Hkv][D][16] int8; Ksc, Vsc [P][Hkv][16] fp16."""
+    import torch
+    if Kq.dtype != torch.int8 or Vq.dtype != torch.int8:
+        raise TypeError("ddt_tree_attn_q8: Kq and Vq must be int8")
+    if any(t.dtype != torch.float16 for t in (q, Ksc, Vsc, Kt, Vt)) or out.dtype != torch.float32:
+        raise TypeError("ddt_tree_attn_q8: q, Ksc, Vsc, Kt, Vt must be float16 and out float32")
     Hq, D = int(q.shape[1]), int(q.shape[2])
     Hkv = int(Kt.shape[1])
     max_pages = int(page_table.shape[1]) if page_table is not None else 0
