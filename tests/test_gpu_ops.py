@@ -313,6 +313,34 @@ def test_attn_q8(gpu, case):
     assert attn_q8_case(gpu, trees, T, Hq, Hkv, D, 16, paged=paged, n_splits=ns) < TOL
 
 
+def test_attn_q8_full_context_128k_sampled(gpu):
+    """The 8-bit call at the size and launch configuration the benchmark
+    times (T = 131,072, one 22-node tree, 24 q / 4 KV heads, D = 256,
+    contiguous cache, default split count); sampled rows against the oracle."""
+    n, Hq, Hkv, D, T = 22, 24, 4, 256, 131072
+    banner(f"attn q8 full size: T {T} N {n} Hq {Hq} Hkv {Hkv} D {D}, sampled rows")
+    tree = synth.random_tree(synth.rng_for(16, 73, 0), n, 10)
+    tb, par, off = make_batch([tree], 4, gpu)
+    Ta = np.array([T])
+    _, P = synth.page_layout(17, (74,), Ta, [n], shuffle=False)
+    c = synth.kv_pool_q8(17, (74,), P, Hkv, D)
+    a = synth.attn_inputs(17, (75,), n, Hq, Hkv, D, "f16")
+    ws = torch.full((ddt.ddt_tree_attn_workspace(tb, Hq, Hkv, D, T),), 255, dtype=torch.uint8, device=gpu)
+    out = torch.full((n, Hq, D), np.nan, dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_attn_q8(tb, dev(a["q"]), dev(c["Kq"]), dev(c["Ksc"]), dev(c["Vq"]), dev(c["Vsc"]), None,
+                         dev(Ta.astype(np.int32)), T, dev(a["Kt"]), dev(a["Vt"]), out, ws)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isfinite(got).all()
+    K, V = oracle.dequant_q8(c["Kq"], c["Ksc"], c["Vq"], c["Vsc"])
+    rng = np.random.default_rng(3)
+    rows = [(int(i), int(h)) for i, h in zip(rng.integers(0, n, 6), rng.integers(0, Hq, 6))]
+    rows += [(0, 0), (n - 1, Hq - 1)]
+    ref = oracle.tree_attn(par, a["q"], K, V, [T], a["Kt"], a["Vt"], rows=rows)
+    idx = tuple(np.array(rows).T)
+    assert rel_err(got[idx], ref[idx], (0,)) < TOL
+
+
 def _plant_cache(t):
     """Key at cache position t of sequence 0, KV head 0 := 4 q of node 0,
     q head 0: that row's score there is ~4|q|^2, about 90 binades (at scale
