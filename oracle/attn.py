@@ -39,7 +39,10 @@ def dequant_q8(Kq, Ksc, Vq, Vsc):
     scale, the exact product rounded once to fp16 (the int8 code and the fp16
     scale multiply exactly in fp32, 8 + 11 significant bits).  Kq [P][Hkv][16][D],
     Vq [P][Hkv][D][16] int8; Ksc, Vsc [P][Hkv][16] fp16 (one per token).  Returns
-    the (K, V) pages in ``tree_attn``'s fp16 layouts."""
+    the (K, V) pages in ``tree_attn``'s fp16 layouts.  The pages keep the cache
+    quantised to fit long contexts (lucebox-hub README, "Implemented here":
+    the TQ3_0 and Q4_0 KV caches); the 8-bit layout and the rounding are a
+    reading, stated here."""
     K = (np.asarray(Kq, np.float32) * np.asarray(Ksc, np.float32)[..., :, None]).astype(np.float16)
     V = (np.asarray(Vq, np.float32) * np.asarray(Vsc, np.float32)[..., None, :]).astype(np.float16)
     return K, V
