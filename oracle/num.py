@@ -1,4 +1,8 @@
-"""Oracle-side decoding of stored inputs to fp64 (test infrastructure)."""
+"""Oracle-side decoding of stored inputs to fp64 (test infrastructure).
+
+Pinned by tests/test_oracle_num.py: all 65,536 bf16 patterns against
+torch's bfloat16 type, and hand-worked values of the format.
+"""
 import numpy as np
 
 
