@@ -73,6 +73,7 @@ class Stack:
         # room for the accepted tokens of every step the benchmark runs
         self.T_max = T + headroom_steps * N
         npages = (self.T_max + N + 15) // 16
+        self.npages = npages
         g = torch.Generator(device=device)
         n_gdn, n_attn = c["n_gdn"], c["n_attn"]
         self.gdn, self.conv, self.gdn_out, self.conv_out, self.gdn_u = [], [], [], [], []
@@ -184,7 +185,8 @@ class Stack:
         self._timed("commit", lambda: ddt.ddt_commit_state(
             self.tb, self.path, self.L, ddt.DDT_COMMIT_UPDATE, self.fused_table if fused else self.gdn_table,
             c["n_gdn"], c["Hk"], c["Hv"], c["dk"], c["dv"], ddt.DDT_F32 if fused else ddt.DDT_BF16, c["C"],
-            ddt.DDT_BF16, self.attn_table, c["n_attn"], c["Hkv"], c["D"], ddt.DDT_F16, None, self.T, stream))
+            ddt.DDT_BF16, self.attn_table, c["n_attn"], c["Hkv"], c["D"], ddt.DDT_F16, None, self.T, stream,
+            cache_pages=self.npages))
 
     def op_batches(self):
         """Idempotent calls of the short ops for batch timing: every layer's
@@ -755,6 +757,7 @@ def main():
         },
         "kernels": kernels,
         "cpu_baseline": None,
+        "library_source_sha256": ddt.ddt_source_hash(),
     }
     if not args.no_next:
         # widening ahead of the step (reported beside it, not part of `value`)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DDT_VERSION 1
+#define DDT_VERSION 2
 
 /* return codes */
 #define DDT_OK 0
@@ -107,20 +107,20 @@ typedef struct ddt_plan {
   int32_t *win;    /* out [n_total][max(W-1,1)]: entry j-1 = j-th previous
                       token on prefix ++ root path: local node id >= 0, or
                       -(s+1) for committed prefix slot s (0 = oldest)     */
-  int32_t *order;  /* out [n_total] per tree: local ids in the order the
-                      linear-attention kernels visit them (a depth-first
-                      preorder that visits each node's largest subtree
-                      last; parents precede children)                     */
-  int32_t *slot;   /* out [n_total] state slot of each node for that visit
-                      order; slots <= floor(log2(n_max))                  */
   int32_t *status; /* out [B] device status word, DDT_ST_* bits          */
 } ddt_plan;
 
 int ddt_version(void);
 const char *ddt_status_str(int code);
 
-/* Number of state slots the visit order needs for trees of n_max nodes. */
-int ddt_plan_slots(int32_t n_max);
+/*
+ * sha256 (64 lowercase hex digits) of the sources this library was built
+ * from: include/ddtree.h and every file of the package's csrc/ directory,
+ * taken in name order as "<relative path>\0<bytes>" records.  A caller can
+ * hash its checked-out sources the same way to confirm which build it runs.
+ * The string is static; the caller must not free it.
+ */
+const char *ddt_source_hash(void);
 
 /*
  * Tree plan on the host: same outputs as ddt_tree_plan, all pointers in
@@ -134,8 +134,8 @@ int ddt_tree_plan_host(const ddt_plan *plan, int32_t max_levels);
 
 /*
  * Tree plan on the device (one wavefront per sequence).  Reads
- * plan->tree_off and plan->parent, writes depth, anc, win, order, slot and
- * resets status[b] to the sequence's DDT_ST_TREE / DDT_ST_LEVELS bits.  A
+ * plan->tree_off and plan->parent, writes depth, anc, win and resets
+ * status[b] to the sequence's DDT_ST_TREE / DDT_ST_LEVELS bits.  A
  * malformed tree is flagged and replaced by a safe plan (invalid parents
  * read as the root) so later kernels stay in bounds.  Must run before the
  * other calls of a step.
@@ -312,6 +312,15 @@ int ddt_accept_sample(const ddt_plan *plan, const void *logits, int32_t dtype, i
  *  - each attention layer: the path's Kt/Vt are written to cache positions
  *    T[b] .. T[b]+L-1 (the page table must already map them), and finally
  *    T[b] += L.
+ * Cache capacity (when n_attn > 0): page_table is [B][max_pages]; for a
+ * contiguous cache (page_table NULL, B == 1) max_pages is the number of
+ * DDT_PAGE-token pages each layer's Kc / Vc holds.  Either way max_pages >= 1
+ * (else DDT_E_SHAPE) and sequence b fits when 0 <= T[b] and
+ * T[b] + L[b] <= DDT_PAGE * max_pages.  A sequence that does not fit is not
+ * committed at all -- its delta-net states, conv prefixes, cache and T[b]
+ * are left as they were -- and DDT_ST_CTX is set in its status word, so its
+ * layers never move ahead of its cache.  With n_attn == 0 there is no cache
+ * and every sequence is committed.
  * The layer descriptor arrays live in DEVICE memory (the caller builds them
  * once); their shapes are given here.  Per-layer fields may be NULL where
  * noted.

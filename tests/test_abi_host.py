@@ -21,61 +21,48 @@ def test_library_exports_every_declared_symbol():
     L = ddt.lib()
     for n in sorted(names):
         assert hasattr(L, n), n
-    assert ddt.ddt_version() == 1
+    assert ddt.ddt_version() == 2
+
+
+def test_library_reports_the_sources_it_was_built_from():
+    from tree_verification_ddtree_amd import build
+    h = ddt.ddt_source_hash()
+    assert re.fullmatch(r"[0-9a-f]{64}", h), h
+    assert h == build.source_hash(), "libddtree.so was built from other sources: rebuild it"
 
 
 def host_plan(trees, W=4, max_levels=64, n_max=None):
     par, off = synth.concat_trees(trees)
     n = len(par)
     out = dict(depth=np.zeros(n, np.int32), anc=np.zeros(n, np.uint64),
-               win=np.zeros(n * max(W - 1, 1), np.int32), order=np.zeros(n, np.int32),
-               slot=np.zeros(n, np.int32), status=np.zeros(len(trees), np.int32))
+               win=np.zeros(n * max(W - 1, 1), np.int32), status=np.zeros(len(trees), np.int32))
     nm = n_max or max(len(t) for t in trees)
     st = ddt.plan_struct(len(trees), n, nm, W, off, par, out["depth"], out["anc"], out["win"],
-                         out["order"], out["slot"], out["status"])
+                         out["status"])
     rc = ddt.ddt_tree_plan_host(st, max_levels)
     return rc, par, off, out
 
 
-def check_schedule(par, order, slot, n):
-    """Replay the visit order with per-slot contents: every parent state must
-    still be in its slot when a child reads it; slots stay within the bound."""
-    assert sorted(order) == list(range(n))
-    pos = {v: i for i, v in enumerate(order)}
-    assert all(pos[int(par[i])] < pos[i] for i in range(1, n))      # parents first
-    # preorder: each subtree is a contiguous run starting at its root
-    for u in range(n):
-        sub = [v for v in range(n) if u in oracle.root_path(par, v)]
-        ps = sorted(pos[v] for v in sub)
-        assert ps == list(range(pos[u], pos[u] + len(sub)))
-    nslot = ddt.ddt_plan_slots(n)
-    held = {}
-    for v in order:
-        p = int(par[v])
-        if p >= 0:
-            assert held.get(int(slot[p])) == p, "parent state overwritten"
-        assert 0 <= slot[v] < nslot
-        held[int(slot[v])] = v
-
-
 @pytest.mark.parametrize("seed", range(6))
-def test_host_plan_matches_oracle_and_schedules(seed):
+def test_host_plan_matches_oracle(seed):
     sizes = [22, 64, 1, 7, 33, 2]
     trees = [synth.random_tree(synth.rng_for(seed, 20, b), s, 10 if s > 22 else 8)
              for b, s in enumerate(sizes)]
     trees.append(synth.chain(40))
     trees.append(synth.binary_tree(5))   # 31 nodes
-    rc, par, off, out = host_plan(trees, W=4)
-    assert rc == 0
-    W1 = 3
-    for b, t in enumerate(trees):
-        o, e = off[b], off[b + 1]
-        n = e - o
-        assert list(out["depth"][o:e]) == list(oracle.depth(t))
-        assert [int(x) for x in out["anc"][o:e]] == oracle.ancestor_mask(t)
-        np.testing.assert_array_equal(out["win"][o * W1:e * W1].reshape(n, W1), oracle.conv_window(t, 4))
-        check_schedule(t, list(out["order"][o:e]), out["slot"][o:e], n)
-        assert out["status"][b] == 0
+    for W in (4, 1, 8):
+        rc, par, off, out = host_plan(trees, W=W)
+        assert rc == 0
+        W1 = max(W - 1, 1)
+        for b, t in enumerate(trees):
+            o, e = off[b], off[b + 1]
+            n = e - o
+            assert list(out["depth"][o:e]) == list(oracle.depth(t))
+            assert [int(x) for x in out["anc"][o:e]] == oracle.ancestor_mask(t)
+            if W > 1:
+                np.testing.assert_array_equal(out["win"][o * W1:e * W1].reshape(n, W1),
+                                              oracle.conv_window(t, W))
+            assert out["status"][b] == 0
 
 
 def test_host_plan_all_small_trees():
@@ -86,14 +73,8 @@ def test_host_plan_all_small_trees():
             rc, par, off, out = host_plan([t], W=3)
             assert rc == 0
             assert [int(x) for x in out["anc"]] == oracle.ancestor_mask(t)
-            check_schedule(t, list(out["order"]), out["slot"], n)
-
-
-def test_slot_bound_is_tight_for_complete_binary_trees():
-    for lv in range(1, 7):
-        t = synth.binary_tree(lv)
-        rc, par, off, out = host_plan([t], W=2)
-        assert rc == 0 and int(out["slot"].max()) + 1 <= ddt.ddt_plan_slots(len(t))
+            assert list(out["depth"]) == list(oracle.depth(t))
+            np.testing.assert_array_equal(out["win"].reshape(n, 2), oracle.conv_window(t, 3))
 
 
 def test_host_plan_rejects_malformed_trees():
@@ -108,7 +89,7 @@ def test_host_plan_rejects_malformed_trees():
 
 def _dummy_plan(B=1, n=4, n_max=4, W=4):
     z = np.zeros(64, np.int64)
-    return ddt.plan_struct(B, n, n_max, W, z, z, z, z, z, z, z, z)
+    return ddt.plan_struct(B, n, n_max, W, z, z, z, z, z, z)
 
 
 def test_device_entry_points_validate_before_launch():
@@ -152,6 +133,14 @@ def test_device_entry_points_validate_before_launch():
                               256, 1, None, 0, None, None) == -1
     assert L.ddt_commit_state(bp, one, one, 0, one, 1, 16, 30, 128, 128, 2, 8192, 2, None, 0, 4,
                               256, 1, None, 0, None, None) == -3
+    # commit with attention layers: the cache's capacity must be given, for a
+    # contiguous cache (no page table) as for a paged one
+    assert L.ddt_commit_state(bp, one, one, 2, one, 1, 16, 32, 128, 128, 2, 8192, 2, one, 1, 4,
+                              256, 1, None, 0, one, None) == -3
+    assert L.ddt_commit_state(bp, one, one, 2, one, 1, 16, 32, 128, 128, 2, 8192, 2, one, 1, 4,
+                              256, 1, one, 0, one, None) == -3
+    assert L.ddt_commit_state(bp, one, one, 2, one, 1, 16, 32, 128, 128, 2, 8192, 2, one, 1, 4,
+                              256, 1, None, 4, None, None) == -1   # attention layers need T
     # draft top-K: K outside 1..8, dtype, workspace; tree build: L > 16, N > 64, null output
     ws = ddt.ddt_draft_topk_workspace(1, 16, 151936, 8)
     assert ws > 0 and ddt.ddt_draft_topk_workspace(1, 16, 151936, 9) == 0

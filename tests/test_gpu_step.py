@@ -232,3 +232,99 @@ def test_commit_deep_path_and_conv_widths(gpu, W, cdt):
             p = uc["prefix"]
             got = host(p)[b] if cdt == "f32" else host(p.view(torch.int16)).view(np.uint16)[b]
             assert np.array_equal(oracle.num.f64(got), pre)
+
+
+def _commit_case(gpu, trees, paths, T, page_table, n_pages, cache_pages=None, seed=12):
+    """One UPDATE commit of explicit paths over one delta-net + conv layer and
+    one attention layer; returns the host inputs and the device buffers."""
+    par, off = synth.concat_trees(trees)
+    n, B = len(par), len(trees)
+    tb = ddt.TreeBatch(par, off, W, gpu)
+    ddt.ddt_tree_plan(tb, 64)
+    ph = np.full((B, tb.n_max), -1, np.int32)
+    for b, p in enumerate(paths):
+        ph[b, :len(p)] = p
+    Lh = np.array([len(p) for p in paths], np.int32)
+    g = synth.gdn_inputs(seed, (90,), n, Hk, Hv, dk, dk, "bf16", B=B)
+    c = synth.conv_inputs(seed, (91,), n, C, W, "bf16", B=B)
+    K, Vv = synth.kv_pool(seed, (92,), n_pages, Hkv, D, "f16")
+    a = synth.attn_inputs(seed, (93,), n, Hq, Hkv, D, "f16")
+    dg, dc = {k: dev(v) for k, v in g.items()}, {k: dev(v) for k, v in c.items()}
+    dK, dV, da = dev(K), dev(Vv), {k: dev(v) for k, v in a.items()}
+    o = torch.empty(n, Hv, dk, dtype=torch.float32, device=gpu)
+    nu = torch.empty(n, Hv, dk, dtype=torch.float32, device=gpu)
+    ddt.ddt_tree_gdn(tb, dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"], dg["S_c"], 1.0, o, None, nu)
+    gl = [ddt.GdnLayer(q=dg["q"].data_ptr(), k=dg["k"].data_ptr(), v=dg["v"].data_ptr(),
+                       alpha=dg["alpha"].data_ptr(), beta=dg["beta"].data_ptr(), S_c=dg["S_c"].data_ptr(),
+                       node_u=nu.data_ptr(), x=dc["x"].data_ptr(), prefix=dc["prefix"].data_ptr())]
+    al = [ddt.AttnLayer(da["Kt"].data_ptr(), da["Vt"].data_ptr(), dK.data_ptr(), dV.data_ptr())]
+    dT = dev(np.asarray(T, np.int32))
+    pt = dev(page_table) if page_table is not None else None
+    ddt.ddt_commit_state(tb, dev(ph), dev(Lh), ddt.DDT_COMMIT_UPDATE, ddt.layer_table(gl, gpu), 1, Hk, Hv,
+                         dk, dk, ddt.DDT_BF16, C, ddt.DDT_BF16, ddt.layer_table(al, gpu), 1, Hkv, D,
+                         ddt.DDT_F16, pt, dT, cache_pages=cache_pages)
+    torch.cuda.synchronize()
+    return dict(par=par, off=off, g=g, c=c, K=K, V=Vv, a=a, dg=dg, dc=dc, dK=dK, dV=dV, T=dT,
+                status=host(tb.status))
+
+
+def _u16(t):
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def test_commit_refuses_a_sequence_its_cache_cannot_hold(gpu):
+    """A sequence whose accepted tokens do not fit its pages is not committed
+    at all (state, conv prefix, cache and T untouched, DDT_ST_CTX set); the
+    other sequence of the batch is committed as usual."""
+    banner("commit capacity: paged batch, one sequence refused")
+    trees = [synth.random_tree(synth.rng_for(5, 94, b), 22, 8) for b in range(2)]
+    paths = [oracle.root_path(t, int(np.argmax(oracle.depth(t))))[:4] for t in trees]
+    n_pages = 40
+    pt = np.arange(2 * 16, dtype=np.int32).reshape(2, 16)[:, ::-1].copy()  # 16 pages per sequence
+    pt[1] = pt[1] + 8                                                        # shared pool of 40 pages
+    T = [100, 16 * 16 - 2]   # sequence 1: 254 + 4 > 256 slots of its table
+    r = _commit_case(gpu, trees, paths, T, pt, n_pages)
+    assert r["status"][0] == 0 and r["status"][1] == ddt.DDT_ST_CTX
+    assert list(host(r["T"])) == [100 + 4, T[1]]
+    off = r["off"]
+    # sequence 1 untouched, bit for bit
+    S = host(r["dg"]["S_c"])
+    assert np.array_equal(S[1], r["g"]["S_c"][1])
+    assert np.array_equal(_u16(r["dc"]["prefix"])[1], r["c"]["prefix"][1])
+    # sequence 0 committed: state, prefix and its four cache slots
+    pg = [off[0] + j for j in paths[0]]
+    g = r["g"]
+    S_ref = oracle.commit_gdn_state(g["S_c"], g["q"], g["k"], g["v"], g["alpha"], g["beta"], pg, 0)
+    assert rel_err(S[0], S_ref, (0,)) < TOL
+    assert np.array_equal(oracle.num.f64(_u16(r["dc"]["prefix"])[0]),
+                          oracle.commit_conv_prefix(r["c"]["prefix"], r["c"]["x"], pg, 0))
+    K2, V2, _ = oracle.commit_kv(r["K"], r["V"], pt, np.asarray(T), r["a"]["Kt"], r["a"]["Vt"], pg, 0)
+    # no slot of sequence 1's pages changed: the whole pool equals sequence 0's commit alone
+    assert np.array_equal(host(r["dK"]).view(np.uint16), K2.view(np.uint16))
+    assert np.array_equal(host(r["dV"]).view(np.uint16), V2.view(np.uint16))
+
+
+@pytest.mark.parametrize("room", [2, 3])
+def test_commit_contiguous_cache_capacity(gpu, room):
+    """A contiguous cache of 8 pages (128 tokens) and a 3-token path: with 2
+    free slots the commit is refused whole; with 3 it fills the last slots."""
+    banner(f"commit capacity: contiguous cache, {room} free slots")
+    tree = synth.random_tree(synth.rng_for(6, 95), 22, 8)
+    path = oracle.root_path(tree, int(np.argmax(oracle.depth(tree))))[:3]
+    T0 = 128 - room
+    r = _commit_case(gpu, [tree], [path], [T0], None, 8, cache_pages=8)
+    S = host(r["dg"]["S_c"])
+    if room < 3:
+        assert r["status"][0] == ddt.DDT_ST_CTX and int(host(r["T"])[0]) == T0
+        assert np.array_equal(S, r["g"]["S_c"])
+        assert np.array_equal(_u16(r["dc"]["prefix"]), r["c"]["prefix"])
+        assert np.array_equal(host(r["dK"]).view(np.uint16), r["K"].view(np.uint16))
+        assert np.array_equal(host(r["dV"]).view(np.uint16), r["V"].view(np.uint16))
+    else:
+        assert r["status"][0] == 0 and int(host(r["T"])[0]) == 128
+        g = r["g"]
+        S_ref = oracle.commit_gdn_state(g["S_c"], g["q"], g["k"], g["v"], g["alpha"], g["beta"], path, 0)
+        assert rel_err(S[0], S_ref, (0,)) < TOL
+        K2, V2, _ = oracle.commit_kv(r["K"], r["V"], None, np.array([T0]), r["a"]["Kt"], r["a"]["Vt"], path, 0)
+        assert np.array_equal(host(r["dK"]).view(np.uint16), K2.view(np.uint16))
+        assert np.array_equal(host(r["dV"]).view(np.uint16), V2.view(np.uint16))

@@ -25,7 +25,7 @@ _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c
 class Plan(ctypes.Structure):
     _fields_ = [("B", _i32), ("n_total", _i32), ("n_max", _i32), ("W", _i32),
                 ("tree_off", _vp), ("parent", _vp), ("depth", _vp), ("anc", _vp),
-                ("win", _vp), ("order", _vp), ("slot", _vp), ("status", _vp)]
+                ("win", _vp), ("status", _vp)]
 
 
 class GdnLayer(ctypes.Structure):
@@ -46,7 +46,7 @@ class DDTError(RuntimeError):
 _SIGS = {
     "ddt_version": ([], _i32),
     "ddt_status_str": ([_i32], ctypes.c_char_p),
-    "ddt_plan_slots": ([_i32], _i32),
+    "ddt_source_hash": ([], ctypes.c_char_p),
     "ddt_tree_plan_host": ([ctypes.POINTER(Plan), _i32], _i32),
     "ddt_tree_plan": ([ctypes.POINTER(Plan), _i32, _vp], _i32),
     "ddt_tree_conv": ([ctypes.POINTER(Plan), _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
@@ -124,11 +124,10 @@ def dtype_code(t):
     return {torch.float32: DDT_F32, torch.float16: DDT_F16, torch.bfloat16: DDT_BF16}[t.dtype]
 
 
-def plan_struct(B, n_total, n_max, W, tree_off, parent, depth, anc, win, order, slot, status):
+def plan_struct(B, n_total, n_max, W, tree_off, parent, depth, anc, win, status):
     """Fill a Plan from tensors / arrays (device for ddt_tree_plan, host for
     ddt_tree_plan_host)."""
-    return Plan(B, n_total, n_max, W, *[_ptr(x) for x in
-                                         (tree_off, parent, depth, anc, win, order, slot, status)])
+    return Plan(B, n_total, n_max, W, *[_ptr(x) for x in (tree_off, parent, depth, anc, win, status)])
 
 
 class TreeBatch:
@@ -152,12 +151,9 @@ class TreeBatch:
         self.depth = torch.zeros(n, **i32)
         self.anc = torch.zeros(n, dtype=torch.int64, device=dev)
         self.win = torch.zeros(n * max(self.W - 1, 1), **i32)
-        self.order = torch.zeros(n, **i32)
-        self.slot = torch.zeros(n, **i32)
         self.status = torch.zeros(self.B, **i32)
         self.struct = plan_struct(self.B, self.n_total, self.n_max, self.W, self.tree_off,
-                                  self.parent, self.depth, self.anc, self.win, self.order,
-                                  self.slot, self.status)
+                                  self.parent, self.depth, self.anc, self.win, self.status)
 
 
 def _plan(p):
@@ -169,8 +165,8 @@ def ddt_version():
     return lib().ddt_version()
 
 
-def ddt_plan_slots(n_max):
-    return lib().ddt_plan_slots(int(n_max))
+def ddt_source_hash():
+    return lib().ddt_source_hash().decode()
 
 
 def ddt_tree_plan_host(plan_struct_host, max_levels):
@@ -286,8 +282,10 @@ def layer_table(structs, device):
 
 def ddt_commit_state(plan, path, L, mode, gdn_table, n_gdn, Hk, Hv, dk, dv, gdn_dtype, C,
                      conv_dtype, attn_table, n_attn, Hkv, D, kv_dtype, page_table, T,
-                     stream=None):
-    max_pages = int(page_table.shape[1]) if page_table is not None else 0
+                     stream=None, cache_pages=None):
+    """cache_pages: pages of a contiguous cache (page_table None), which
+    bounds the appends; with a page table its width is the bound."""
+    max_pages = int(page_table.shape[1]) if page_table is not None else int(cache_pages or 0)
     _check(lib().ddt_commit_state(_plan(plan), _ptr(path), _ptr(L), int(mode), _ptr(gdn_table),
                                   int(n_gdn), int(Hk), int(Hv), int(dk), int(dv), int(gdn_dtype),
                                   int(C), int(conv_dtype), _ptr(attn_table), int(n_attn),

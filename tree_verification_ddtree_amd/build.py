@@ -4,6 +4,7 @@
 """
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -23,9 +24,28 @@ FLAGS = [
 ]
 
 
-def _compile(src):
+def source_files():
+    """The files a build reads: the C header and every file of csrc/, in name order."""
+    files = [os.path.join(ROOT, "include", "ddtree.h")]
+    files += [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))]
+    return files
+
+
+def source_hash():
+    """sha256 of the sources, as "<path relative to the repository>\\0<bytes>"
+    records in name order; the library reports the value it was built with
+    (ddt_source_hash), so a caller can tell which sources a binary came from."""
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.relpath(f, ROOT).replace(os.sep, "/").encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _compile(src, src_hash):
     obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, f'-DDDT_SOURCE_HASH="{src_hash}"', "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -36,8 +56,9 @@ def _compile(src):
 def build(jobs=None, verbose=False):
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    h = source_hash()
     with cf.ThreadPoolExecutor(jobs) as ex:
-        res = list(ex.map(_compile, SOURCES))
+        res = list(ex.map(lambda f: _compile(f, h), SOURCES))
     for _, m in res:
         if m.strip() and verbose:
             print(m)

@@ -170,7 +170,6 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   // direct loads per wave and tile: fp16 K and V; or 8-bit K and V (1 KB
   // pieces, D / 128 each per wave) plus one load of the tile's scales
   constexpr int LPT = Q8 ? 2 * (D / 128) + 1 : 2 * WAVE_CH;
-  constexpr int FPS = Q8 ? LdsQ8<D>::FP_STAGES : NSTAGE;  // fp16 stages the matrix cores read
   constexpr int KS = D / 32;               // k-steps of the score product
   constexpr int DB = D / 16;               // channel blocks of the value product
   extern __shared__ half8 lds_raw[];

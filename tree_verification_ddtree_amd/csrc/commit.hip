@@ -31,6 +31,17 @@ __device__ __forceinline__ int path_len(const CommitArgs &A, int b, int n) {
   int l = A.L[b];
   return l < 0 ? 0 : (l > n ? n : l);
 }
+
+// Whether sequence b is committed: with attention layers its cache must take
+// the Lb accepted tokens (T0 + Lb <= 16 * max_pages, for a paged and for a
+// contiguous cache alike).  Every part of the commit asks the same question
+// on the same T[b] (only commit_len_kernel, which runs after them, changes
+// it), so a sequence is committed whole or not at all.
+__device__ __forceinline__ int seq_T0(const CommitArgs &A, int b) { return A.n_attn ? A.T[b] : 0; }
+__device__ __forceinline__ bool seq_fits(const CommitArgs &A, int T0, int Lb) {
+  if (A.n_attn == 0) return true;
+  return T0 >= 0 && (long long)T0 + Lb <= (long long)A.max_pages * DDT_PAGE;
+}
 __device__ __forceinline__ int path_node(const CommitArgs &A, int b, int r, int n) {
   int x = A.path[(size_t)b * A.P.n_max + r];
   return (x >= 0 && x < n) ? x : 0;
@@ -144,10 +155,12 @@ __device__ void commit_state_tile(const CommitArgs &A, int unit, char *lds) {
   int praw = 0;  // UPDATE: lane r's path entry r
   if constexpr (MODE == DDT_COMMIT_UPDATE) praw = A.path[(size_t)b * A.P.n_max + min(tid & 63, A.P.n_max - 1)];
   const int Lb = path_len(A, b, s.n);
-  // the layer record, the path and its length arrive in one round trip
-  // (without this the compiler moves each load behind the branch before it)
-  if constexpr (MODE == DDT_COMMIT_UPDATE) asm volatile("" ::"v"(praw), "v"(Lb), "v"(lay.node_u));
-  if (Lb == 0) return;
+  const int T0 = seq_T0(A, b);
+  // the layer record, the path, its length and the committed length arrive
+  // in one round trip (without this the compiler moves each load behind the
+  // branch before it)
+  if constexpr (MODE == DDT_COMMIT_UPDATE) asm volatile("" ::"v"(praw), "v"(Lb), "v"(T0), "v"(lay.node_u));
+  if (Lb == 0 || !seq_fits(A, T0, Lb)) return;
   float *Sbase = lay.S_c + (((size_t)b * A.Hv + h) * A.dv + row0) * DK;
   if (MODE == DDT_COMMIT_SELECT) {
     if (!lay.node_states) {
@@ -212,7 +225,7 @@ __device__ void commit_prefix(const CommitArgs &A, int unit) {
   if (!lay.x || !lay.prefix) return;
   const Seq s = seq_of(A.P, b);
   const int Lb = path_len(A, b, s.n), W1 = A.P.W - 1;
-  if (Lb == 0 || W1 == 0) return;
+  if (Lb == 0 || W1 == 0 || !seq_fits(A, seq_T0(A, b), Lb)) return;
   const int c = (cg * 256 + (int)threadIdx.x) * NE;
   if (c >= A.C) return;
   E *pre = (E *)lay.prefix + (size_t)b * W1 * A.C;
@@ -232,17 +245,13 @@ __device__ void commit_prefix(const CommitArgs &A, int unit) {
     if (j < W1) *reinterpret_cast<uint4 *>(pre + (size_t)j * A.C + c) = v[j];
 }
 
-__device__ __forceinline__ bool kv_fits(const CommitArgs &A, int b, int T0, int Lb) {
-  return !A.pt || Lb == 0 || (T0 + Lb - 1) / DDT_PAGE < A.max_pages;
-}
-
 template <typename E>
 __device__ void commit_kv(const CommitArgs &A, int unit) {
   const int b = unit % A.P.B, layer = unit / A.P.B;
   const Seq s = seq_of(A.P, b);
   const int Lb = path_len(A, b, s.n);
   const int T0 = A.T[b];
-  if (T0 < 0 || !kv_fits(A, b, T0, Lb)) return;
+  if (!seq_fits(A, T0, Lb)) return;
   constexpr int NE = Chunk<E>::N;
   const int cpr = A.D / NE;  // chunks per (token, head) row
   const ddt_attn_layer lay = A.al[layer];
@@ -270,7 +279,7 @@ __global__ void commit_len_kernel(CommitArgs A) {
   const Seq s = seq_of(A.P, b);
   const int Lb = path_len(A, b, s.n);
   const int T0 = A.T[b];
-  if (T0 >= 0 && kv_fits(A, b, T0, Lb))
+  if (seq_fits(A, T0, Lb))
     A.T[b] = T0 + Lb;
   else
     A.P.status[b] |= DDT_ST_CTX;
@@ -360,7 +369,7 @@ extern "C" int ddt_commit_state(const ddt_plan *P, const int32_t *path, const in
     if (Hkv < 1 || D < 1) return DDT_E_SHAPE;
     if (kv_dtype != DDT_F16 && kv_dtype != DDT_F32) return DDT_E_DTYPE;
     if (!page_table && P->B != 1) return DDT_E_ARG;
-    if (page_table && max_pages < 1) return DDT_E_SHAPE;
+    if (max_pages < 1) return DDT_E_SHAPE;  // the cache's capacity, paged or contiguous
     const int ne = kv_dtype == DDT_F16 ? 8 : 4;
     if (D % ne) return DDT_E_SHAPE;
     A.Hkv = Hkv; A.D = D; A.kvdt = kv_dtype;

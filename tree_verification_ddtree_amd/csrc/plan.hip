@@ -2,21 +2,13 @@
 //
 // The plan turns a parent-pointer draft tree (lucebox-hub README,
 // "02 · DFlash DDtree", "Algorithms used": DDTree verifies a tree of draft
-// tokens in one pass) into the index tables the other kernels read:
-// depth, ancestor bitmask (the attention mask), conv windows, and a visit
-// order with state slots for the tree recurrences.
-//
-// Visit order: a depth-first preorder in which the children of every node
-// are visited by increasing (subtree size, index), so the largest subtree
-// comes last.  A node's state must stay live until its last child has been
-// computed; giving a node its parent's slot when it is that last child, and
-// the parent's slot + 1 otherwise, never overwrites a live state, and each
-// "+1" edge leads into a subtree at most half as large as its parent's, so
-// floor(log2(n)) + 1 slots suffice for n nodes.
+// tokens in one pass) into the index tables the other kernels read: depth,
+// ancestor bitmask (the attention mask and the delta-net's root paths) and
+// conv windows.  Parents precede their children, so index order is already
+// topological and no visit order is needed.
 #include <stdio.h>
 #include <string.h>
 
-#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -42,109 +34,67 @@ static int plan_fields_ok(const ddt_plan *P) {
   if (!P) return DDT_E_ARG;
   if (P->B < 1 || P->n_total < 1 || P->n_max < 1 || P->n_max > DDT_MAX_NODES) return DDT_E_SHAPE;
   if (P->W < 1 || P->W > DDT_MAX_W) return DDT_E_SHAPE;
-  if (!P->tree_off || !P->parent || !P->depth || !P->anc || !P->win || !P->order || !P->slot ||
-      !P->status)
-    return DDT_E_ARG;
+  if (!P->tree_off || !P->parent || !P->depth || !P->anc || !P->win || !P->status) return DDT_E_ARG;
   return DDT_OK;
 }
 
 int check_plan(const ddt_plan *P) { return plan_fields_ok(P); }
 
 // ------------------------------------------------------------------ device plan
-// One wavefront per sequence, lane c = node c.  After the parents are in LDS
-// and each lane has chased its own root path, every table is built from
-// loops over the nodes whose index is the same in all lanes, reading the
-// other nodes' values out of their lanes (readlane) or as ballots, so no
-// step waits on an LDS read.
+// One wavefront per sequence, lane c = node c, nothing through LDS.  The
+// ancestor masks come from pointer jumping: after round k every lane holds
+// the nodes within 2^k steps above it and a pointer 2^k steps up (the root
+// points at itself), so six rounds cover any tree of up to 64 nodes.  The
+// depth is the mask's population count less one.  Ancestors have smaller
+// indices than their descendants, so the j-th previous token of a node is
+// the j-th highest bit of its mask below its own.
 __global__ __launch_bounds__(64) void plan_kernel(ddt_plan P, int max_levels) {
-  __shared__ int par[64];
   const int b = blockIdx.x, c = threadIdx.x;
   unsigned st = 0;
-  int o = P.tree_off[b], e = P.tree_off[b + 1];
-  if (!(o >= 0 && e > o && e <= P.n_total && e - o <= P.n_max)) st |= DDT_ST_TREE;
-  if (P.B == 1 && (o != 0 || e != P.n_total)) st |= DDT_ST_TREE;
-  Seq s = seq_of(P, b);
-  o = s.o;
-  const int n = s.n;
+  {
+    const int o = P.tree_off[b], e = P.tree_off[b + 1];
+    if (!(o >= 0 && e > o && e <= P.n_total && e - o <= P.n_max)) st |= DDT_ST_TREE;
+    if (P.B == 1 && (o != 0 || e != P.n_total)) st |= DDT_ST_TREE;
+  }
+  const Seq s = seq_of(P, b);
+  const int o = s.o, n = s.n;
   if (n == 0) {
     if (c == 0) P.status[b] = st | DDT_ST_TREE;
     return;
   }
-  int p = (c < n) ? P.parent[o + c] : 0;
-  bool ok = (c == 0) ? (p == -1) : (p >= 0 && p < c);
-  if (c < n && !ok) p = (c == 0) ? -1 : 0;  // safe stand-in: hang it off the root
-  if (__ballot(c < n && !ok)) st |= DDT_ST_TREE;
-  const int pc = (c == 0) ? -1 : p;  // this node's parent
-  par[c] = pc;
-  __syncthreads();
-
-  int d = 0;
-  unsigned long long a = 0;
-  if (c < n) {
-    a = 1ull << c;
-    for (int j = c; j > 0;) {
-      j = par[j];
-      a |= 1ull << j;
-      ++d;
-    }
+  const bool on = c < n;
+  int p = on ? P.parent[o + c] : 0;
+  const bool ok = (c == 0) ? (p == -1) : (p >= 0 && p < c);
+  if (__ballot(on && !ok)) st |= DDT_ST_TREE;
+  if (on && !ok) p = (c == 0) ? -1 : 0;  // safe stand-in: hang it off the root
+  // lanes past the tree point at themselves and hold no nodes
+  int up = !on ? c : (c == 0 ? 0 : p);
+  unsigned long long a = !on ? 0ull : ((1ull << c) | (1ull << up));
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const unsigned lo = __shfl((unsigned)a, up), hi = __shfl((unsigned)(a >> 32), up);
+    a |= ((unsigned long long)hi << 32) | lo;
+    up = __shfl(up, up);
   }
+  const int d = on ? __popcll(a) - 1 : 0;
   int dmax = d;
   for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
   if (dmax + 1 > max_levels) st |= DDT_ST_LEVELS;
-
-  // subtree sizes: the nodes whose root path holds x, one ballot per x
-  int size = 0;
-  for (int x = 0; x < n; ++x) {
-    const unsigned long long m = __ballot(c < n && ((a >> x) & 1ull));
-    if (c == x) size = __popcll(m);
-  }
-  // heaviest child = the one visited last: largest (size, index); and the
-  // summed sizes of the siblings visited before this node (smaller (size,
-  // index) under the same parent)
-  int hv = -1, hvs = 0, sb = 0;
-  for (int j = 1; j < n; ++j) {
-    const int pj = __builtin_amdgcn_readlane(pc, j), sj = __builtin_amdgcn_readlane(size, j);
-    if (pj == c && (hv < 0 || sj >= hvs)) {
-      hv = j;
-      hvs = sj;
-    }
-    if (pj == pc && j != c && (sj < size || (sj == size && j < c))) sb += sj;
-  }
-  // a node is light if it is not its parent's heaviest child
-  int hpar = -1;
-  for (int y = 0; y < n; ++y) {
-    const int hy = __builtin_amdgcn_readlane(hv, y);
-    if (y == pc) hpar = hy;
-  }
-  const int light1 = (c > 0 && hpar != c) ? 1 : 0;
-
-  if (c < n) {
+  if (on) {
     const int g = o + c;
-    // preorder position: the proper ancestors, plus for every node x on the
-    // root path (root excluded) the subtrees of the siblings visited before x
-    int pos = d, light = 0;
-    for (int x = 1; x < n; ++x) {
-      const int sbx = __builtin_amdgcn_readlane(sb, x), lx = __builtin_amdgcn_readlane(light1, x);
-      if ((a >> x) & 1ull) {
-        pos += sbx;
-        light += lx;
-      }
-    }
-    P.order[o + pos] = c;
-    P.slot[g] = light;
     P.depth[g] = d;
     P.anc[g] = a;
     const int W1 = P.W - 1;
-    int y = c, m = 0;  // walk up one ancestor per window entry
+    unsigned long long m = a & ~(1ull << c);  // proper ancestors
     for (int j = 1; j <= W1; ++j) {
-      if (m < d) {
-        y = par[y];
-        ++m;
-        P.win[(size_t)g * W1 + (j - 1)] = y;
+      int v;
+      if (j <= d) {
+        v = 63 - __clzll((long long)m);  // nearest remaining ancestor
+        m &= ~(1ull << v);
       } else {
-        int sl = W1 - (j - d);
-        P.win[(size_t)g * W1 + (j - 1)] = -(sl + 1);
+        v = -((W1 - (j - d)) + 1);  // committed prefix slot W1 - (j - d)
       }
+      P.win[(size_t)g * W1 + (j - 1)] = v;
     }
     if (W1 == 0) P.win[g] = 0;
   }
@@ -156,6 +106,13 @@ __global__ __launch_bounds__(64) void plan_kernel(ddt_plan P, int max_levels) {
 using namespace ddt;
 
 extern "C" int ddt_version(void) { return DDT_VERSION; }
+
+// The build passes the sha256 of the sources it compiled (build.py,
+// source_hash); a build that does not says so.
+#ifndef DDT_SOURCE_HASH
+#define DDT_SOURCE_HASH "unknown"
+#endif
+extern "C" const char *ddt_source_hash(void) { return DDT_SOURCE_HASH; }
 
 extern "C" const char *ddt_status_str(int code) {
   switch (code) {
@@ -169,13 +126,6 @@ extern "C" const char *ddt_status_str(int code) {
     case DDT_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
     default: return "unknown status";
   }
-}
-
-extern "C" int ddt_plan_slots(int32_t n_max) {
-  if (n_max < 1) return 1;
-  int s = 0;
-  while ((2 << s) <= n_max) ++s;  // floor(log2(n_max))
-  return s + 1;
 }
 
 extern "C" int ddt_tree_plan(const ddt_plan *P, int32_t max_levels, void *stream) {
@@ -209,35 +159,15 @@ extern "C" int ddt_tree_plan_host(const ddt_plan *P, int32_t max_levels) {
   for (int b = 0; b < B; ++b) {
     const int o = P->tree_off[b], n = P->tree_off[b + 1] - o;
     const int32_t *par = P->parent + o;
-    std::vector<int> d(n, 0), size(n, 1);
+    std::vector<int> d(n, 0);
     std::vector<unsigned long long> a(n, 1ull);
     for (int i = 1; i < n; ++i) {
       d[i] = d[par[i]] + 1;
       a[i] = a[par[i]] | (1ull << i);
     }
-    a[0] = 1ull;
-    for (int i = n - 1; i > 0; --i) size[par[i]] += size[i];
-    std::vector<std::vector<int>> ch(n);
-    for (int i = 1; i < n; ++i) ch[par[i]].push_back(i);
-    for (auto &v : ch)
-      std::sort(v.begin(), v.end(), [&](int x, int y) {
-        return size[x] != size[y] ? size[x] < size[y] : x < y;
-      });
-    std::vector<int> slot(n, 0), ord;
-    std::vector<int> stack{0};
-    while (!stack.empty()) {  // preorder, children by increasing (size, index)
-      int u = stack.back();
-      stack.pop_back();
-      ord.push_back(u);
-      for (int k = (int)ch[u].size() - 1; k >= 0; --k) stack.push_back(ch[u][k]);
-      for (size_t k = 0; k < ch[u].size(); ++k)
-        slot[ch[u][k]] = slot[u] + (k + 1 == ch[u].size() ? 0 : 1);
-    }
     for (int i = 0; i < n; ++i) {
       P->depth[o + i] = d[i];
       P->anc[o + i] = a[i];
-      P->order[o + i] = ord[i];
-      P->slot[o + i] = slot[i];
       int y = i;
       for (int j = 1; j <= W1; ++j) {
         int v;

@@ -14,12 +14,17 @@
 // Per node the distribution needs only the top_k logits (k <= 32), in
 // descending order with ties to the lower index:
 //  - samp_chunk_kernel: a 256-thread workgroup holds one chunk of a row in
-//    registers as order-preserving 32-bit keys.  The k-th largest thread
-//    maximum bounds the chunk's top k from below; the chunk's k-th largest
-//    key among the elements above that bound comes from three histogram
-//    passes over the key bits (11, 11, 10 bits; exact, and bounded work even
-//    for flat rows), ties at it go to the lowest indices (two passes over
-//    the index bits), and the k entries are written sorted;
+//    registers as order-preserving 32-bit keys.  A lower bound on the
+//    chunk's top k (the bar) comes from the thread maxima: each wavefront
+//    takes the ceil(k/4)-th largest of its 64 maxima by DPP maximum rounds,
+//    and the smallest of the four wavefronts' values is the bar, so at least
+//    k elements reach it.  On ordinary rows only a few elements do; they are
+//    compacted into LDS and ranked by counting (value, then lower index
+//    first).  Near-flat rows, where more than SAMP_FAST elements reach the
+//    bar, take the exact path instead: three histogram passes over the key
+//    bits (11, 11, 10 bits) find the k-th largest key, ties at it go to the
+//    lowest indices (two passes over the index bits).  Either way the k
+//    entries are written sorted;
 //  - samp_merge_kernel: one workgroup per row ranks the chunks' entries,
 //    then one wavefront forms p_i = 2^((v_i - v_0) log2(e) / T), the top-p
 //    cut (smallest prefix with c_i >= top_p * total) and the inverse-CDF
