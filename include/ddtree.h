@@ -264,6 +264,26 @@ int ddt_accept_walk(const ddt_plan *plan, const void *logits, int32_t dtype, int
                     int32_t *bonus, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The same verify argmax and walk for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, and
+ * harnesses that forbid allocation.  Arguments and results are those of
+ * ddt_accept_walk, without the workspace: the chunk maxima go to a static
+ * device array of DDT_NOALLOC_MAX_NODES * 16 keys (512 KiB) that the library
+ * holds on every GPU it runs on until the process ends.  The call allocates
+ * and frees nothing.  Every key it reads is first written by the same call,
+ * so the array needs no clearing; but all calls on one GPU share it, so two
+ * calls that overlap on one GPU (different streams, not ordered) race and
+ * must be ordered by the caller.
+ * Errors: as ddt_accept_walk, plus DDT_E_SHAPE for n_total above
+ * DDT_NOALLOC_MAX_NODES and DDT_E_HIP if the array's device address cannot
+ * be found; nothing is launched then.
+ */
+#define DDT_NOALLOC_MAX_NODES 4096
+int ddt_accept_walk_noalloc(const ddt_plan *plan, const void *logits, int32_t dtype, int32_t V,
+                            const int32_t *draft_tok, int32_t *argmax, int32_t *path, int32_t *L,
+                            int32_t *bonus, void *stream);
+
+/*
  * Stochastic acceptance (temperature > 0).  Requests without a temperature
  * are sampled with the model card's settings (temperature 1.0, top_p 0.95,
  * top_k 20; codehub lucebox-hub@main, "Making requests"); the pages give no

@@ -125,6 +125,11 @@ def test_device_entry_points_validate_before_launch():
     # walk: workspace, dtype
     assert L.ddt_accept_walk(bp, one, 2, 1000, one, one, one, one, one, one, 0, None) == -6
     assert L.ddt_accept_walk(bp, one, 1, 1000, one, one, one, one, one, one, 1 << 20, None) == -4
+    # allocation-free walk: more nodes than its static scratch holds, dtype
+    big = _dummy_plan(n=4097)
+    assert L.ddt_accept_walk_noalloc(ctypes.byref(big), one, 2, 1000, one, one, one, one, one, None) == -3
+    assert L.ddt_accept_walk_noalloc(bp, one, 1, 1000, one, one, one, one, one, None) == -4
+    assert L.ddt_accept_walk_noalloc(bp, None, 2, 1000, one, one, one, one, one, None) == -1
     # plan struct itself
     assert L.ddt_tree_plan(ctypes.byref(_dummy_plan(n_max=65)), 8, None) == -3
     assert L.ddt_tree_plan(ctypes.byref(_dummy_plan(W=0)), 8, None) == -3

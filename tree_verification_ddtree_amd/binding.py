@@ -66,6 +66,7 @@ _SIGS = {
     "ddt_accept_walk_workspace": ([ctypes.POINTER(Plan), _i32], _sz),
     "ddt_accept_walk": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                          _vp], _i32),
+    "ddt_accept_walk_noalloc": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "ddt_commit_state": ([ctypes.POINTER(Plan), _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp], _i32),
     "ddt_draft_topk_workspace": ([_i32, _i32, _i32, _i32], _sz),
@@ -268,6 +269,13 @@ def ddt_accept_walk(plan, logits, draft_tok, argmax, path, L, bonus, ws, stream=
     _check(lib().ddt_accept_walk(_plan(plan), _ptr(logits), dtype_code(logits), V,
                                  _ptr(draft_tok), _ptr(argmax), _ptr(path), _ptr(L), _ptr(bonus),
                                  _ptr(ws), wsb, _stream(stream)), "ddt_accept_walk")
+
+
+def ddt_accept_walk_noalloc(plan, logits, draft_tok, argmax, path, L, bonus, stream=None):
+    """ddt_accept_walk with the library's static scratch instead of a workspace."""
+    _check(lib().ddt_accept_walk_noalloc(_plan(plan), _ptr(logits), dtype_code(logits), int(logits.shape[-1]),
+                                         _ptr(draft_tok), _ptr(argmax), _ptr(path), _ptr(L), _ptr(bonus),
+                                         _stream(stream)), "ddt_accept_walk_noalloc")
 
 
 def layer_table(structs, device):

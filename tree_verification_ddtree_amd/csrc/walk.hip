@@ -10,6 +10,8 @@
 // associative, so the result does not depend on reduction order.  NaN is
 // keyed as -inf and -0 as +0.  A second kernel (one wavefront per tree)
 // combines the chunk keys, validates, and walks the tree with ballots.
+#include <mutex>
+
 #include "common.h"
 
 namespace ddt {
@@ -128,20 +130,15 @@ extern "C" size_t ddt_accept_walk_workspace(const ddt_plan *P, int32_t V) {
   return (size_t)P->n_total * NCHUNK * sizeof(unsigned long long);
 }
 
-extern "C" int ddt_accept_walk(const ddt_plan *P, const void *logits, int32_t dtype, int32_t V,
-                               const int32_t *draft_tok, int32_t *argmax, int32_t *path,
-                               int32_t *L, int32_t *bonus, void *ws, size_t ws_bytes,
-                               void *stream) {
-  int r = check_plan(P);
-  if (r) return r;
-  if (!logits || !draft_tok || !argmax || !path || !L || !bonus || !ws) return DDT_E_ARG;
-  if (V < 1) return DDT_E_SHAPE;
-  if (ws_bytes < ddt_accept_walk_workspace(P, V)) return DDT_E_WS;
+// The argmax and the walk with the chunk keys in `part` (n_total * NCHUNK
+// keys): argmax_chunks writes every key the walk reads, so `part` needs no
+// initialisation.
+static int walk_with(const ddt_plan *P, const void *logits, int32_t dtype, int32_t V, const int32_t *draft_tok,
+                     int32_t *argmax, int32_t *path, int32_t *L, int32_t *bonus, unsigned long long *part,
+                     hipStream_t st) {
   const int chunk = chunk_len(V);
   const int used = (V + chunk - 1) / chunk;
-  hipStream_t st = (hipStream_t)stream;
   dim3 grid(used, P->n_total);
-  auto *part = (unsigned long long *)ws;
   if (dtype == DDT_BF16)
     hipLaunchKernelGGL(argmax_chunks<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)logits,
                        V, P->n_total, chunk, part);
@@ -150,7 +147,74 @@ extern "C" int ddt_accept_walk(const ddt_plan *P, const void *logits, int32_t dt
                        P->n_total, chunk, part);
   else
     return DDT_E_DTYPE;
-  r = launch_status();
+  const int r = launch_status();
   if (r) return r;
   return launch_walk(P, V, used, part, draft_tok, argmax, path, L, bonus, st);
+}
+
+extern "C" int ddt_accept_walk(const ddt_plan *P, const void *logits, int32_t dtype, int32_t V,
+                               const int32_t *draft_tok, int32_t *argmax, int32_t *path,
+                               int32_t *L, int32_t *bonus, void *ws, size_t ws_bytes,
+                               void *stream) {
+  int r = check_plan(P);
+  if (r) return r;
+  if (!logits || !draft_tok || !argmax || !path || !L || !bonus || !ws) return DDT_E_ARG;
+  if (V < 1) return DDT_E_SHAPE;
+  if (dtype != DDT_BF16 && dtype != DDT_F32) return DDT_E_DTYPE;
+  if (ws_bytes < ddt_accept_walk_workspace(P, V)) return DDT_E_WS;
+  return walk_with(P, logits, dtype, V, draft_tok, argmax, path, L, bonus, (unsigned long long *)ws,
+                   (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// The walk for callers that cannot allocate: its chunk keys live in a
+// file-scope device array.  Each GPU holds its own copy of the array at its
+// own address, found once per device with hipGetSymbolAddress while that
+// device is current; host code passes that address, never the array's name
+// (which on the host is only a stand-in, not a device address).
+static __device__ __align__(256) unsigned long long scratch[DDT_NOALLOC_MAX_NODES * NCHUNK];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+unsigned long long *g_scratch[MAX_DEVICES] = {};
+
+// address of this device's copy of `scratch` (NULL and a recorded HIP error
+// if it cannot be had)
+unsigned long long *scratch_of_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_hip_error(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    set_hip_error(hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      set_hip_error(e);
+      return nullptr;
+    }
+    g_scratch[dev] = (unsigned long long *)ptr;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+extern "C" int ddt_accept_walk_noalloc(const ddt_plan *P, const void *logits, int32_t dtype, int32_t V,
+                                       const int32_t *draft_tok, int32_t *argmax, int32_t *path, int32_t *L,
+                                       int32_t *bonus, void *stream) {
+  int r = check_plan(P);
+  if (r) return r;
+  if (!logits || !draft_tok || !argmax || !path || !L || !bonus) return DDT_E_ARG;
+  if (V < 1 || P->n_total > DDT_NOALLOC_MAX_NODES) return DDT_E_SHAPE;
+  if (dtype != DDT_BF16 && dtype != DDT_F32) return DDT_E_DTYPE;
+  unsigned long long *part = scratch_of_current_device();
+  if (!part) return DDT_E_HIP;
+  return walk_with(P, logits, dtype, V, draft_tok, argmax, path, L, bonus, part, (hipStream_t)stream);
 }
