@@ -32,7 +32,10 @@
 //    blocks each).  A wavefront skips blocks past the sequence's rows.
 //  - The tree itself is one or two extra 32-key tiles (draft K/V of up to
 //    64 nodes) processed by the last split of the sequence, masked by the
-//    plan's ancestor bitmask; cache keys are never masked per row.
+//    plan's ancestor bitmask; cache keys are never masked per row.  That
+//    split stages its first tree tile in a fifth LDS stage before its main
+//    loop (fp16 path), so at the end the tile costs it only its matrix work,
+//    not a memory round trip.
 //  - Online softmax without rescaling the accumulators and without a
 //    cross-lane max per tile: a row's reference max is fixed by its first
 //    tile and probabilities are formed against it (fp16 P has 15 binades
@@ -117,6 +120,14 @@ __device__ __forceinline__ int n_active_splits(const AttnArgs &A, int Tb) {
   return n > A.n_splits ? A.n_splits : n;
 }
 
+// Registers of N 16-byte K chunks and N V chunks of a tile being filled.
+template <int N_>
+struct TileRegs {
+  static constexpr int N = N_;
+  uint4 k[N_];
+  half8 v[N_];
+};
+
 template <int D>
 struct Lds {
   // K stage: [32 rows][D] halves; row r = 16*tt + m holds the key that the
@@ -163,6 +174,15 @@ __device__ __forceinline__ int key_of_krow(int r) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Workgroup barrier of the K/V ring: this wave's LDS and scalar-memory
+// operations are complete (lgkmcnt(0)) and its direct-to-LDS tile loads are
+// left in flight, since every wave has already waited for exactly the tile
+// it needs (wait_tiles) before it arrives.  __syncthreads() would also drain
+// every vector-memory load (the compiler puts vmcnt(0) before its barrier,
+// because direct-to-LDS loads write LDS), which empties the ring at every
+// tile and leaves one tile of lookahead instead of NSTAGE - 1.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int D, int NB, bool Q8>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
@@ -181,25 +201,15 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   const int rows_b = A.G * s.n;
   const int row0 = rg * A.rows_wg;
   if (row0 >= rows_b) return;
-  bool cut;
-  const int Tb = ctx_len(A, b, &cut);
-  const int nsp = n_active_splits(A, Tb);
-  if (split >= nsp) return;
-  if (cut && split == 0 && g == 0 && rg == 0 && threadIdx.x == 0) A.P.status[b] |= DDT_ST_CTX;
-
-  const int chunk = split_chunk(A, Tb);
-  const int t_beg = split * chunk;
-  const int t_end = min(Tb, t_beg + chunk);
-  const int n_keys = t_end > t_beg ? t_end - t_beg : 0;
-  const int n_full = n_keys / TILE;                      // direct-load tiles
-  const bool has_part = (n_keys % TILE) != 0;            // ragged last cache tile
-  const int n_tree = (split == nsp - 1) ? (s.n + TILE - 1) / TILE : 0;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
 
-  // ---- resident Q fragments and per-row tree masks
+  // ---- resident Q fragments and per-row tree masks.  Rows past the
+  // sequence's rows (padding of the last row block) load the last real row:
+  // their results are never written out, and with every load unconditional
+  // the compiler can count the loads in flight (a guarded load makes it wait
+  // for all of them before the first matrix instruction).
   half8 qf[NB][KS];
   unsigned long long ancr[NB];
   bool blk_on[NB];
@@ -207,20 +217,29 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   for (int j = 0; j < NB; ++j) {
     const int blk0 = row0 + 16 * (w + 4 * j);
     blk_on[j] = blk0 < rows_b;
-    const int rho = blk0 + l16;
-    const bool ok = rho < rows_b;
-    const int node = ok ? rho / A.G : 0;
-    const int hq = g * A.G + (ok ? rho % A.G : 0);
-    ancr[j] = ok ? A.P.anc[s.o + node] : 0ull;
+    const int rho = min(blk0 + l16, rows_b - 1);
+    const int node = rho / A.G;
+    const int hq = g * A.G + rho % A.G;
+    ancr[j] = A.P.anc[s.o + node];
     const _Float16 *qp = A.q + ((size_t)(s.o + node) * A.Hq + hq) * D + 8 * lq;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ok)
-        qf[j][ks] = *reinterpret_cast<const half8 *>(qp + 32 * ks);
-      else
-        qf[j][ks] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[j][ks] = *reinterpret_cast<const half8 *>(qp + 32 * ks);
   }
+
+  // ---- the split's keys: these need the committed length, read while the
+  // Q fragments are on their way
+  bool cut;
+  const int Tb = ctx_len(A, b, &cut);
+  const int nsp = n_active_splits(A, Tb);
+  if (split >= nsp) return;
+  if (cut && split == 0 && g == 0 && rg == 0 && threadIdx.x == 0) A.P.status[b] |= DDT_ST_CTX;
+  const int chunk = split_chunk(A, Tb);
+  const int t_beg = split * chunk;
+  const int t_end = min(Tb, t_beg + chunk);
+  const int n_keys = t_end > t_beg ? t_end - t_beg : 0;
+  const int n_full = n_keys / TILE;                      // direct-load tiles
+  const bool has_part = (n_keys % TILE) != 0;            // ragged last cache tile
+  const int n_tree = (split == nsp - 1) ? (s.n + TILE - 1) / TILE : 0;
 
   f32x4 o[NB][DB];
   float mrow[NB], mseen[NB], lsum[NB];
@@ -342,9 +361,60 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  // ---- ragged cache tile or tree tile -> LDS stage through registers,
-  // zero-filling keys past the end (unwritten cache slots may hold NaN).
-  auto fill_tile = [&](bool tree, int kbase, int stage) {
+  // ---- a tree tile -> LDS stage through registers, zero-filling keys past
+  // the tree.  Thread tid fills K chunks and V chunks tid + 256 u, each one
+  // 16-byte slot of the stage: K chunk ci = key tau's channels 8 cc ..
+  // 8 cc + 7 (tau = ci / CPR), V chunk ci = keys 8 qg .. 8 qg + 7 of channel
+  // d (d = ci / 4, qg = ci % 4), so every LDS store is a whole slot on its
+  // own banks.  Every load (at clamped addresses, so none is conditional)
+  // is issued before the first store: a tile costs one memory round trip.
+  constexpr int CPT = TILE * CPR / 256;  // K (and V) chunks per thread and tile
+  static_assert(TILE * CPR == 4 * D, "as many V chunks as K chunks");
+  auto load_tree_tile = [&](int kbase, int h, auto &R) {
+    constexpr int HPT = std::remove_reference_t<decltype(R)>::N;
+    const int nlast = s.n > 0 ? s.n - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+      const int ci = tid + 256 * (h * HPT + u);
+      const int tau = ci / CPR, cc = ci % CPR;
+      const int key = kbase + tau;
+      const uint4 kx = *reinterpret_cast<const uint4 *>(
+          A.Kt + ((size_t)(s.o + min(key, nlast)) * A.Hkv + kv_head) * D + 8 * cc);
+      R.k[u] = key < s.n ? kx : make_uint4(0, 0, 0, 0);
+      const int d = ci >> 2, k0 = kbase + 8 * (ci & 3);
+      half8 vx;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vx[e] = A.Vt[((size_t)(s.o + min(k0 + e, nlast)) * A.Hkv + kv_head) * D + d];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + e >= s.n) vx[e] = (_Float16)0.0f;
+      R.v[u] = vx;
+    }
+  };
+  auto store_tile = [&](const auto &R, int h, int stage) {
+    constexpr int HPT = std::remove_reference_t<decltype(R)>::N;
+    _Float16 *Ks = lds + stage * Lds<D>::STAGE;
+    _Float16 *Vs = Ks + Lds<D>::K_HALVES;
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+      const int ci = tid + 256 * (h * HPT + u);
+      const int tau = ci / CPR, cc = ci % CPR;
+      const int r = krow_of(tau);
+      *reinterpret_cast<uint4 *>(Ks + r * D + 8 * (cc ^ ksw(r))) = R.k[u];
+      const int d = ci >> 2, qg = ci & 3;
+      *reinterpret_cast<half8 *>(Vs + d * 32 + 8 * (qg ^ vsw(d))) = R.v[u];
+    }
+  };
+  // a whole tree tile in one pass (one memory round trip)
+  auto fill_tree_tile = [&](int kbase, int stage) {
+    TileRegs<CPT> R;
+    load_tree_tile(kbase, 0, R);
+    store_tile(R, 0, stage);
+  };
+  // The epilogue's fill (a ragged cache tile, a second tree tile, or the
+  // 8-bit path's tree tile), with the accumulators live: one chunk at a time.
+  auto fill_tile_rolled = [&](bool tree, int kbase, int stage) {
     _Float16 *Ks = lds + stage * Lds<D>::STAGE;
     _Float16 *Vs = Ks + Lds<D>::K_HALVES;
     for (int ci = tid; ci < TILE * CPR; ci += 256) {
@@ -386,6 +456,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       }
     }
   };
+  // fp16 cache: the split that takes the tree stages its first tree tile in
+  // the spare LDS stage now, before the loop; the epilogue computes on it
+  // directly (the 8-bit path has no spare stage and fills it afterwards).
+  constexpr int TREE_STAGE = NSTAGE;
+  if constexpr (!Q8) {
+    if (n_tree > 0) fill_tree_tile(0, TREE_STAGE);
+  }
+  // Every load so far (the Q fragments, issued together with the read of
+  // the committed length) is complete before the first tiles go out: the
+  // compiler then sees no load pending on a register when the first matrix
+  // instruction runs and leaves the tiles in flight (vmcnt(0) only).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- scores of one 32-key tile: S^T = K Q^T (two 16-key halves)
   auto qk = [&](int stage, f32x4 (&S)[2][NB]) {
@@ -589,12 +671,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
           for (int j = 0; j < NB; ++j) Sc[tt][j] = Sn[tt][j];
       };
       if constexpr (!Q8) {
+        // the first NSTAGE - 1 tiles, all issued: a split with fewer tiles
+        // reads its last tile again into stages it never uses, so that the
+        // number of loads in flight is fixed and the first wait can leave
+        // them all but tile 0 outstanding
 #pragma unroll
-        for (int t = 0; t < NSTAGE - 1; ++t)
-          if (t < n_full) issue_tile(t, t, tile_page(t, 0), tile_page(t, 1));
+        for (int t = 0; t < NSTAGE - 1; ++t) {
+          const int tc = min(t, n_full - 1);
+          issue_tile(tc, t, tile_page(tc, 0), tile_page(tc, 1));
+        }
         // wait for tile 0: the loads of the later tiles may stay outstanding
-        wait_tiles(min(n_full, NSTAGE - 1) - 1);
-        __syncthreads();
+        wait_tiles(NSTAGE - 2);
+        ring_barrier();
         qk(0, Sn);
         fix_refs();
         auto main_loop = [&](auto NBA_c) {
@@ -603,7 +691,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
             const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
             // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
             if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
-            __syncthreads();  // tile it+1 landed; every wave is past tile it-1
+            ring_barrier();  // tile it+1 landed; every wave is past tile it-1
             // scores of tile it+1 (past the last tile they read a stale stage
             // and are dropped), probabilities and value product of tile it; the
             // loads of tile it+3 go out while the first K fragments arrive
@@ -625,9 +713,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         for (int t = 0; t < QS - 1; ++t)
           if (t < n_full) issue_q8(t, tile_page(t, 0), tile_page(t, 1));
         wait_tiles(min(n_full, QS - 1) - 1);
-        __syncthreads();
+        ring_barrier();
         convert_q8(0, 0);
-        __syncthreads();
+        ring_barrier();
         qk(0, Sn);
         fix_refs();
         auto main_loop = [&](auto NBA_c) {
@@ -635,9 +723,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
             const int nt = it + QS - 1;  // 8-bit tile issued in this iteration
             const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
             if (it + 1 < n_full) wait_tiles(min(n_full, it + QS - 1) - (it + 2));
-            __syncthreads();  // tile it+1 landed; every wave is past tile it-1
+            ring_barrier();  // tile it+1 landed; every wave is past tile it-1
             if (it + 1 < n_full) convert_q8((it + 1) % QS, (it + 1) % FS);  // into tile it-1's fp16 stage
-            __syncthreads();
+            ring_barrier();
             f32x4 Sc[2][NB];
             copy_S(Sc);
             tile_step(NBA_c, lds + ((it + 1) % FS) * Lds<D>::STAGE,
@@ -657,14 +745,15 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     for (int e = 0; e < n_ep; ++e) {
       const bool tree = !(has_part && e == 0);
       const int kbase = tree ? (e - (has_part ? 1 : 0)) * TILE : t_beg + n_full * TILE;
+      const int stage = (!Q8 && tree && kbase == 0) ? TREE_STAGE : 0;
       __syncthreads();  // the stage is no longer read
-      fill_tile(tree, kbase, 0);
+      if (stage == 0) fill_tile_rolled(tree, kbase, 0);
       __syncthreads();
       f32x4 S[2][NB];
       half8 pf[NB];
-      qk(0, S);
+      qk(stage, S);
       softmax(S, tree ? 2 : 1, kbase, pf);
-      pv(0, pf);
+      pv(stage, pf);
     }
     // any overflow in the workgroup?  The flags go through the first ring
     // stage, idle by now (a block-wide vote would take static LDS, and the
@@ -940,8 +1029,9 @@ static AttnArgs attn_args(const ddt_plan *P, const void *q, const int32_t *page_
 template <bool Q8>
 static int launch_attn_mfma(const ddt_plan &P, const AttnArgs &A, const Cfg &c, int D, hipStream_t st) {
   dim3 grid(c.n_splits, A.Hkv, P.B * c.n_rg);
+  // fp16: the ring and one spare stage for the tree tile (160 KiB at D = 256)
   const size_t lds = Q8 ? (size_t)(D == 256 ? LdsQ8<256>::TOTAL : LdsQ8<128>::TOTAL)
-                        : (size_t)NSTAGE * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
+                        : (size_t)(NSTAGE + 1) * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
 #define DDT_ATTN(DD, NBB)                                                                       \
   do {                                                                                          \
     hipError_t e_ = hipFuncSetAttribute((const void *)attn_mfma_kernel<DD, NBB, Q8>,            \
