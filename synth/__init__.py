@@ -182,19 +182,22 @@ def kv_pool(seed, key, n_pages, Hkv, D, dtype="f16", page=PAGE):
     return store(K, dtype), store(V, dtype)
 
 
-def kv_pool_q8(seed, key, n_pages, Hkv, D, page=PAGE):
+def kv_pool_q8(seed, key, n_pages, Hkv, D, page=PAGE, ksc=(0.015, 0.035), vsc=(0.015, 0.035), log2=False):
     """Paged 8-bit KV pool (the layouts of ``kv_pool``, int8) and one fp16 scale
     per token and KV head: Kq [n_pages][Hkv][page][D], Vq [n_pages][Hkv][D][page],
     Ksc and Vsc [n_pages][Hkv][page].  Codes are N(0, 40) rounded and clipped to
-    +-127, scales uniform in [0.015, 0.035], so code * scale is about N(0, 1)."""
+    +-127; scales are uniform in ``ksc`` / ``vsc`` (default [0.015, 0.035], so
+    code * scale is about N(0, 1)), or with ``log2`` 2**u for u uniform in the
+    given range of exponents."""
     def codes(tag, shape):
         x = np.rint(rng_for(seed, *key, tag).normal(0.0, 40.0, shape))
         return np.clip(x, -127, 127).astype(np.int8)
 
-    def scales(tag):
-        return rng_for(seed, *key, tag).uniform(0.015, 0.035, (n_pages, Hkv, page)).astype(np.float16)
-    return dict(Kq=codes(_T_KQ, (n_pages, Hkv, page, D)), Ksc=scales(_T_KS),
-                Vq=codes(_T_VQ, (n_pages, Hkv, D, page)), Vsc=scales(_T_VS))
+    def scales(tag, rng_):
+        u = rng_for(seed, *key, tag).uniform(rng_[0], rng_[1], (n_pages, Hkv, page))
+        return (np.exp2(u) if log2 else u).astype(np.float16)
+    return dict(Kq=codes(_T_KQ, (n_pages, Hkv, page, D)), Ksc=scales(_T_KS, ksc),
+                Vq=codes(_T_VQ, (n_pages, Hkv, D, page)), Vsc=scales(_T_VS, vsc))
 
 
 def attn_inputs(seed, key, n, Hq, Hkv, D, dtype="f16"):

@@ -271,12 +271,20 @@ def test_attn_mfma_shapes(gpu, case):
 
 
 # ---- 8-bit cache: the same attention over fp16(code * token scale)
-def attn_q8_case(gpu, trees, T, Hq, Hkv, D, seed, paged=True, n_splits=0):
+Q8_SCALES = {
+    "default": {},
+    # V scales over 16 binades (2^-12 .. 2^4) in token order: later tiles hold
+    # scales far above and below the first tile's, K scales up to 0.06
+    "wide": dict(ksc=(-10.0, -4.0), vsc=(-12.0, 4.0), log2=True),
+}
+
+
+def attn_q8_case(gpu, trees, T, Hq, Hkv, D, seed, paged=True, n_splits=0, scales="default"):
     tb, par, off = make_batch(trees, 4, gpu)
     n, B = len(par), len(trees)
     T = np.asarray(T)
     pt, P = synth.page_layout(seed, (70,), T, [len(t) for t in trees], shuffle=paged)
-    c = synth.kv_pool_q8(seed, (70,), P, Hkv, D)
+    c = synth.kv_pool_q8(seed, (70,), P, Hkv, D, **Q8_SCALES[scales])
     a = synth.attn_inputs(seed, (71,), n, Hq, Hkv, D, "f16")
     use_pt = paged or B > 1
     T_max = int(T.max())
@@ -304,15 +312,19 @@ ATTN_Q8 = {
     "batch_paged": ([22, 8, 64], [1500, 37, 3001], 24, 4, 256, True, 0),
     "d128": ([16, 32], [777, 2048], 16, 2, 128, True, 3),
     "many_splits": ([22], [40000], 6, 1, 256, False, 100),
+    "ragged_tiny_splits": ([5], [75], 24, 4, 256, False, 4),
+    "wide_scales": ([22], [4133], 24, 4, 256, False, 0, "wide"),
+    "wide_scales_d128_paged": ([16, 9], [3000, 517], 16, 2, 128, True, 5, "wide"),
 }
 
 
 @pytest.mark.parametrize("case", list(ATTN_Q8))
 def test_attn_q8(gpu, case):
-    sizes, T, Hq, Hkv, D, paged, ns = ATTN_Q8[case]
-    banner(f"attn q8 {case}: sizes {sizes} T {T} Hq {Hq} Hkv {Hkv} D {D} splits {ns}")
+    sizes, T, Hq, Hkv, D, paged, ns, *sc = ATTN_Q8[case]
+    sc = sc[0] if sc else "default"
+    banner(f"attn q8 {case}: sizes {sizes} T {T} Hq {Hq} Hkv {Hkv} D {D} splits {ns} scales {sc}")
     trees = [synth.random_tree(synth.rng_for(16, 72, b), n, 10) for b, n in enumerate(sizes)]
-    assert attn_q8_case(gpu, trees, T, Hq, Hkv, D, 16, paged=paged, n_splits=ns) < TOL
+    assert attn_q8_case(gpu, trees, T, Hq, Hkv, D, 16, paged=paged, n_splits=ns, scales=sc) < TOL
 
 
 def test_attn_q8_full_context_128k_sampled(gpu):

@@ -57,6 +57,7 @@ namespace ddt {
 constexpr int KV_STREAM_CPOL = 2;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TILE = 32;  // keys per pipeline stage (two pages)
@@ -76,8 +77,11 @@ struct AttnArgs {
   int Hq, Hkv, G;
   float c;  // scale * log2(e)
   int n_splits, n_rg, rows_wg;
-  float *Opart;  // [B][Hkv][n_rg][n_splits][rows_wg][D]
-  float2 *ML;    // [B][Hkv][n_rg][n_splits][rows_wg]
+  // a split's output rows divided by their own row sums, in fp16 (values of
+  // V's range; the rounding, 2^-11 relative, stays within the fp16 inputs'
+  // own precision), and each row's reference max and sum
+  _Float16 *Opart;  // [B][Hkv][n_rg][n_splits][rows_wg][D]
+  float2 *ML;       // [B][Hkv][n_rg][n_splits][rows_wg]
   float *out;    // [n_total][Hq][D]
 };
 
@@ -133,8 +137,10 @@ struct Lds {
   // K stage: [32 rows][D] halves; row r = 16*tt + m holds the key that the
   // score MFMA of key-half tt reads as A-row m; the 16-byte chunk c of a row
   // sits at chunk position c ^ ksw(r).
-  // V stage: [D channels][4 groups][8 keys] halves; group q of channel d
-  // sits at slot q ^ vsw(d).
+  // V stage: [2 page halves][D channels][2 groups][8 keys] halves: group q
+  // (keys 8q .. 8q + 7 of the tile) of channel d sits in half q >> 1, slot
+  // (q & 1) ^ bit 3 of d (vslot).  Every 1 KB piece of a stage then lies in
+  // one page half, so each direct load of a wave reads from one page.
   // Both swizzles give the 16 lanes that read one 16-byte slot each in a
   // matrix-core operand load 16 different bank groups.
   static constexpr int K_HALVES = TILE * D;
@@ -158,10 +164,13 @@ struct LdsQ8 {
 };
 
 // K rows are whole bank periods (256 B) long, so rows r and r + 8 collide
-// without the low four row bits in the swizzle; V channel rows are a quarter
-// period, so channels d and d + 4 share banks unless bits 2-3 of d enter.
+// without the low four row bits in the swizzle; V channel rows are an eighth
+// of a period, so channels d and d + 8 share banks unless bit 3 of d enters.
 __device__ __forceinline__ int ksw(int r) { return r & 15; }
-__device__ __forceinline__ int vsw(int d) { return (d >> 2) & 3; }
+template <int D>
+__device__ __forceinline__ int vslot(int d, int q) {
+  return (q >> 1) * (16 * D) + d * 16 + 8 * ((q & 1) ^ ((d >> 3) & 1));
+}
 
 // tile-local key tau (0..31) <-> K row in LDS
 __device__ __forceinline__ int krow_of(int tau) {
@@ -257,31 +266,42 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 
   // ---- full cache tile -> LDS stage, straight from HBM (global_load_lds).
   // Wave w fills 1 KB pieces w, w+4, ...; lane l of a piece lands at byte
-  // 16*l, so each lane fetches whichever chunk belongs there.
-  auto issue_tile = [&](int it, int stage, int pg0, int pg1) {
+  // 16*l, so each lane fetches whichever chunk belongs there.  A piece lies
+  // in one page (the K rows of a piece are keys of one page half, and V
+  // pieces are laid out by page half), so a load's address is the page's
+  // base, the same for the whole wave, plus a lane offset that every tile
+  // shares: khalf / vhalf say which page, koff / voff the offsets in halves.
+  int koff[WAVE_CH], voff[WAVE_CH];
+  bool khalf[WAVE_CH], vhalf[WAVE_CH];
+#pragma unroll
+  for (int k = 0; k < WAVE_CH; ++k) {
+    const int piece = w + 4 * k;
+    const int P = piece * 64 + lane;       // chunk position in the stage
+    const int r = P / CPR, cpos = P % CPR;  // K row and chunk slot
+    const int tau = key_of_krow(r);
+    khalf[k] = __builtin_amdgcn_readfirstlane(tau >> 4);
+    koff[k] = (tau & 15) * D + 8 * (cpos ^ ksw(r));
+    constexpr int PPH = D / 32;  // V pieces per page half
+    const int Pv = (piece % PPH) * 64 + lane;
+    const int d = Pv >> 1, q1 = (Pv & 1) ^ ((d >> 3) & 1);
+    vhalf[k] = piece >= PPH;
+    voff[k] = d * DDT_PAGE + 8 * q1;
+  }
+  auto issue_tile = [&](int stage, int pg0, int pg1) {
     _Float16 *Ks = lds + stage * Lds<D>::STAGE;
     _Float16 *Vs = Ks + Lds<D>::K_HALVES;
+    const _Float16 *kb0 = A.Kc + ((size_t)pg0 * A.Hkv + kv_head) * DDT_PAGE * D;
+    const _Float16 *kb1 = A.Kc + ((size_t)pg1 * A.Hkv + kv_head) * DDT_PAGE * D;
+    const _Float16 *vb0 = A.Vc + ((size_t)pg0 * A.Hkv + kv_head) * D * DDT_PAGE;
+    const _Float16 *vb1 = A.Vc + ((size_t)pg1 * A.Hkv + kv_head) * D * DDT_PAGE;
 #pragma unroll
-    for (int k = 0; k < WAVE_CH; ++k) {
-      const int piece = w + 4 * k;
-      const int P = piece * 64 + lane;       // chunk position in the stage
-      const int r = P / CPR, cpos = P % CPR;  // K row and chunk slot
-      const int cc = cpos ^ ksw(r);
-      const int tau = key_of_krow(r);
-      const int pg = tau < 16 ? pg0 : pg1;
-      const _Float16 *src = A.Kc + (((size_t)pg * A.Hkv + kv_head) * DDT_PAGE + (tau & 15)) * D + 8 * cc;
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Ks + piece * 512), 16, 0, KV_STREAM_CPOL);
-    }
+    for (int k = 0; k < WAVE_CH; ++k)
+      __builtin_amdgcn_global_load_lds((const void *)((khalf[k] ? kb1 : kb0) + koff[k]),
+                                       (lds_void *)(Ks + (w + 4 * k) * 512), 16, 0, KV_STREAM_CPOL);
 #pragma unroll
-    for (int k = 0; k < WAVE_CH; ++k) {
-      const int piece = w + 4 * k;
-      const int P = piece * 64 + lane;
-      const int d = P >> 2, slot = P & 3;
-      const int qg = slot ^ vsw(d);
-      const int pg = (qg >> 1) ? pg1 : pg0;
-      const _Float16 *src = A.Vc + (((size_t)pg * A.Hkv + kv_head) * D + d) * DDT_PAGE + 8 * (qg & 1);
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(Vs + piece * 512), 16, 0, KV_STREAM_CPOL);
-    }
+    for (int k = 0; k < WAVE_CH; ++k)
+      __builtin_amdgcn_global_load_lds((const void *)((vhalf[k] ? vb1 : vb0) + voff[k]),
+                                       (lds_void *)(Vs + (w + 4 * k) * 512), 16, 0, KV_STREAM_CPOL);
   };
 
   // ---- Q8: 8-bit tile -> its staging stage, straight from HBM.  A page of
@@ -320,7 +340,10 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     const _Float16 *Sc = reinterpret_cast<const _Float16 *>(St + LdsQ8<D>::K_BYTES + LdsQ8<D>::V_BYTES);
     _Float16 *Kf = lds + fstage * Lds<D>::STAGE;
     _Float16 *Vf = Kf + Lds<D>::K_HALVES;
-    auto dq8 = [](uint2 q, half8 sc8) -> half8 {
+    // codes are read as a vector type (not HIP's uint2): the compiler then
+    // leaves the ring's direct-to-LDS loads in flight across the read
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    auto dq8 = [](u32x2 q, half8 sc8) -> half8 {
       const unsigned x0 = q.x ^ 0x80808080u, x1 = q.y ^ 0x80808080u;
       typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 hb = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
@@ -330,20 +353,24 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       const half8 v = __builtin_bit_cast(half8, hb) - (half8)(_Float16)1152.0f;
       return v * sc8;
     };
-#pragma unroll 2
+#pragma unroll
     for (int k = 0; k < (TILE * CPR) / 256; ++k) {  // K: token tau, chunk cc
       const int idx = threadIdx.x + 256 * k, tau = idx / CPR, cc = idx % CPR;
-      const uint2 q = *reinterpret_cast<const uint2 *>(St + tau * D + 8 * cc);
+      const u32x2 q = *reinterpret_cast<const u32x2 *>(St + tau * D + 8 * cc);
       const half8 v = dq8(q, (half8)Sc[tau]);
       const int r = krow_of(tau);
       *reinterpret_cast<half8 *>(Kf + r * D + 8 * (cc ^ ksw(r))) = v;
     }
-#pragma unroll 2
-    for (int k = 0; k < (4 * D) / 256; ++k) {  // V: channel d, keys 8 qg .. 8 qg + 7
-      const int idx = threadIdx.x + 256 * k, d = idx >> 2, qg = idx & 3;
-      const uint2 q = *reinterpret_cast<const uint2 *>(St + LdsQ8<D>::K_BYTES + (qg >> 1) * 16 * D + 16 * d + 8 * (qg & 1));
+    // V: thread idx writes slot idx & 1 of channel d of page half h, in the
+    // order of the fp16 stage (a 16-lane phase writes 256 contiguous bytes);
+    // the slot holds group q1 = slot ^ bit 3 of d, keys 8 q1 .. 8 q1 + 7
+#pragma unroll
+    for (int k = 0; k < (4 * D) / 256; ++k) {
+      const int idx = threadIdx.x + 256 * k, h = idx / (2 * D), d = (idx >> 1) % D;
+      const int q1 = (idx & 1) ^ ((d >> 3) & 1), qg = 2 * h + q1;
+      const u32x2 q = *reinterpret_cast<const u32x2 *>(St + LdsQ8<D>::K_BYTES + h * 16 * D + 16 * d + 8 * q1);
       const half8 sv = *reinterpret_cast<const half8 *>(Sc + TILE + 8 * qg);
-      *reinterpret_cast<half8 *>(Vf + d * 32 + 8 * (qg ^ vsw(d))) = dq8(q, sv);
+      *reinterpret_cast<half8 *>(Vf + vslot<D>(d, qg)) = dq8(q, sv);
     }
   };
 
@@ -403,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
       const int r = krow_of(tau);
       *reinterpret_cast<uint4 *>(Ks + r * D + 8 * (cc ^ ksw(r))) = R.k[u];
       const int d = ci >> 2, qg = ci & 3;
-      *reinterpret_cast<half8 *>(Vs + d * 32 + 8 * (qg ^ vsw(d))) = R.v[u];
+      *reinterpret_cast<half8 *>(Vs + vslot<D>(d, qg)) = R.v[u];
     }
   };
   // a whole tree tile in one pass (one memory round trip)
@@ -452,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int d = 8 * cc + x;
-        Vs[d * 32 + 8 * (qg ^ vsw(d)) + e] = vx[x];
+        Vs[vslot<D>(d, qg) + e] = vx[x];
       }
     }
   };
@@ -551,16 +578,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   };
   auto vfrag = [&](const _Float16 *Vs, int n) -> half8 {
     const int d = 16 * n + l16;
-    return *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ vsw(d)));
+    return *reinterpret_cast<const half8 *>(Vs + vslot<D>(d, lq));
   };
-  // One full tile of the main loop: scores of the next tile (Ks1) while the
+  // The 8-bit path's tile step: the same work in batches, no loads (the
+  // fp16 path's step below measured slower here, behind the conversion pass
+  // and its second barrier).  Scores of the next tile (Ks1) while the
   // probabilities and value product of this tile (S, Vs0) are formed, for
   // the first NBA row blocks of this wave (the others are padding past the
   // sequence's rows and are skipped).  sched_barrier fences keep each batch
   // of LDS reads one batch ahead of the MFMAs that consume it and put the
   // softmax next to the score MFMAs.
-  auto tile_step = [&](auto NBA_c, const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
-                       f32x4 (&Sn)[2][NB], auto &&in_shadow) {
+  auto tile_step_ahead = [&](auto NBA_c, const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
+                             f32x4 (&Sn)[2][NB]) {
     constexpr int NBA = decltype(NBA_c)::value;
     constexpr int KH = KS / 2;
 #pragma unroll
@@ -574,8 +603,6 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) ka[tt][ks] = kfrag(Ks1, tt, ks);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    in_shadow();  // work that needs no fragment, done while they arrive
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NBA > 0) {
 #pragma unroll
@@ -621,13 +648,76 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     }
   };
 
+  // One full tile of the main loop: scores of the next tile (Ks1) while the
+  // probabilities and value product of this tile (S, Vs0) are formed, for
+  // the first NBA row blocks of this wave (the others are padding past the
+  // sequence's rows and are skipped).  With one wavefront per SIMD, a VALU
+  // instruction runs in the shadow of the matrix pipe only when it sits
+  // between two MFMAs, a few per MFMA; so the VALU work is spread over all
+  // of them: the score MFMAs carry the tile's loads (`issue`, straight-line
+  // code) and block 0's probabilities, and block j's value product carries
+  // block j + 1's probabilities (sched_group_barrier pairs each MFMA with a
+  // few other instructions).
+  auto tile_step = [&](auto NBA_c, const _Float16 *Ks1, const _Float16 *Vs0, const f32x4 (&S)[2][NB],
+                       f32x4 (&Sn)[2][NB], auto &&issue) {
+    constexpr int NBA = decltype(NBA_c)::value;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < NBA; ++j) Sn[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NBA == 0) {
+      issue();
+    } else {
+      half8 kf[2][KS], pf[NB];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) kf[tt][ks] = kfrag(Ks1, tt, ks);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < NBA; ++j)
+            Sn[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[tt][ks], qf[j][ks], Sn[tt][j], 0, 0, 0);
+      issue();
+      softmax_blk(S, 0, pf[0]);
+#pragma unroll
+      for (int i = 0; i < 2 * KS * NBA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x416, 3, 0);  // VALU, SALU, VMEM, transcendental
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      half8 vf[DB];
+#pragma unroll
+      for (int n = 0; n < DB; ++n) vf[n] = vfrag(Vs0, n);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NBA; ++j) {
+#pragma unroll
+        for (int n = 0; n < DB; ++n)
+          o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[n], pf[j], o[j][n], 0, 0, 0);
+        if (j + 1 < NBA) {
+          softmax_blk(S, j + 1, pf[j + 1]);
+#pragma unroll
+          for (int n = 0; n < DB; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x406, 4, 1);  // VALU, SALU, transcendental
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // ---- O^T += V^T P^T for one tile
   auto pv = [&](int stage, const half8 (&pf)[NB]) {
     const _Float16 *Vs = lds + stage * Lds<D>::STAGE + Lds<D>::K_HALVES;
 #pragma unroll
     for (int n = 0; n < DB; ++n) {
       const int d = 16 * n + l16;
-      const half8 vf = *reinterpret_cast<const half8 *>(Vs + d * 32 + 8 * (lq ^ vsw(d)));
+      const half8 vf = *reinterpret_cast<const half8 *>(Vs + vslot<D>(d, lq));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         o[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[j], o[j][n], 0, 0, 0);
@@ -678,7 +768,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
         for (int t = 0; t < NSTAGE - 1; ++t) {
           const int tc = min(t, n_full - 1);
-          issue_tile(tc, t, tile_page(tc, 0), tile_page(tc, 1));
+          issue_tile(t, tile_page(tc, 0), tile_page(tc, 1));
         }
         // wait for tile 0: the loads of the later tiles may stay outstanding
         wait_tiles(NSTAGE - 2);
@@ -686,21 +776,29 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         qk(0, Sn);
         fix_refs();
         auto main_loop = [&](auto NBA_c) {
-          for (int it = 0; it < n_full; ++it) {
+          // while tiles are left to issue: one goes out per iteration, and
+          // exactly one more is in flight behind tile it + 1
+          int it = 0;
+          for (; it + NSTAGE - 1 < n_full; ++it) {
             const int nt = it + NSTAGE - 1;  // tile issued in this iteration
-            const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
-            // tile it+1 must have landed; tiles up to it+NSTAGE-2 may be in flight
-            if (it + 1 < n_full) wait_tiles(min(n_full, it + NSTAGE - 1) - (it + 2));
-            ring_barrier();  // tile it+1 landed; every wave is past tile it-1
-            // scores of tile it+1 (past the last tile they read a stale stage
-            // and are dropped), probabilities and value product of tile it; the
-            // loads of tile it+3 go out while the first K fragments arrive
+            const int npg0 = tile_page(nt, 0), npg1 = tile_page(nt, 1);
+            wait_tiles(NSTAGE - 3);  // tile it + 1 landed
+            ring_barrier();  // ... for every wave; every wave is past tile it - 1
             f32x4 Sc[2][NB];
             copy_S(Sc);
             tile_step(NBA_c, lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
-                      lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
-                        if (nt < n_full) issue_tile(nt, nt % NSTAGE, npg0, npg1);
-                      });
+                      lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn,
+                      [&]() { issue_tile(nt % NSTAGE, npg0, npg1); });
+          }
+          // the last tiles: nothing left to issue (past the last tile the
+          // scores read a stale stage and are dropped)
+          for (; it < n_full; ++it) {
+            if (it + 1 < n_full) wait_tiles(n_full - it - 2);
+            ring_barrier();
+            f32x4 Sc[2][NB];
+            copy_S(Sc);
+            tile_step(NBA_c, lds + ((it + 1) % NSTAGE) * Lds<D>::STAGE,
+                      lds + (it % NSTAGE) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {});
           }
         };
         if (blk_on[NB - 1])
@@ -724,14 +822,15 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
             const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
             if (it + 1 < n_full) wait_tiles(min(n_full, it + QS - 1) - (it + 2));
             ring_barrier();  // tile it+1 landed; every wave is past tile it-1
+            // the next 8-bit tile goes out first (its stage held tile it - 1,
+            // converted two iterations ago)
+            if (nt < n_full) issue_q8(nt % QS, npg0, npg1);
             if (it + 1 < n_full) convert_q8((it + 1) % QS, (it + 1) % FS);  // into tile it-1's fp16 stage
             ring_barrier();
             f32x4 Sc[2][NB];
             copy_S(Sc);
-            tile_step(NBA_c, lds + ((it + 1) % FS) * Lds<D>::STAGE,
-                      lds + (it % FS) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn, [&]() {
-                        if (nt < n_full) issue_q8(nt % QS, npg0, npg1);
-                      });
+            tile_step_ahead(NBA_c, lds + ((it + 1) % FS) * Lds<D>::STAGE,
+                            lds + (it % FS) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn);
           }
         };
         if (blk_on[NB - 1])
@@ -785,17 +884,20 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
     const int rl = 16 * (w + 4 * j) + l16;  // row within the workgroup
     if (row0 + rl >= rows_b) continue;
     if (lq == 0) A.ML[base + rl] = make_float2(mrow[j], l);
-    float *op = A.Opart + (base + rl) * D + 4 * lq;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    _Float16 *op = A.Opart + (base + rl) * D + 4 * lq;
 #pragma unroll
     for (int n = 0; n < DB; ++n)
-      *reinterpret_cast<float4 *>(op + 16 * n) = make_float4(o[j][n][0], o[j][n][1], o[j][n][2], o[j][n][3]);
+      *reinterpret_cast<half4 *>(op + 16 * n) = half4{(_Float16)(o[j][n][0] * inv), (_Float16)(o[j][n][1] * inv),
+                                                      (_Float16)(o[j][n][2] * inv), (_Float16)(o[j][n][3] * inv)};
   }
 }
 
 // Merge the splits of one query row: one workgroup per row.  Every thread
 // first issues the loads of its share of the partial outputs (4 channels x
 // splits sg, sg + SG, ...); meanwhile wavefront 0 turns the split maxima
-// and sums into weights 2^((m_s - M) c) and the total L.  The weighted sums
+// and sums into weights l_s 2^((m_s - M) c) (the partials are normalised by
+// their own sums l_s) and their total L.  The weighted sums
 // are then added in a fixed order, so the result does not depend on timing.
 constexpr int MAX_SPLITS = 1024;
 
@@ -814,7 +916,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
   const int tid = threadIdx.x, lane = tid & 63;
   const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
   const int dc = tid % TPR, sg = tid / TPR;
-  const float *src = A.Opart + base * D + 4 * dc;
+  const _Float16 *src = A.Opart + base * D + 4 * dc;
   const size_t sstride = (size_t)A.rows_wg * D;
   // Every load that depends on no other goes out first: the context length,
   // wave 0's split statistics and each thread's first BATCH partials.  Split
@@ -824,10 +926,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
   const int nw = A.n_splits;
   float2 ml0 = make_float2(-INFINITY, 0.f);
   if (tid < 64) ml0 = A.ML[base + (size_t)min(lane, nw - 1) * A.rows_wg];
-  float4 v[BATCH];
+  half4 v[BATCH];
 #pragma unroll
-  for (int t = 0; t < BATCH; ++t)
-    v[t] = *reinterpret_cast<const float4 *>(src + min(sg + t * SG, nw - 1) * sstride);
+  for (int t = 0; t < BATCH; ++t) v[t] = *reinterpret_cast<const half4 *>(src + min(sg + t * SG, nw - 1) * sstride);
   // the context length is read after the partials are requested (left to
   // itself the scheduler clamps it first and so waits for it before them)
   __builtin_amdgcn_sched_barrier(0);
@@ -840,9 +941,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
     float l = 0.f;
     for (int sp = lane; sp < nsp; sp += 64) {
       const float2 ml = sp == lane ? ml0 : A.ML[base + (size_t)sp * A.rows_wg];
-      const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f((ml.x - m) * A.c);
+      const float wgt = (ml.x == -INFINITY) ? 0.f : ml.y * exp2f((ml.x - m) * A.c);
       wts[sp] = wgt;
-      l = fmaf(ml.y, wgt, l);
+      l += wgt;
     }
     // fixed-order total: lane partials gathered in lane order
 #pragma unroll
@@ -859,19 +960,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
     const int sp = sg + t * SG;
     if (sp < nsp) {
       const float wgt = wts[sp];
-      acc.x = fmaf(v[t].x, wgt, acc.x);
-      acc.y = fmaf(v[t].y, wgt, acc.y);
-      acc.z = fmaf(v[t].z, wgt, acc.z);
-      acc.w = fmaf(v[t].w, wgt, acc.w);
+      acc.x = fmaf((float)v[t].x, wgt, acc.x);
+      acc.y = fmaf((float)v[t].y, wgt, acc.y);
+      acc.z = fmaf((float)v[t].z, wgt, acc.z);
+      acc.w = fmaf((float)v[t].w, wgt, acc.w);
     }
   }
   for (int sp = sg + BATCH * SG; sp < nsp; sp += SG) {
     const float wgt = wts[sp];
-    const float4 x = *reinterpret_cast<const float4 *>(src + sp * sstride);
-    acc.x = fmaf(x.x, wgt, acc.x);
-    acc.y = fmaf(x.y, wgt, acc.y);
-    acc.z = fmaf(x.z, wgt, acc.z);
-    acc.w = fmaf(x.w, wgt, acc.w);
+    const half4 x = *reinterpret_cast<const half4 *>(src + sp * sstride);
+    acc.x = fmaf((float)x.x, wgt, acc.x);
+    acc.y = fmaf((float)x.y, wgt, acc.y);
+    acc.z = fmaf((float)x.z, wgt, acc.z);
+    acc.w = fmaf((float)x.w, wgt, acc.w);
   }
   part[sg][dc] = acc;
   __syncthreads();
@@ -1019,8 +1120,8 @@ static AttnArgs attn_args(const ddt_plan *P, const void *q, const int32_t *page_
   A.n_rg = c.n_rg;
   A.rows_wg = c.rows_wg;
   const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
-  A.Opart = (float *)ws;
-  A.ML = (float2 *)((char *)ws + rows * D * sizeof(float));
+  A.Opart = (_Float16 *)ws;
+  A.ML = (float2 *)((char *)ws + rows * D * sizeof(_Float16));
   A.out = out;
   return A;
 }
@@ -1068,7 +1169,7 @@ extern "C" size_t ddt_tree_attn_workspace(const ddt_plan *P, int32_t Hq, int32_t
   Cfg c = attn_cfg(P, Hq, Hkv, D, T_max, n_splits, DDT_F16);
   if (!c.mfma) return 0;
   const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
-  return rows * (size_t)D * sizeof(float) + rows * sizeof(float2);
+  return rows * (size_t)D * sizeof(_Float16) + rows * sizeof(float2);
 }
 
 extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, const void *Vc,
