@@ -24,10 +24,16 @@
 //    tokens that one 16-byte read of a channel-major V page provides.
 //  - K and V pages go straight from HBM into a 4-stage LDS ring
 //    (global_load_lds_dwordx4, up to three 32-key tiles in flight, no
-//    staging registers); the scores of the next tile are computed while
-//    the current tile's probabilities and value product are formed; 16-byte chunks are XOR-swizzled so the operand reads of a
-//    wavefront hit distinct banks.  The ragged last tile and the tree tiles
-//    go through registers so keys past the end can be zero-filled.
+//    staging registers); each direct load of a wavefront reads one page, at
+//    a wave-uniform page base plus a lane offset fixed for the whole split.
+//    16-byte chunks are XOR-swizzled so the operand reads of a wavefront
+//    hit distinct banks.  The ragged last tile and the tree tiles go
+//    through registers so keys past the end can be zero-filled.
+//  - One wavefront per SIMD (the accumulators and resident Q take ~490
+//    registers per lane), so a VALU instruction runs in the shadow of the
+//    matrix pipe only when it sits between two MFMAs: the scores of the next
+//    tile are issued with the tile's loads and block 0's probabilities
+//    between them, and block j's value product with block j + 1's.
 //  - Rows: 16-row blocks are dealt round-robin to the 4 wavefronts (NB
 //    blocks each).  A wavefront skips blocks past the sequence's rows.
 //  - The tree itself is one or two extra 32-key tiles (draft K/V of up to
@@ -42,9 +48,9 @@
 //    of headroom above 1); each lane only checks its own scores.  A split whose scores
 //    outgrow that headroom is recomputed with the true maxima, so the
 //    result is exact either way; on ordinary data the redo never happens.
-//  - Each split writes unnormalised partial O^T, its reference max and the
-//    row sum; a combine kernel merges the splits in fixed order
-//    (deterministic, no atomics).
+//  - Each split writes its output rows divided by their row sums (fp16),
+//    its reference max and the row sum; a combine kernel merges the splits
+//    in fixed order (deterministic, no atomics).
 #include <type_traits>
 
 #include "common.h"
