@@ -47,6 +47,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix peak
 METRIC = "tree-verify steps/sec (budget 22) + achieved HBM GB/s vs peak, 1 GPU"
 SETTLE_BATCH = 10  # settle-phase steps between restores of the committed length
+MIN_EACH_STEPS = 100  # one-by-one timed steps of a workload line, at least
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 CONFIGS = ("tiny", "layer_gdn", "layer_attn", "batched")
 
@@ -62,9 +63,10 @@ def _dev(a, device):
 def headroom(warmup=5, steps=100, kernel_reps=5):
     """Steps of context growth a workload must have room for: the committed
     length is put back to its configured value before every timed phase, and
-    the longest phase is the larger of the timed steps, the warmup, the
-    per-call passes and a settle batch (plus a few for the graph capture)."""
-    return max(warmup, steps, kernel_reps, SETTLE_BATCH) + 8
+    the longest phase is the larger of the timed steps (at least the 100 a
+    workload line times one by one), the warmup, the per-call passes and a
+    settle batch (plus a few for the graph capture)."""
+    return max(warmup, steps, MIN_EACH_STEPS, kernel_reps, SETTLE_BATCH) + 8
 
 
 class Workload:
@@ -268,9 +270,10 @@ class Workload:
             cache_pages=self.max_pages if (self.n_attn and self.pt is None) else None))
 
     def op_batches(self):
-        """Idempotent calls of the short ops for batch timing: every layer's
-        conv, every layer's delta-net, and the plan and walk (20 each)."""
-        ddt, c = self.ddt, self.c
+        """Idempotent calls of the ops for batch timing: every layer's conv,
+        every layer's delta-net, every attention layer's call (each on its own
+        cache, as in the step), and the plan and walk (20 each)."""
+        ddt, c, cp = self.ddt, self.c, self.copy[0]
         conv = [lambda x=x, y=y: ddt.ddt_tree_conv(self.tb, x["x"], x["prefix"], x["w"], 0, y)
                 for x, y in zip(self.conv, self.conv_out)]
         gdn = [lambda g=g, o=o, u=u: ddt.ddt_tree_gdn(self.tb, g["q"], g["k"], g["v"], g["alpha"],
@@ -279,7 +282,10 @@ class Workload:
         plan = [lambda: ddt.ddt_tree_plan(self.tb, c["levels"])] * 20
         walk = [lambda: ddt.ddt_accept_walk(self.tb, self.logits, self.tok, self.amax, self.path,
                                             self.L, self.bonus, self.walk_ws)] * 20
-        return {"plan": plan, "conv": conv, "gdn": gdn, "walk": walk}
+        attn = [lambda at=at, kv=kv, o=o: ddt.ddt_tree_attn(self.tb, at["q"], kv[0], kv[1], self.pt, self.T,
+                                                            self.T_max, at["Kt"], at["Vt"], o, self.attn_ws)
+                for at, kv, o in zip(cp.get("attn", []), cp.get("kv", []), cp.get("attn_out", []))]
+        return {"plan": plan, "conv": conv, "gdn": gdn, "walk": walk, "attn": attn}
 
     # ---------------------------------------------------------------- bytes
     def _e(self, which):
@@ -514,7 +520,7 @@ def measure_config(wl, steps, warmup, settle_s, copy_gbps, use_graph=True):
     graph = capture(wl) if use_graph else None
     run_steps(wl, graph, max(1, warmup // wl.ncopies))
     n_settle = settle(wl, graph, settle_s)
-    k = max(10, steps // wl.ncopies) if wl.ncopies > 1 else max(steps, 100)
+    k = max(10, steps // wl.ncopies) if wl.ncopies > 1 else max(steps, MIN_EACH_STEPS)
     ms_mean, L, _ = time_total(wl, graph, k)
     each = time_each(wl, graph, k)
     d = dist(each)
@@ -839,16 +845,17 @@ def cpu_baseline(st, seed, gdn_s=6.0, attn_s=8.0):
             "seconds_per_step": step_s}
 
 
-def kernel_timings(st, reps):
+def kernel_timings(st, reps, settle_s=0.3):
     """Per-call times of the step's ops, with HIP events on the launch stream.
-    Attention (the dominant kernel) and the commit are timed call by call
-    inside eager steps, one op per pass; the short ops (plan, conv,
-    delta-net, walk) as graph-replayed back-to-back batches under one event
-    pair, because an event pair around a single few-microsecond call adds a
-    gap of its own."""
+    The commit is timed call by call inside eager steps; the others (plan,
+    conv, delta-net, attention, walk) as graph-replayed back-to-back batches
+    under one event pair (all 16 attention layers, each on its own cache,
+    as the step runs them), so that a call's time is its kernels' time on
+    the stream and not the gaps an event pair or an eager launch adds; each
+    batch is replayed untimed for settle_s seconds first."""
     import torch
     timer = {}
-    for op in ("attn", "commit"):
+    for op in ("commit",):
         st.reset_T()
         st.timer = {op: []}
         for _ in range(reps):
@@ -866,6 +873,10 @@ def kernel_timings(st, reps):
                 fn()
         gb.replay()
         torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle_s  # the clock falls while the host captures
+        while time.perf_counter() < t_end:
+            gb.replay()
+            torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
@@ -896,6 +907,9 @@ def main():
                          "over a few hundred ms of load)")
     ap.add_argument("--draft", type=int, default=0, metavar="B",
                     help="only time the draft top-K and tree build for B sequences and print that line")
+    ap.add_argument("--workload", default=None, metavar="NAME",
+                    help="measure only this workload (one of the --configs names) and print its line; "
+                         "for profiling one workload alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel "
                          "that scales the HBM byte counters of a profiler run)")
@@ -930,6 +944,16 @@ def main():
     if args.draft > 0:
         print(json.dumps(draft_bench(dev, args.draft, settle=args.settle,
                                      cpu_s=0.0 if args.no_cpu_baseline else 3.0)), flush=True)
+        return
+    if args.workload:
+        if args.workload not in CONFIGS:
+            print(f"unknown workload {args.workload}; choose from {', '.join(CONFIGS)}", file=sys.stderr)
+            sys.exit(2)
+        copy_gbps = copy_bandwidth(dev)
+        print(f"[bench] workload {args.workload} alone", file=sys.stderr, flush=True)
+        wl = build_config(args.workload, dev, args.seed, headroom(args.warmup, args.steps, args.kernel_reps))
+        res = measure_config(wl, args.steps, args.warmup, args.settle, copy_gbps, not args.no_graph)
+        print(json.dumps({"workload": args.workload, **res}), flush=True)
         return
     room = headroom(args.warmup, args.steps, args.kernel_reps)
     copy_gbps = copy_bandwidth(dev)
@@ -973,7 +997,7 @@ def main():
         gbps = ob[op] / (us * 1e-6) / 1e9
         kernels[op] = {"us_per_call": us, "calls_per_step": per_step[op], "bytes_per_call": ob[op],
                        "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
-                       "timed": "per call in eager steps" if op in ("attn", "commit")
+                       "timed": "per call in eager steps" if op == "commit"
                        else "graph-replayed back-to-back batch"}
         if op in kb:
             kernels[op]["kernel_bytes_per_call"] = ob[op] + kb[op]
