@@ -155,17 +155,19 @@ struct Lds {
 };
 constexpr int NSTAGE = 4;  // LDS ring depth: NSTAGE - 1 tiles in flight
 
-// Q8 path: the 8-bit tiles land in their own 4-stage ring (K [32 tokens][D],
-// V [2 pages][D][16], then the tile's 32 K and 32 V scales), and one pass per
-// tile, between two workgroup barriers, turns the next tile into the fp16
-// stage layout above, in a 2-stage fp16 ring.
+// Q8 path: the 8-bit tiles land in their own ring (K [32 tokens][D], V [2
+// pages][D][16], then the tile's 32 K and 32 V scales), and one pass per
+// tile, between two workgroup barriers, turns the next tile's K and this
+// tile's V into the fp16 stage layout above, in one fp16 stage.
 template <int D>
 struct LdsQ8 {
   static constexpr int K_BYTES = TILE * D, V_BYTES = TILE * D, S_BYTES = 4 * TILE;
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + S_BYTES;
-  static constexpr int Q_STAGES = 4;   // 8-bit ring: up to three tiles in flight
-  static constexpr int FP_STAGES = 2;  // fp16 ring: K of the next tile, V of this one
-  static constexpr int FP_BYTES = FP_STAGES * Lds<D>::STAGE * 2;  // fp16 ring, bytes
+  // 8-bit ring: 96 KB of tiles in flight, as many bytes as the fp16 ring
+  // keeps in flight (6 tiles at D = 256, 12 at D = 128)
+  static constexpr int Q_STAGES = 1 + (96 * 1024) / (K_BYTES + V_BYTES);
+  // one fp16 stage: K of the next tile in its K half, V of this tile in its V half
+  static constexpr int FP_BYTES = Lds<D>::STAGE * 2;
   static constexpr int TOTAL = FP_BYTES + Q_STAGES * STAGE_BYTES;
 };
 
@@ -197,6 +199,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 // because direct-to-LDS loads write LDS), which empties the ring at every
 // tile and leaves one tile of lookahead instead of NSTAGE - 1.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most `later` tiles' direct loads (LPT per tile and wave) are
+// outstanding, later in [0, L]: s_waitcnt takes an immediate, so one case
+// per count, the deepest first.
+template <int LPT, int L>
+__device__ __forceinline__ void wait_vm_tiles(int later) {
+  if constexpr (L > 0) {
+    if (later >= L) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * LPT) : "memory");
+      return;
+    }
+    wait_vm_tiles<LPT, L - 1>(later);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
 
 template <int D, int NB, bool Q8>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
@@ -341,35 +359,42 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   // same rows, chunks and swizzles as a direct fp16 tile).  A value is
   // fp16(q * scale): q becomes fp16 exactly (0x6400 | (q + 128) is 1024 + q
   // + 128), and the product is rounded once, by the fp16 multiply.
-  auto convert_q8 = [&](int qstage, int fstage) {
+  // Q8: a staged 8-bit tile's K (conv_k) or V (conv_v) -> the fp16 stage, in
+  // the same rows, chunks and swizzles as a direct fp16 tile.  A value is
+  // fp16(q * scale): q becomes fp16 exactly (0x6400 | (q + 128) is 1024 + q
+  // + 128), and the product is rounded once, by the fp16 multiply.  Codes
+  // are read as a vector type (not HIP's uint2): the compiler then leaves the
+  // ring's direct-to-LDS loads in flight across the read.
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  auto dq8 = [](u32x2 q, half8 sc8) -> half8 {
+    const unsigned x0 = q.x ^ 0x80808080u, x1 = q.y ^ 0x80808080u;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 hb = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
+                      __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
+                      __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
+                      __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
+    const half8 v = __builtin_bit_cast(half8, hb) - (half8)(_Float16)1152.0f;
+    return v * sc8;
+  };
+  auto conv_k = [&](int qstage) {
     const char *St = qbase + qstage * LdsQ8<D>::STAGE_BYTES;
     const _Float16 *Sc = reinterpret_cast<const _Float16 *>(St + LdsQ8<D>::K_BYTES + LdsQ8<D>::V_BYTES);
-    _Float16 *Kf = lds + fstage * Lds<D>::STAGE;
-    _Float16 *Vf = Kf + Lds<D>::K_HALVES;
-    // codes are read as a vector type (not HIP's uint2): the compiler then
-    // leaves the ring's direct-to-LDS loads in flight across the read
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    auto dq8 = [](u32x2 q, half8 sc8) -> half8 {
-      const unsigned x0 = q.x ^ 0x80808080u, x1 = q.y ^ 0x80808080u;
-      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 hb = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
-                        __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
-                        __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
-                        __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
-      const half8 v = __builtin_bit_cast(half8, hb) - (half8)(_Float16)1152.0f;
-      return v * sc8;
-    };
 #pragma unroll
-    for (int k = 0; k < (TILE * CPR) / 256; ++k) {  // K: token tau, chunk cc
+    for (int k = 0; k < (TILE * CPR) / 256; ++k) {  // token tau, chunk cc
       const int idx = threadIdx.x + 256 * k, tau = idx / CPR, cc = idx % CPR;
       const u32x2 q = *reinterpret_cast<const u32x2 *>(St + tau * D + 8 * cc);
       const half8 v = dq8(q, (half8)Sc[tau]);
       const int r = krow_of(tau);
-      *reinterpret_cast<half8 *>(Kf + r * D + 8 * (cc ^ ksw(r))) = v;
+      *reinterpret_cast<half8 *>(lds + r * D + 8 * (cc ^ ksw(r))) = v;
     }
-    // V: thread idx writes slot idx & 1 of channel d of page half h, in the
-    // order of the fp16 stage (a 16-lane phase writes 256 contiguous bytes);
-    // the slot holds group q1 = slot ^ bit 3 of d, keys 8 q1 .. 8 q1 + 7
+  };
+  // V: thread idx writes slot idx & 1 of channel d of page half h, in the
+  // order of the fp16 stage (a 16-lane phase writes 256 contiguous bytes);
+  // the slot holds group q1 = slot ^ bit 3 of d, keys 8 q1 .. 8 q1 + 7
+  auto conv_v = [&](int qstage) {
+    const char *St = qbase + qstage * LdsQ8<D>::STAGE_BYTES;
+    const _Float16 *Sc = reinterpret_cast<const _Float16 *>(St + LdsQ8<D>::K_BYTES + LdsQ8<D>::V_BYTES);
+    _Float16 *Vf = lds + Lds<D>::K_HALVES;
 #pragma unroll
     for (int k = 0; k < (4 * D) / 256; ++k) {
       const int idx = threadIdx.x + 256 * k, h = idx / (2 * D), d = (idx >> 1) % D;
@@ -812,13 +837,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
         else
           main_loop(std::integral_constant<int, NB - 1>{});
       } else {
-        constexpr int QS = LdsQ8<D>::Q_STAGES, FS = LdsQ8<D>::FP_STAGES;
+        // K of tile t is converted in iteration t - 1 and its V in
+        // iteration t, so a tile's 8-bit stage is free once iteration t has
+        // passed its first barrier; up to QS - 2 tiles are in flight behind
+        // the one converted next
+        constexpr int QS = LdsQ8<D>::Q_STAGES;
+        auto wait_q8 = [&](int later) { wait_vm_tiles<LPT, QS - 2>(later); };
 #pragma unroll
         for (int t = 0; t < QS - 1; ++t)
           if (t < n_full) issue_q8(t, tile_page(t, 0), tile_page(t, 1));
-        wait_tiles(min(n_full, QS - 1) - 1);
+        wait_q8(min(n_full, QS - 1) - 1);  // tile 0 landed
         ring_barrier();
-        convert_q8(0, 0);
+        conv_k(0);
         ring_barrier();
         qk(0, Sn);
         fix_refs();
@@ -826,17 +856,17 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
           for (int it = 0; it < n_full; ++it) {
             const int nt = it + QS - 1;  // 8-bit tile issued in this iteration
             const int npg0 = nt < n_full ? tile_page(nt, 0) : 0, npg1 = nt < n_full ? tile_page(nt, 1) : 0;
-            if (it + 1 < n_full) wait_tiles(min(n_full, it + QS - 1) - (it + 2));
-            ring_barrier();  // tile it+1 landed; every wave is past tile it-1
-            // the next 8-bit tile goes out first (its stage held tile it - 1,
-            // converted two iterations ago)
+            if (it + 1 < n_full) wait_q8(min(n_full, it + QS - 1) - (it + 2));  // tile it + 1 landed
+            ring_barrier();  // ... for every wave; every wave is past tile it - 1
+            // the next 8-bit tile goes out first, into the stage of tile
+            // it - 1 (its V was converted in the last iteration)
             if (nt < n_full) issue_q8(nt % QS, npg0, npg1);
-            if (it + 1 < n_full) convert_q8((it + 1) % QS, (it + 1) % FS);  // into tile it-1's fp16 stage
+            if (it + 1 < n_full) conv_k((it + 1) % QS);
+            conv_v(it % QS);
             ring_barrier();
             f32x4 Sc[2][NB];
             copy_S(Sc);
-            tile_step_ahead(NBA_c, lds + ((it + 1) % FS) * Lds<D>::STAGE,
-                            lds + (it % FS) * Lds<D>::STAGE + Lds<D>::K_HALVES, Sc, Sn);
+            tile_step_ahead(NBA_c, lds, lds + Lds<D>::K_HALVES, Sc, Sn);
           }
         };
         if (blk_on[NB - 1])
