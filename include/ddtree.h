@@ -213,6 +213,10 @@ int ddt_tree_gdn(const ddt_plan *plan, const void *q, const void *k, const void 
  * context splits per (sequence, KV head), 0 = automatic.  A sequence whose
  * T[b] exceeds T_max or its page table is flagged DDT_ST_CTX and only its
  * first T_max tokens are read.
+ * Precision (matrix-core path): scores and value sums accumulate in fp32,
+ * probabilities enter the value product as fp16 (as the fp16 values do);
+ * each context split's output rows, divided by their own sums, pass through
+ * fp16 in the workspace (at most 2^-11 relative) before the fp32 merge.
  */
 size_t ddt_tree_attn_workspace(const ddt_plan *plan, int32_t Hq, int32_t Hkv, int32_t D,
                                int32_t T_max, int32_t n_splits);
