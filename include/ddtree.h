@@ -393,7 +393,8 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
  *   out       device [n_total][Hv][dv] fp32
  *   q_out, k_out device [n_total][Hk][dk] fp32 or NULL: the normalised q, k
  *             exactly as the kernel uses them (rounded to 16 significand
- *             bits, within 2^-16 of the normalised values); the commit's
+ *             bits, within 2^-16 of the normalised values plus one fp32 ulp
+ *             of the reciprocal square root); the commit's
  *             UPDATE needs k, REPLAY q, k and v
  *   v_out     device [n_total][Hv][dv] fp32 or NULL: v after SiLU
  *   node_states, node_u  as for ddt_tree_gdn (node_u: the saved u for UPDATE)

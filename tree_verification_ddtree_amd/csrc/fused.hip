@@ -113,9 +113,14 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
     if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(d + 4) = gf32x4{f[4], f[5], f[6], f[7]};
   };
   // every first-round global load is issued before any store (a store
-  // waits for its value, and for everything issued before it): x / prefix
-  // pieces, taps, window entries, then the committed rows and this thread's
-  // gates and mask, which are needed only after the conv
+  // waits for its value, and for everything issued before it): the
+  // committed rows first (their split into bf16 parts runs while the rest
+  // is on its way), then x / prefix pieces, taps, window entries, and this
+  // thread's gates and mask, which are needed only after the conv
+  const float *Srows = S_c + (((size_t)b * Hv + h) * dv + row0) * DK;
+  const bool s_wave = (tid >> 6) < (2 * n + 15) / 16;  // wavefronts that form committed-row products
+  SrowOperand<DK> So;
+  if (s_wave) So.load(Srows);
   gu32x4 r[NRR];
 #pragma unroll
   for (int u = 0; u < NRR; ++u) r[u] = ld16(row_src(min(pr + RPR * u, R - 1)));
@@ -133,13 +138,11 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
     const int e = min(tid + 256 * k, ne - 1), i = e / MW, j = e % MW;
     wr[k] = P.win[(size_t)(s.o + i) * W1w + min(max(j - 1, 0), W1w - 1)];
   }
-  const float *Srows = S_c + (((size_t)b * Hv + h) * dv + row0) * DK;
-  SrowOperand<DK> So;
-  if ((tid >> 6) < (2 * n + 15) / 16) So.load(Srows);
   auto anc_of = [&](int j) { return (P.anc[s.o + j] & ((2ull << j) - 1)) | (1ull << j); };
   const int jt = min(tid, n - 1);
   const float a0 = alpha[(size_t)(s.o + jt) * Hv + h], b0 = beta[(size_t)(s.o + jt) * Hv + h];
   const unsigned long long m0 = anc_of(jt);
+  if (s_wave) So.split();
   // ---- stores into the staging area
 #pragma unroll
   for (int u = 0; u < NRR; ++u)
@@ -180,10 +183,13 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
   }
   __syncthreads();
   // ---- the conv.  Task = 8 channels of one node.  Thread t owns q|k chunk
-  // t % QKC for nodes t / QKC + NG k, and (t < 2n) v chunk t % 2 of node t / 2.
+  // t % QKC for nodes t / QKC + NG k, and (vt = 255 - t < 2n) v chunk vt % 2
+  // of node vt / 2: the v tasks go to the last wavefronts, whose q|k tasks
+  // run out first when n is not a multiple of NG.
   constexpr int QKC = 2 * DK / 8;
   constexpr int NG = 256 / QKC;
-  const int qc = tid % QKC, ng = tid / QKC, vch = tid & 1, iv = min(tid >> 1, n - 1);
+  const int vt = 255 - tid;
+  const int qc = tid % QKC, ng = tid / QKC, vch = vt & 1, iv = min(vt >> 1, n - 1);
   float tq[MW][8], tvv[MW][8];
 #pragma unroll
   for (int j = 0; j < MW; ++j) {
@@ -216,8 +222,9 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
   // q and k rows: the DK / 8 lanes that hold one row (aligned groups of
   // adjacent lanes) add their squares, so every thread normalises its own
   // 8 values and stores them as packed bf16 pairs (hi + lo is the layer's q
-  // or k, within 2^-16 of the normalised value); the workgroup that hands
-  // q and k out writes hi + lo as fp32
+  // or k, within 2^-16 of the normalised value, plus the hardware reciprocal
+  // square root's one ulp); the workgroup that hands q and k out writes
+  // hi + lo as fp32
   {
     const int nk = (n + NG - 1) / NG;  // tasks of the busiest thread, the same in every thread
     const bool isk = qc >= DK / 8;
@@ -230,7 +237,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
       ss = group_sum<DK / 8>(ss);
-      const float inv = 1.0f / sqrtf(ss + FUSED_EPS);
+      const float inv = __builtin_amdgcn_rsqf(ss + FUSED_EPS);
       const gu32x4 p0 = pack_hilo4(gf32x4{y[0], y[1], y[2], y[3]} * inv);
       const gu32x4 p1 = pack_hilo4(gf32x4{y[4], y[5], y[6], y[7]} * inv);
       if (i < n) {
@@ -265,9 +272,13 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
     }
   }
   float yv[8];
-  conv8(iv, 2 * DK + 8 * vch, tvv, yv);
+  if (192 - 64 * (tid >> 6) < 2 * n) {  // this wavefront holds v tasks
+    conv8(iv, 2 * DK + 8 * vch, tvv, yv);
+    // computed before the barrier (the compiler would move it to the stores)
+    asm volatile("" ::"v"(yv[0]), "v"(yv[1]), "v"(yv[2]), "v"(yv[3]), "v"(yv[4]), "v"(yv[5]), "v"(yv[6]), "v"(yv[7]));
+  }
   __syncthreads();  // the x staging is dead from here on
-  if (tid < 2 * n) {
+  if (vt < 2 * n) {
     st8f(V.v + iv * GDN_R + 8 * vch, yv);
     if (v_out) st8f(v_out + ((size_t)(s.o + iv) * Hv + h) * dv + row0 + 8 * vch, yv);
   }

@@ -397,11 +397,13 @@ __device__ __forceinline__ void slice_hilo(const unsigned *row, int k0, gu32x4 (
 
 // Committed-row operand of the products for this lane (row i16, the
 // lane's k-share of every 32-wide step), split exactly into three bf16
-// parts; a caller can load it early and split it later.
+// parts; a caller loads it early and splits it while its other loads are
+// on their way.
 template <int DK>
 struct SrowOperand {
   static constexpr int NS = (DK + 31) / 32;
   gf32x4 x[NS][2];
+  gu32x4 sa[3][NS];  // the parts: hi, mid, lo
   __device__ __forceinline__ void load(const float *__restrict__ Srows) {
     const int lane = threadIdx.x & 63, i16 = lane & 15, kk = lane >> 4;
 #pragma unroll
@@ -411,6 +413,20 @@ struct SrowOperand {
       if (k0 < DK) {
         x[s][0] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0);
         x[s][1] = *reinterpret_cast<const gf32x4 *>(Srows + i16 * DK + k0 + 4);
+      }
+    }
+  }
+  // the split, made to happen where it is called (the compiler would
+  // otherwise move it to its first use, behind a workgroup barrier)
+  __device__ __forceinline__ void split() {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      gu32x4 t3[3];
+      split3(x[s][0], x[s][1], t3);
+#pragma unroll
+      for (int part = 0; part < 3; ++part) {
+        sa[part][s] = t3[part];
+        asm volatile("" ::"v"(sa[part][s]));
       }
     }
   }
@@ -444,14 +460,7 @@ __device__ void gdn_front_lds_rb(GdnView &V, int n, const unsigned *qn, const un
     }
   };
   if (wave >= ncb) return;
-  gu32x4 sa[3][NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    gu32x4 t3[3];
-    split3(S.x[s][0], S.x[s][1], t3);
-#pragma unroll
-    for (int part = 0; part < 3; ++part) sa[part][s] = t3[part];
-  }
+  const auto &sa = S.sa;
   for (int cb = wave; cb < ncb; cb += nw) {
     const int c = 16 * cb + i16;
     const bool con = c < 2 * n;
