@@ -20,10 +20,10 @@
 // staged in LDS, where it aliases the delta-net area that is only filled
 // afterwards.  A thread convolves 8 channels of a node at a time; the lanes
 // holding one q or k row add their squares, normalise, and store the row as
-// packed bf16 pairs hi | lo << 16 (hi + lo is the layer's q or k, within
-// 2^-16 of the normalised value and exact in fp32), which feed the
-// matrix-core products directly (gdn_front_lds); the rest is the delta-net
-// kernel's solve.  Sixteen workgroups share a key head and each computes its q and k
+// two bf16 planes hi and lo (hi + lo is the layer's q or k, within 2^-16 of
+// the normalised value and exact in fp32), which are the matrix-core
+// operands of the products as they stand (gdn_front_lds); the rest is the
+// delta-net kernel's solve.  Sixteen workgroups share a key head and each computes its q and k
 // itself: 2*dk*(n + W-1) extra reads from L2 per workgroup instead of a
 // second launch.
 #include "gdn_wy.h"
@@ -34,21 +34,21 @@ constexpr float FUSED_EPS = 1e-6f;
 
 // LDS carve-up (bytes): the delta-net area first, with the prologue's
 // staging aliasing it (prefix and node rows [W_max - 1 + nmax][2 dk + 16]
-// and the taps [W_max][2 dk + 16], fp32); then q and k rows
-// [nmax][dk + 4] fp32 (4 floats of padding keep the operand reads of 16
-// rows on distinct banks) and the conv windows as staged rows [nmax][W_max].
+// and the taps [W_max][2 dk + 16], fp32); then the q and k rows as four
+// bf16 planes q hi, q lo, k hi, k lo [nmax][dk + 8] (8 elements of padding
+// keep the operand reads of 16 rows on distinct banks) and the conv
+// windows as staged rows [nmax][W_max].
 struct FusedLds {
   GdnLds g;
-  int ldk, xw;
-  size_t qn, kn, win, total;
+  int ldh, xw;
+  size_t qk, win, total;
   __host__ __device__ FusedLds(int nmax, int dk) : g(nmax) {
     auto up = [](size_t x) { return (x + 15) / 16 * 16; };
-    ldk = dk + 4;
+    ldh = dk + 8;
     xw = 2 * dk + GDN_R;
     const size_t xs_bytes = (size_t)(nmax + 2 * DDT_MAX_W - 1) * xw * 4;  // staged rows + tap rows
-    qn = up(g.total > xs_bytes ? g.total : xs_bytes);
-    kn = up(qn + (size_t)nmax * ldk * 4);
-    win = up(kn + (size_t)nmax * ldk * 4);
+    qk = up(g.total > xs_bytes ? g.total : xs_bytes);
+    win = up(qk + (size_t)4 * nmax * ldh * 2);
     total = up(win + (size_t)nmax * DDT_MAX_W * 4);
   }
 };
@@ -73,10 +73,11 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
   const FusedLds FL(P.n_max, DK);
   GdnView V(base, FL.g, P.n_max);
   float *xs = reinterpret_cast<float *>(base);  // prologue only
-  float *qn = reinterpret_cast<float *>(base + FL.qn);  // raw fp32, then packed bf16 pairs in place
-  float *kn = reinterpret_cast<float *>(base + FL.kn);
+  uint16_t *qk = reinterpret_cast<uint16_t *>(base + FL.qk);  // planes q hi, q lo, k hi, k lo
+  const int ldh = FL.ldh;
+  const size_t plane = (size_t)P.n_max * ldh;
+  const QkPlanes Q{qk, qk + plane, qk + 2 * plane, qk + 3 * plane, ldh};
   int *wins = reinterpret_cast<int *>(base + FL.win);
-  const int ldk = FL.ldk;
   const int b = blockIdx.z, h = blockIdx.y, row0 = blockIdx.x * GDN_R;
   const int tid = threadIdx.x;
   const Seq s = seq_of(P, b);
@@ -221,15 +222,15 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
   };
   // q and k rows: the DK / 8 lanes that hold one row (aligned groups of
   // adjacent lanes) add their squares, so every thread normalises its own
-  // 8 values and stores them as packed bf16 pairs (hi + lo is the layer's q
-  // or k, within 2^-16 of the normalised value, plus the hardware reciprocal
-  // square root's one ulp); the workgroup that hands q and k out writes
-  // hi + lo as fp32
+  // 8 values and stores their bf16 parts hi and lo in the planes (hi + lo is
+  // the layer's q or k, within 2^-16 of the normalised value, plus the
+  // hardware reciprocal square root's one ulp); the workgroup that hands q
+  // and k out writes hi + lo as fp32
   {
     const int nk = (n + NG - 1) / NG;  // tasks of the busiest thread, the same in every thread
     const bool isk = qc >= DK / 8;
     const int c0 = 8 * (isk ? qc - DK / 8 : qc);
-    float *dst = (isk ? kn : qn) + c0;
+    uint16_t *dh = const_cast<uint16_t *>(isk ? Q.kh : Q.qh) + c0, *dl = const_cast<uint16_t *>(isk ? Q.kl : Q.ql) + c0;
     float *ho = isk ? k_out : q_out;
     const bool hand = ho && blockIdx.x == 0 && h % (Hv / Hk) == 0;
     auto finish = [&](int i, const float (&y)[8]) {
@@ -238,17 +239,20 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
       for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
       ss = group_sum<DK / 8>(ss);
       const float inv = __builtin_amdgcn_rsqf(ss + FUSED_EPS);
-      const gu32x4 p0 = pack_hilo4(gf32x4{y[0], y[1], y[2], y[3]} * inv);
-      const gu32x4 p1 = pack_hilo4(gf32x4{y[4], y[5], y[6], y[7]} * inv);
+      float yn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yn[e] = y[e] * inv;
+      gu32x4 hi, lo;
+      split_hilo8(yn, hi, lo);
       if (i < n) {
-        *reinterpret_cast<gu32x4 *>(dst + i * ldk) = p0;
-        *reinterpret_cast<gu32x4 *>(dst + i * ldk + 4) = p1;
+        *reinterpret_cast<gu32x4 *>(dh + i * ldh) = hi;
+        *reinterpret_cast<gu32x4 *>(dl + i * ldh) = lo;
         if (hand) {
           float *o = ho + ((size_t)(s.o + i) * Hk + g) * DK + c0;
           *reinterpret_cast<gf32x4 *>(o) =
-              gf32x4{unpack_hilo(p0[0]), unpack_hilo(p0[1]), unpack_hilo(p0[2]), unpack_hilo(p0[3])};
+              gf32x4{hilo_value(hi, lo, 0), hilo_value(hi, lo, 1), hilo_value(hi, lo, 2), hilo_value(hi, lo, 3)};
           *reinterpret_cast<gf32x4 *>(o + 4) =
-              gf32x4{unpack_hilo(p1[0]), unpack_hilo(p1[1]), unpack_hilo(p1[2]), unpack_hilo(p1[3])};
+              gf32x4{hilo_value(hi, lo, 4), hilo_value(hi, lo, 5), hilo_value(hi, lo, 6), hilo_value(hi, lo, 7)};
         }
       }
     };
@@ -283,8 +287,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
     if (v_out) st8f(v_out + ((size_t)(s.o + iv) * Hv + h) * dv + row0 + 8 * vch, yv);
   }
   // (the front reads only the q and k rows; the barrier after it orders V.v)
-  const unsigned *qp = reinterpret_cast<const unsigned *>(qn), *kp = reinterpret_cast<const unsigned *>(kn);
-  gdn_front_lds<DK>(V, n, qp, kp, ldk, So, a0, b0, m0);
+  gdn_front_lds<DK>(V, n, Q, So, a0, b0, m0);
   __syncthreads();
   const int nlev = gdn_nlev(n, (tid & 63) < n ? V.anc[tid & 63] : 0ull);
   gdn_scalar<true>(V, n, nlev, scale);
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(ddt_plan P, const T *__re
   }
   if (node_states && tid < GDN_R * LPR) {
     const int lr = tid / LPR, c0 = (tid % LPR) * 8;
-    auto krow = [&](int a) { return PackedRow{kp + a * ldk}; };
+    auto krow = [&](int a) { return PlaneRow{Q.kh + a * ldh, Q.kl + a * ldh}; };
     for (int i = 0; i < n; ++i) {
       float st[8];
       gdn_state(V, i, lr, c0, Srows + lr * DK, krow, st);

@@ -349,50 +349,38 @@ __device__ void gdn_front(GdnView &V, int n, Gid gid, Anc anc_of, const T *__res
     gdn_front_rb<T, DK, 4>(V, n, gid, anc_of, q, k, v, alpha, beta, Srows, Hk, Hv, dv, g, h, row0);
 }
 
-// Packed words of two bf16 parts, hi | lo << 16, each rounded to nearest
-// even (x - hi is exact in fp32): hi + lo keeps 16 significand bits,
-// |x - (hi + lo)| <= 2^-16 |x|, and hi + lo is exact in fp32.
-// four values at once, with the packed fp32 -> bf16 conversion
+// The two bf16 parts of 8 fp32 values x: hi is x rounded to bf16 (nearest
+// even), lo the rounding of x - hi (exact in fp32).  hi + lo keeps 16
+// significand bits, |x - (hi + lo)| <= 2^-16 |x|, and hi + lo is exact in
+// fp32.  Each part comes as 8 bf16 in order (16 bytes), the layout of a
+// matrix-core operand slice; the packed fp32 -> bf16 conversion does two
+// values at once.
 typedef __bf16 gbf16x2 __attribute__((ext_vector_type(2)));
 typedef float gf32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ gu32x4 pack_hilo4(gf32x4 v) {
-  const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector((gf32x2){v[0], v[1]}, gbf16x2));
-  const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector((gf32x2){v[2], v[3]}, gbf16x2));
-  const gf32x2 r01 = {v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u)};
-  const gf32x2 r23 = {v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u)};
-  const unsigned l01 = __builtin_bit_cast(unsigned, __builtin_convertvector(r01, gbf16x2));
-  const unsigned l23 = __builtin_bit_cast(unsigned, __builtin_convertvector(r23, gbf16x2));
-  return gu32x4{__builtin_amdgcn_perm(l01, h01, 0x05040100u), __builtin_amdgcn_perm(l01, h01, 0x07060302u),
-                __builtin_amdgcn_perm(l23, h23, 0x05040100u), __builtin_amdgcn_perm(l23, h23, 0x07060302u)};
-}
-__device__ __forceinline__ float unpack_hilo(unsigned w) {
-  return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
-}
-// A row of packed words read as fp32 values hi + lo (for gdn_state).
-struct PackedRow {
-  const unsigned *p;
-  __device__ PackedRow operator+(int c) const { return {p + c}; }
-};
-__device__ __forceinline__ void load8(PackedRow r, float *f) {
-  const gu32x4 a = *reinterpret_cast<const gu32x4 *>(r.p), b = *reinterpret_cast<const gu32x4 *>(r.p + 4);
+__device__ __forceinline__ void split_hilo8(const float (&v)[8], gu32x4 &hi, gu32x4 &lo) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = unpack_hilo(a[e]);
-    f[e + 4] = unpack_hilo(b[e]);
+  for (int p = 0; p < 4; ++p) {
+    const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector((gf32x2){v[2 * p], v[2 * p + 1]}, gbf16x2));
+    const gf32x2 r = {v[2 * p] - __uint_as_float(h << 16), v[2 * p + 1] - __uint_as_float(h & 0xffff0000u)};
+    hi[p] = h;
+    lo[p] = __builtin_bit_cast(unsigned, __builtin_convertvector(r, gbf16x2));
   }
 }
-// 8 packed words at row + k0 -> the matrix-core operands of their hi and lo
-// parts (8 bf16 each)
-__device__ __forceinline__ void slice_hilo(const unsigned *row, int k0, gu32x4 (&o)[2]) {
-  const gu32x4 a = *reinterpret_cast<const gu32x4 *>(row + k0), b = *reinterpret_cast<const gu32x4 *>(row + k0 + 4);
-  o[0][0] = __builtin_amdgcn_perm(a[1], a[0], 0x05040100u);
-  o[0][1] = __builtin_amdgcn_perm(a[3], a[2], 0x05040100u);
-  o[0][2] = __builtin_amdgcn_perm(b[1], b[0], 0x05040100u);
-  o[0][3] = __builtin_amdgcn_perm(b[3], b[2], 0x05040100u);
-  o[1][0] = __builtin_amdgcn_perm(a[1], a[0], 0x07060302u);
-  o[1][1] = __builtin_amdgcn_perm(a[3], a[2], 0x07060302u);
-  o[1][2] = __builtin_amdgcn_perm(b[1], b[0], 0x07060302u);
-  o[1][3] = __builtin_amdgcn_perm(b[3], b[2], 0x07060302u);
+// hi + lo of element e of such a pair
+__device__ __forceinline__ float hilo_value(const gu32x4 &hi, const gu32x4 &lo, int e) {
+  const unsigned hw = hi[e >> 1], lw = lo[e >> 1];
+  return (e & 1) ? __uint_as_float(hw & 0xffff0000u) + __uint_as_float(lw & 0xffff0000u)
+                 : __uint_as_float(hw << 16) + __uint_as_float(lw << 16);
+}
+// A row held as hi and lo planes, read as fp32 values hi + lo (gdn_state).
+struct PlaneRow {
+  const uint16_t *h, *l;
+  __device__ PlaneRow operator+(int c) const { return {h + c, l + c}; }
+};
+__device__ __forceinline__ void load8(PlaneRow r, float *f) {
+  const gu32x4 a = *reinterpret_cast<const gu32x4 *>(r.h), b = *reinterpret_cast<const gu32x4 *>(r.l);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = hilo_value(a, b, e);
 }
 
 // Committed-row operand of the products for this lane (row i16, the
@@ -432,56 +420,54 @@ struct SrowOperand {
   }
 };
 
+// q and k rows of the fused layer in LDS: hi and lo planes of bf16 (node
+// j's row of each at j * ld), whose values hi + lo are the layer's q and k.
+struct QkPlanes {
+  const uint16_t *qh, *ql, *kh, *kl;
+  int ld;
+};
+
 // gdn_front for q and k that the workgroup computed itself (the fused
-// layer): they are rows of packed bf16 pairs in LDS (pack_hilo; node j's
-// row at qn + j * ldk, kn + j * ldk), whose values hi + lo are the q and k
-// of the layer; the tile's v rows are already in V.v, and this thread's
+// layer): matrix operands are read straight from the planes (16 bytes per
+// slice and part); the tile's v rows are already in V.v, and this thread's
 // gates and mask (node tid, n <= blockDim) and its committed-row operand
-// were loaded by the caller.  Same products and LDS outputs as gdn_front;
-// the committed rows are split into their three exact parts.  D and F sum
-// the part products (row, column) lo*hi, mid*hi, hi*lo, hi*hi and the key
-// products lo*hi, hi*lo, hi*hi: every dropped term stays below about 2^-15
-// of |row| |column|.
+// were loaded (and split) by the caller.  Same products and LDS outputs as
+// gdn_front.  D and F sum the part products (row, column) lo*hi, mid*hi,
+// hi*lo, hi*hi and the key products lo*hi, hi*lo, hi*hi: every dropped term
+// stays below about 2^-15 of |row| |column|.  Rows and columns past the
+// tree read the last node, so their products are finite, and they are
+// never stored.
 template <int DK, int NRB>
-__device__ void gdn_front_lds_rb(GdnView &V, int n, const unsigned *qn, const unsigned *kn, int ldk,
-                                 const SrowOperand<DK> &S) {
+__device__ void gdn_front_lds_rb(GdnView &V, int n, const QkPlanes &Q, const SrowOperand<DK> &S) {
   constexpr int NS = SrowOperand<DK>::NS;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = nth >> 6;
   const int lane = tid & 63, i16 = lane & 15, kk = lane >> 4;
   const int ncb = (2 * n + 15) / 16;
   const gu32x4 z = {0u, 0u, 0u, 0u};
-  auto slice2 = [&](const unsigned *row, int k0, gu32x4 (&o)[2]) {
-    if (k0 < DK) {
-      slice_hilo(row, k0, o);
+  // hi and lo operand slices of row `row` of planes (h, l), channels k0 .. k0 + 7
+  auto slice = [&](const uint16_t *h, const uint16_t *l, int row, int k0, gu32x4 (&o)[2]) {
+    if (DK >= 32 || k0 < DK) {
+      o[0] = *reinterpret_cast<const gu32x4 *>(h + row * Q.ld + k0);
+      o[1] = *reinterpret_cast<const gu32x4 *>(l + row * Q.ld + k0);
     } else {
-      o[0] = z;
-      o[1] = z;
+      o[0] = o[1] = z;
     }
   };
   if (wave >= ncb) return;
   const auto &sa = S.sa;
   for (int cb = wave; cb < ncb; cb += nw) {
     const int c = 16 * cb + i16;
-    const bool con = c < 2 * n;
     const int cn = min(c, 2 * n - 1) >> 1;
-    const unsigned *brow = ((c & 1) ? qn : kn) + cn * ldk;
+    const bool isq = c & 1;
     // every operand read of the column block before any product is stored
     gu32x4 bv[NS][2], ka[NRB][NS][2];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      slice2(brow, 32 * s + 8 * kk, bv[s]);
-      if (!con) bv[s][0] = bv[s][1] = z;
-    }
+    for (int s = 0; s < NS; ++s) slice(isq ? Q.qh : Q.kh, isq ? Q.ql : Q.kl, cn, 32 * s + 8 * kk, bv[s]);
 #pragma unroll
-    for (int m = 0; m < NRB; ++m) {
-      const int a = 16 * m + i16;
+    for (int m = 0; m < NRB; ++m)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        slice2(kn + min(a, n - 1) * ldk, 32 * s + 8 * kk, ka[m][s]);
-        if (a >= n) ka[m][s][0] = ka[m][s][1] = z;
-      }
-    }
+      for (int s = 0; s < NS; ++s) slice(Q.kh, Q.kl, min(16 * m + i16, n - 1), 32 * s + 8 * kk, ka[m][s]);
     gf32x4 acc = {0.f, 0.f, 0.f, 0.f}, g4[NRB];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -507,9 +493,9 @@ __device__ void gdn_front_lds_rb(GdnView &V, int n, const unsigned *qn, const un
                                                         __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
       }
     }
-    if (con) {
+    if (c < 2 * n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
+      for (int e = 0; e < 4; ++e) (isq ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
 #pragma unroll
       for (int m = 0; m < NRB; ++m)
 #pragma unroll
@@ -524,15 +510,15 @@ __device__ void gdn_front_lds_rb(GdnView &V, int n, const unsigned *qn, const un
 // The row-block count (16 nodes each) picks the instantiation, so that all
 // of a column block's operand reads are unconditional and issue together.
 template <int DK>
-__device__ void gdn_front_lds(GdnView &V, int n, const unsigned *qn, const unsigned *kn, int ldk,
-                              const SrowOperand<DK> &S, float a0, float b0, unsigned long long m0) {
+__device__ void gdn_front_lds(GdnView &V, int n, const QkPlanes &Q, const SrowOperand<DK> &S, float a0, float b0,
+                              unsigned long long m0) {
   const int nrb = (n + 15) / 16;
   if (nrb <= 1)
-    gdn_front_lds_rb<DK, 1>(V, n, qn, kn, ldk, S);
+    gdn_front_lds_rb<DK, 1>(V, n, Q, S);
   else if (nrb <= 2)
-    gdn_front_lds_rb<DK, 2>(V, n, qn, kn, ldk, S);
+    gdn_front_lds_rb<DK, 2>(V, n, Q, S);
   else
-    gdn_front_lds_rb<DK, DDT_MAX_NODES / 16>(V, n, qn, kn, ldk, S);
+    gdn_front_lds_rb<DK, DDT_MAX_NODES / 16>(V, n, Q, S);
   const int tid = threadIdx.x;
   if (tid < n) {
     V.al[tid] = a0;
@@ -541,14 +527,18 @@ __device__ void gdn_front_lds(GdnView &V, int n, const unsigned *qn, const unsig
   }
 }
 
-// Levels of a tree (max depth + 1) from the masks, by one wavefront; the
-// result is the same in every lane.
+// The depth class of a tree from the masks (lane j < n holds node j's),
+// the same in every lane: 4, 8 or GDN_PATH when every node's level count
+// (its mask's popcount) fits, else 64.  The solve only compares the level
+// count with those bounds, and three ballots decide that without the
+// cross-lane round trips of a maximum.
 __device__ __forceinline__ int gdn_nlev(int n, unsigned long long a) {
   const int lane = threadIdx.x & 63;
-  int d = lane < n ? __popcll(a) : 0;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) d = max(d, __shfl_xor(d, o));
-  return d;
+  const int d = lane < n ? __popcll(a) : 0;
+  if (__ballot(d > GDN_PATH)) return 64;
+  if (__ballot(d > 8)) return GDN_PATH;
+  if (__ballot(d > 4)) return 8;
+  return 4;
 }
 
 // ------------------------------------------------------------ register path solve
@@ -808,8 +798,9 @@ __device__ void gdn_level_solve(GdnView &V, int n, float scale) {
 }
 
 // The whole scalar part after the products, called by every thread of a
-// 256-thread workgroup after a barrier that follows gdn_front.  `nlev`
-// (levels of the tree) must be the same in every thread.
+// 256-thread workgroup after a barrier that follows gdn_front.  `nlev` (a
+// bound on the tree's levels, such as gdn_nlev's class) must be the same in
+// every thread.
 template <bool WANT_O>
 __device__ void gdn_scalar(GdnView &V, int n, int nlev, float scale) {
   if (nlev <= 4) {
