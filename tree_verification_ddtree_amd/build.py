@@ -21,6 +21,9 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
     # packed fp32 math off (v_pk_*_f32): only plain fp32 VALU ops are emitted
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 argument dwords of a kernel (scalars and pointers only)
+    # arrive preloaded in scalar registers instead of being fetched
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -17,11 +17,17 @@ namespace ddt {
 // and issued together; the window gather then reads the x slice from LDS.
 constexpr int CS = 64;
 
+// The plan's sizes and the pointers come first among the arguments, so that
+// they arrive preloaded in scalar registers (see fused_kernel).
 template <typename T, int W>
-__global__ __launch_bounds__(256) void conv_kernel(ddt_plan P, const T *__restrict__ x,
-                                                   const T *__restrict__ prefix,
-                                                   const T *__restrict__ w, int C, int act,
-                                                   float *__restrict__ y) {
+__global__ __launch_bounds__(256) void conv_kernel(int plan_B, int plan_n_total, int plan_n_max,
+                                                   const T *__restrict__ x, const T *__restrict__ prefix,
+                                                   const T *__restrict__ w, float *__restrict__ y, int C, int act,
+                                                   ddt_plan P) {
+  P.B = plan_B;
+  P.n_total = plan_n_total;
+  P.n_max = plan_n_max;
+  asm volatile("" ::"s"(C), "s"(act), "s"(P.win));  // fetched now, in one round
   constexpr int W1 = W - 1;
   __shared__ float4 xs4[DDT_MAX_NODES * CS / 4];  // [node][CS] fp32
   float *xs = reinterpret_cast<float *>(xs4);
@@ -121,12 +127,13 @@ extern "C" int ddt_tree_conv(const ddt_plan *P, const void *x, const void *prefi
 #define DDT_CONV(WW)                                                                              \
   do {                                                                                            \
     if (dtype == DDT_BF16)                                                                        \
-      hipLaunchKernelGGL((conv_kernel<uint16_t, WW>), grid, dim3(256), 0, st, *P,                 \
-                         (const uint16_t *)x, (const uint16_t *)prefix, (const uint16_t *)w, C,   \
-                         act, y);                                                                 \
+      hipLaunchKernelGGL((conv_kernel<uint16_t, WW>), grid, dim3(256), 0, st, P->B, P->n_total,   \
+                         P->n_max, (const uint16_t *)x, (const uint16_t *)prefix, (const uint16_t *)w, \
+                         y, C, act, *P);                                                          \
     else                                                                                          \
-      hipLaunchKernelGGL((conv_kernel<float, WW>), grid, dim3(256), 0, st, *P, (const float *)x,  \
-                         (const float *)prefix, (const float *)w, C, act, y);                     \
+      hipLaunchKernelGGL((conv_kernel<float, WW>), grid, dim3(256), 0, st, P->B, P->n_total,      \
+                         P->n_max, (const float *)x, (const float *)prefix, (const float *)w, y, C,   \
+                         act, *P);                                                                \
   } while (0)
   switch (P->W) {
     case 1: DDT_CONV(1); break;

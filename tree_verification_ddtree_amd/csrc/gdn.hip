@@ -20,17 +20,23 @@
 
 namespace ddt {
 
+// The plan's sizes and the first pointers come first among the arguments,
+// so that they arrive preloaded in scalar registers (see fused_kernel).
 template <typename T, int DK>
-__global__ __launch_bounds__(256, 1) void gdn_kernel(ddt_plan P, const T *__restrict__ q,
-                                                     const T *__restrict__ k,
-                                                     const T *__restrict__ v,
-                                                     const T *__restrict__ alpha,
-                                                     const T *__restrict__ beta,
-                                                     const float *__restrict__ S_c, int Hk,
-                                                     int Hv, int dv, float scale,
+__global__ __launch_bounds__(256, 1) void gdn_kernel(int plan_B, int plan_n_total, int plan_n_max,
+                                                     const float *__restrict__ S_c, const T *__restrict__ q,
+                                                     const T *__restrict__ k, const T *__restrict__ v,
+                                                     const T *__restrict__ alpha, const T *__restrict__ beta,
+                                                     ddt_plan P, int Hk, int Hv, int dv, float scale,
                                                      float *__restrict__ out,
                                                      float *__restrict__ node_states,
                                                      float *__restrict__ node_u) {
+  P.B = plan_B;
+  P.n_total = plan_n_total;
+  P.n_max = plan_n_max;
+  // every other argument fetched now, in one round
+  asm volatile("" ::"s"(P.anc), "s"(Hk), "s"(Hv), "s"(dv), "s"(scale), "s"(out), "s"(node_states),
+               "s"(node_u));
   constexpr int LPR = DK / 8;  // lanes per state row when storing states
   extern __shared__ float4 lds4[];
   const GdnLds L(P.n_max);
@@ -79,9 +85,9 @@ static void launch_gdn(int dk, dim3 grid, size_t lds, hipStream_t st, const ddt_
   do {                                                                                          \
     (void)hipFuncSetAttribute((const void *)gdn_kernel<T, D>,                                   \
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);            \
-    hipLaunchKernelGGL((gdn_kernel<T, D>), grid, dim3(256), lds, st, P, (const T *)q,          \
-                       (const T *)k, (const T *)v, (const T *)al, (const T *)be, S, Hk, Hv, dv, \
-                       scale, out, ns, nu);                                                     \
+    hipLaunchKernelGGL((gdn_kernel<T, D>), grid, dim3(256), lds, st, P.B, P.n_total, P.n_max, S,      \
+                       (const T *)q, (const T *)k, (const T *)v, (const T *)al, (const T *)be, P, Hk,  \
+                       Hv, dv, scale, out, ns, nu);                                                    \
   } while (0)
   switch (dk) {
     case 16: DDT_GDN(16); break;
