@@ -188,6 +188,7 @@ class Workload:
         self.L = torch.empty(B, **i32)
         self.bonus = torch.empty(B, **i32)
         self.timer = None  # {op: [(start, end) events]} while timing eager steps
+        self.fused_step = False  # steps run each conv + delta-net pair as one fused call (setup_fused)
 
     # ------------------------------------------------------------------ step
     def _timed(self, name, fn):
@@ -232,9 +233,12 @@ class Workload:
                                    c["Hk"], c["dk"], 1.0, self.gdn_out[l], k_out=f["k"],
                                    node_u=self.gdn_u[l], stream=stream)
 
-    def step(self, ci=0, stream=None, fused=False):
+    def step(self, ci=0, stream=None, fused=None):
         """One verify step on copy ci of the inputs (fused: each conv +
-        delta-net pair as one fused layer call; copy 0 only)."""
+        delta-net pair as one fused layer call; copy 0 only; None: the
+        workload's own choice, fused_step)."""
+        if fused is None:
+            fused = self.fused_step
         ddt, c, cp = self.ddt, self.c, self.copy[ci]
         gdt = {"bf16": ddt.DDT_BF16, "f32": ddt.DDT_F32}[self.gdt]
         self._timed("plan", lambda: ddt.ddt_tree_plan(self.tb, c["levels"], stream))
@@ -285,7 +289,10 @@ class Workload:
         attn = [lambda at=at, kv=kv, o=o: ddt.ddt_tree_attn(self.tb, at["q"], kv[0], kv[1], self.pt, self.T,
                                                             self.T_max, at["Kt"], at["Vt"], o, self.attn_ws)
                 for at, kv, o in zip(cp.get("attn", []), cp.get("kv", []), cp.get("attn_out", []))]
-        return {"plan": plan, "conv": conv, "gdn": gdn, "walk": walk, "attn": attn}
+        out = {"plan": plan, "conv": conv, "gdn": gdn, "walk": walk, "attn": attn}
+        if hasattr(self, "fz"):
+            out["fused"] = [lambda l=l: self.fused_call(l) for l in range(self.n_gdn)]
+        return out
 
     # ---------------------------------------------------------------- bytes
     def _e(self, which):
@@ -304,7 +311,7 @@ class Workload:
         eg, ea, el = self._e("g"), self._e("a"), self._e("l")
         W1 = c["W"] - 1
         out = {"plan": n * 4 + (B + 1) * 4 + n * (4 + 8 + 4 * max(W1, 1)) + B * 4,
-               "conv": 0, "gdn": 0, "attn": 0,
+               "conv": 0, "gdn": 0, "fused": 0, "attn": 0,
                "walk": n * synth.VOCAB * el + n * 4 + n * 4 + B * (self.tb.n_max * 4 + 8), "commit": 0}
         if self.n_gdn:
             state = c["Hv"] * c["dv"] * c["dk"] * 4
@@ -312,6 +319,9 @@ class Workload:
             out["gdn"] = (B * state + n * c["Hk"] * c["dk"] * eg * 2 + n * c["Hv"] * c["dv"] * eg
                           + n * c["Hv"] * eg * 2 + n * c["Hv"] * c["dv"] * 4)
             out["commit"] += self.n_gdn * B * (state + W1 * c["C"] * eg)
+            # the fused layer: x, prefix and taps in, gates (fp32) and state in, o out
+            out["fused"] = (n * c["C"] * eg + B * W1 * c["C"] * eg + c["C"] * c["W"] * eg + B * state
+                            + n * c["Hv"] * 4 * 2 + n * c["Hv"] * c["dv"] * 4)
         if self.n_attn:
             out["attn"] = (float(T.sum()) * c["Hkv"] * c["D"] * ea * 2 + n * c["Hq"] * c["D"] * ea
                            + n * c["Hkv"] * c["D"] * ea * 2 + n * c["Hq"] * c["D"] * 4)
@@ -328,16 +338,19 @@ class Workload:
         gates of the accepted path."""
         c, n, B = self.c, self.n, self.B
         if not self.n_gdn:
-            return {"gdn": 0, "commit": 0}
+            return {"gdn": 0, "fused": 0, "commit": 0}
         Ls = float(np.atleast_1d(np.asarray(L, dtype=np.float64)).sum())
         eg = self._e("g")
+        ek = 4 if self.fused_step else eg  # the keys the commit reads: the fused layer hands out fp32
         state = c["Hv"] * c["dv"] * c["dk"] * 4
         return {"gdn": n * c["Hv"] * c["dv"] * 4,
-                "commit": self.n_gdn * (B * state + Ls * (c["Hv"] * c["dv"] * 4 + c["Hk"] * c["dk"] * eg
+                "fused": n * c["Hv"] * c["dv"] * 4 + n * c["Hk"] * c["dk"] * 4,
+                "commit": self.n_gdn * (B * state + Ls * (c["Hv"] * c["dv"] * 4 + c["Hk"] * c["dk"] * ek
                                                          + c["Hv"] * eg))}
 
     def calls(self):
-        return {"plan": 1, "conv": self.n_gdn, "gdn": self.n_gdn, "attn": self.n_attn, "walk": 1, "commit": 1}
+        g, f = (0, self.n_gdn) if self.fused_step else (self.n_gdn, 0)
+        return {"plan": 1, "conv": g, "gdn": g, "fused": f, "attn": self.n_attn, "walk": 1, "commit": 1}
 
     def step_bytes(self, T, L):
         """Algorithmic HBM bytes of one step (the sum over its calls)."""
@@ -406,7 +419,7 @@ def build_config(name, device, seed, room_steps):
 
 
 # ------------------------------------------------------------------ timing
-def capture(wl, fused=False):
+def capture(wl, fused=None):
     """One HIP graph of one step per copy (after one eager round)."""
     import torch
     for ci in range(wl.ncopies):
@@ -422,7 +435,7 @@ def capture(wl, fused=False):
     return g
 
 
-def run_steps(wl, graph, k, fused=False):
+def run_steps(wl, graph, k, fused=None):
     for _ in range(k):
         if graph is not None:
             graph.replay()
@@ -431,7 +444,7 @@ def run_steps(wl, graph, k, fused=False):
                 wl.step(ci, fused=fused)
 
 
-def settle(wl, graph, seconds, fused=False):
+def settle(wl, graph, seconds, fused=None):
     """Untimed replays for `seconds` (the clock ramps under load), with the
     committed length put back after every batch; returns the steps run."""
     import torch
@@ -451,7 +464,7 @@ def check_status(wl):
         raise RuntimeError(f"{wl.name}: device status {st}")
 
 
-def time_total(wl, graph, k, fused=False):
+def time_total(wl, graph, k, fused=None):
     """k replays under one event pair, from the configured context: ms per
     step, the per-sequence mean accepted length, and the host wall time."""
     import torch
@@ -473,7 +486,7 @@ def time_total(wl, graph, k, fused=False):
     return e0.elapsed_time(e1) / steps, L, wall
 
 
-def time_each(wl, graph, k, fused=False):
+def time_each(wl, graph, k, fused=None):
     """k replays, each under its own event pair: per-step times (a replay of
     a graph of several copies counts as that many steps)."""
     import torch
@@ -608,42 +621,22 @@ def draft_bench(device, B, reps=5, calls=20, settle=0.3, cpu_s=0.0):
     return out
 
 
-def fused_stack_bench(st, steps, settle_s, reps=5):
-    """The same 128K step with each conv + delta-net pair replaced by one
-    fused ddt_tree_conv_gdn call (48 launches fewer), timed like the step:
-    eager round, one captured graph, settle replays with the committed
-    length put back, then `steps` timed replays from the configured context.
-    The fused call alone is timed as a graph-replayed batch of the 48
-    layers."""
-    import torch
-    st.setup_fused()
-    graph = capture(st, fused=True)
-    settle(st, graph, settle_s, fused=True)
-    ms, _, _ = time_total(st, graph, steps, fused=True)
-    each = time_each(st, graph, steps, fused=True)
+def unfused_stack_bench(st, steps, settle_s):
+    """The same 128K step with each linear-attention layer as two launches,
+    ddt_tree_conv then ddt_tree_gdn (on the layer's own bf16 q, k, v), timed
+    like the headline step: eager round, one captured graph, settle replays
+    with the committed length put back, then `steps` timed replays from the
+    configured context."""
+    graph = capture(st, fused=False)
+    settle(st, graph, settle_s, fused=False)
+    ms, _, _ = time_total(st, graph, steps, fused=False)
+    each = time_each(st, graph, steps, fused=False)
     del graph
-    calls = [lambda l=l: st.fused_call(l) for l in range(st.n_gdn)]
-    for fn in calls:
-        fn()
-    gb = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gb):
-        for fn in calls:
-            fn()
-    gb.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        gb.replay()
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / (reps * len(calls))
-    del gb
     st.reset_T()
     d = dist(each)
-    return {"workload": st.name + "_fused_conv_gdn", "ms_per_step": ms, "ms_per_step_each": d,
-            "steps_per_s": 1000.0 / ms, "fused_us_per_layer": us, "layers": st.n_gdn,
-            "timed": "graph-replayed step after a settle phase; the fused call as a graph-replayed batch"}
+    return {"workload": st.name + "_unfused_conv_then_gdn", "ms_per_step": ms, "ms_per_step_each": d,
+            "steps_per_s": 1000.0 / ms, "layers": st.n_gdn,
+            "timed": "graph-replayed step after a settle phase"}
 
 
 def q8_attn_bench(st, reps=5, settle=0.4, pools=4):
@@ -960,6 +953,11 @@ def main():
     print(f"[bench] device copy {copy_gbps:.0f} GB/s; building the 128K stack (seed {args.seed})",
           file=sys.stderr, flush=True)
     st = Stack(dev, seed=args.seed, headroom_steps=room)
+    # each linear-attention layer runs as one fused conv -> delta-net call
+    # (ddt_tree_conv_gdn), the faster of the two paths; the unfused step
+    # (ddt_tree_conv, then ddt_tree_gdn) is timed beside it under `next`
+    st.setup_fused()
+    st.fused_step = True
     torch.cuda.synchronize()
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -992,13 +990,15 @@ def main():
     kb = st.kernel_bytes([max(L_step, 1.0)])
     per_step = st.calls()
     kernels = {}
-    for op in ("plan", "conv", "gdn", "attn", "walk", "commit"):
+    for op in ("plan", "fused", "conv", "gdn", "attn", "walk", "commit"):
         us = float(np.mean(timer[op])) * 1e3
         gbps = ob[op] / (us * 1e-6) / 1e9
         kernels[op] = {"us_per_call": us, "calls_per_step": per_step[op], "bytes_per_call": ob[op],
                        "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
                        "timed": "per call in eager steps" if op == "commit"
                        else "graph-replayed back-to-back batch"}
+        if per_step[op] == 0:
+            kernels[op]["note"] = "the unfused path's kernel, not in the headline step"
         if op in kb:
             kernels[op]["kernel_bytes_per_call"] = ob[op] + kb[op]
             kernels[op]["kernel_GBps"] = (ob[op] + kb[op]) / (us * 1e-6) / 1e9
@@ -1035,7 +1035,8 @@ def main():
             "attn_layers": st.n_attn, "kv_heads": st.c["Hkv"], "q_heads": st.c["Hq"],
             "head_dim": st.c["D"], "gdn_heads": [st.c["Hk"], st.c["Hv"]], "state": [st.c["dv"], st.c["dk"]],
             "conv_channels": st.c["C"], "vocab": synth.VOCAB, "graph": use_graph,
-            "inputs": "fp16 KV cache and attention, bf16 delta-net/conv/logits, fp32 state and accumulation",
+            "linear_attention_layer": "fused conv -> SiLU -> q|k|v -> L2 norm -> delta-net (ddt_tree_conv_gdn)",
+            "inputs": "fp16 KV cache and attention, bf16 conv input/logits, fp32 gates, state and accumulation",
             "mean_accepted_L": L_step,
         },
         "achieved_GBps_step": step_gbps,
@@ -1062,11 +1063,12 @@ def main():
     if not args.no_next:
         # widenings beside the step (not part of `value`)
         cs = 0.0 if args.no_cpu_baseline else 3.0
-        print("[bench] fused conv -> delta-net step", file=sys.stderr, flush=True)
-        fz = fused_stack_bench(st, args.steps, args.settle)
-        fz["vs_unfused_step"] = ms / fz["ms_per_step"]
-        fz["unfused_conv_plus_gdn_us"] = kernels["conv"]["us_per_call"] + kernels["gdn"]["us_per_call"]
-        out["next"] = {"fused_stack": fz}
+        print("[bench] unfused conv, delta-net step", file=sys.stderr, flush=True)
+        uf = unfused_stack_bench(st, args.steps, args.settle)
+        uf["fused_step_speedup"] = uf["ms_per_step"] / ms
+        uf["conv_plus_gdn_us"] = kernels["conv"]["us_per_call"] + kernels["gdn"]["us_per_call"]
+        uf["fused_us"] = kernels["fused"]["us_per_call"]
+        out["next"] = {"unfused_stack": uf}
         print("[bench] 8-bit KV attention", file=sys.stderr, flush=True)
         out["next"]["q8_attention"] = q8_attn_bench(st)
         print("[bench] sampled acceptance", file=sys.stderr, flush=True)

@@ -87,6 +87,49 @@ def test_stack_128k_full_size_sampled(gpu):
             assert torch.equal(V[t // 16, :, :, t % 16], a["Vt"][node])
 
 
+def test_stack_128k_fused_full_size_sampled(gpu):
+    """The benchmark's headline step: each linear-attention layer as one
+    fused conv -> delta-net call, at full size; sampled layers against the
+    fused oracle, the walk, and the commit of their state and prefix."""
+    import bench
+    banner("stack 48 fused conv->gdn / 16 attn, T=131072, N=22 (the benchmark's step): sampled parity")
+    st = bench.Stack(gpu, seed=0, headroom_steps=bench.headroom())
+    st.setup_fused()
+    st.fused_step = True
+    c = st.c
+    chk_g = [0, c["n_gdn"] - 1]
+    pre = {l: dict(S_c=host(st.gdn[l]["S_c"]).copy(), prefix=u16(st.conv[l]["prefix"]).copy())
+           for l in chk_g}
+    T0 = int(st.T.item())
+    st.step()
+    torch.cuda.synchronize()
+    assert not host(st.tb.status).any()
+    par = st.parent
+    refs = {}
+    for l in chk_g:
+        x = {k: u16(v) for k, v in st.conv[l].items()}
+        x["prefix"] = pre[l]["prefix"]
+        f = st.fz[l]
+        al, be = host(f["alpha"]), host(f["beta"])
+        out, q, k, v = oracle.tree_conv_gdn(par, x["x"], x["prefix"], x["w"], al, be, pre[l]["S_c"],
+                                            c["Hk"], c["Hv"], c["dk"], c["dv"])
+        assert rel_err(host(st.gdn_out[l]), out, (0, 1)) < TOL
+        assert rel_err(host(f["k"]), k, (0, 1)) < TOL  # the keys handed to the commit
+        refs[l] = (x, q, k, v, al, be)
+    am = oracle.argmax_rows(u16(st.logits))
+    assert np.array_equal(host(st.amax), am)
+    paths, L, bonus = oracle.accept_walk(par, host(st.tok), am)
+    assert int(host(st.L)[0]) == L[0] and int(host(st.bonus)[0]) == bonus[0]
+    assert int(st.T.item()) == T0 + L[0]
+    pg = list(paths[0])
+    for l in chk_g:
+        x, q, k, v, al, be = refs[l]
+        S_ref = oracle.commit_gdn_state(pre[l]["S_c"], q, k, v, al, be, pg, 0)
+        assert rel_err(host(st.gdn[l]["S_c"])[0], S_ref, (0,)) < TOL
+        pre_ref = oracle.commit_conv_prefix(x["prefix"], x["x"], pg, 0)
+        assert np.array_equal(oracle.num.f64(u16(st.conv[l]["prefix"]))[0], pre_ref)
+
+
 def test_batched_full_size_sampled(gpu):
     banner("batched 8 sequences, paged, budgets {8..64}, T in [2K, 64K]: sampled parity")
     cfg = synth.BATCHED
