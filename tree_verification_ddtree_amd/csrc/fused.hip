@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_to
   }
   __syncthreads();  // the x staging is dead from here on
   if (vt < 2 * n) {
-    st8f(V.v + iv * GDN_R + 8 * vch, yv);
+    st8f(V.v + iv * GDN_RS + 8 * vch, yv);
     if (v_out) st8f(v_out + ((size_t)(s.o + iv) * Hv + h) * dv + row0 + 8 * vch, yv);
   }
   // (the front reads only the q and k rows; the barrier after it orders V.v)
@@ -306,10 +306,10 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_to
   for (int idx = tid; idx < n * 4; idx += blockDim.x) {
     const int i = idx >> 2, c = (idx & 3) * 4;
     *reinterpret_cast<float4 *>(out + ((size_t)(s.o + i) * Hv + h) * dv + row0 + c) =
-        *reinterpret_cast<const float4 *>(V.O + i * GDN_R + c);
+        *reinterpret_cast<const float4 *>(V.O + i * GDN_RS + c);
     if (node_u)
       *reinterpret_cast<float4 *>(node_u + ((size_t)(s.o + i) * Hv + h) * dv + row0 + c) =
-          *reinterpret_cast<const float4 *>(V.U + i * GDN_R + c);
+          *reinterpret_cast<const float4 *>(V.U + i * GDN_RS + c);
   }
   if (node_states && tid < GDN_R * LPR) {
     const int lr = tid / LPR, c0 = (tid % LPR) * 8;

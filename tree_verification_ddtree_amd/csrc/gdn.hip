@@ -58,10 +58,10 @@ __global__ __launch_bounds__(256, 1) void gdn_kernel(int plan_B, int plan_n_tota
   for (int idx = tid; idx < n * 4; idx += blockDim.x) {
     const int i = idx >> 2, c = (idx & 3) * 4;
     *reinterpret_cast<float4 *>(out + ((size_t)(s.o + i) * Hv + h) * dv + row0 + c) =
-        *reinterpret_cast<const float4 *>(V.O + i * GDN_R + c);
+        *reinterpret_cast<const float4 *>(V.O + i * GDN_RS + c);
     if (node_u)
       *reinterpret_cast<float4 *>(node_u + ((size_t)(s.o + i) * Hv + h) * dv + row0 + c) =
-          *reinterpret_cast<const float4 *>(V.U + i * GDN_R + c);
+          *reinterpret_cast<const float4 *>(V.U + i * GDN_RS + c);
   }
   if (node_states && tid < GDN_R * LPR) {
     const int lr = tid / LPR, c0 = (tid % LPR) * 8;

@@ -39,6 +39,11 @@ typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int GDN_R = 16;     // state rows per workgroup (one matrix-core row block)
+// Floats per node in the node-major row arrays (v, D, F, U, O): the 16 rows
+// and 4 of padding.  Lanes of the solve read the rows of different nodes;
+// with a stride of 16 floats every node's row r falls on the same two LDS
+// banks, with 20 the nodes spread over the banks, 16-byte alignment kept.
+constexpr int GDN_RS = 20;
 constexpr int GDN_MAXA = 8;   // nearest ancestors whose coefficients a node record keeps
 constexpr int GDN_PATH = 12;  // deepest tree (levels) the register path solve takes
 
@@ -53,7 +58,8 @@ struct GdnRec {
 };
 
 // LDS carve-up, every array 16-byte aligned; per-node row data is
-// node-major ([node][16 rows]) so a lane's 4 rows are one 16-byte access.
+// node-major ([node][GDN_RS], rows first) so a lane's 4 rows are one
+// 16-byte access.
 struct GdnLds {
   int n16, gs;
   size_t v, al, be, anc, lvl, pos, lvs, meta, Gm, D, F, U, O, rec, total;
@@ -61,8 +67,8 @@ struct GdnLds {
     auto up = [](size_t x) { return (x + 15) / 16 * 16; };
     n16 = (nmax + 15) / 16 * 16;
     gs = 2 * n16;
-    v = 0;                                       // [nmax][16] v of the tile's rows
-    al = up(v + (size_t)nmax * GDN_R * 4);       // [nmax]
+    v = 0;                                       // [nmax][GDN_RS] v of the tile's rows
+    al = up(v + (size_t)nmax * GDN_RS * 4);      // [nmax]
     be = up(al + (size_t)nmax * 4);              // [nmax]
     anc = up(be + (size_t)nmax * 4);             // [nmax] u64, self included
     lvl = up(anc + (size_t)nmax * 8);            // [nmax] nodes by level
@@ -70,11 +76,11 @@ struct GdnLds {
     lvs = up(pos + (size_t)nmax * 4);            // [nmax + 2] level starts
     meta = up(lvs + (size_t)(nmax + 2) * 4);     // [4]: number of levels
     Gm = up(meta + 16);                          // [n16][gs] k_a . (k|q)_j
-    D = up(Gm + (size_t)n16 * gs * 4);           // [nmax][16] S_c . k_j
-    F = up(D + (size_t)nmax * GDN_R * 4);        // [nmax][16] S_c . q_j
-    U = up(F + (size_t)nmax * GDN_R * 4);        // [nmax][16] u
-    O = up(U + (size_t)nmax * GDN_R * 4);        // [nmax][16] outputs
-    rec = up(O + (size_t)nmax * GDN_R * 4);      // [nmax] GdnRec (deep trees only)
+    D = up(Gm + (size_t)n16 * gs * 4);           // [nmax][GDN_RS] S_c . k_j
+    F = up(D + (size_t)nmax * GDN_RS * 4);       // [nmax][GDN_RS] S_c . q_j
+    U = up(F + (size_t)nmax * GDN_RS * 4);       // [nmax][GDN_RS] u
+    O = up(U + (size_t)nmax * GDN_RS * 4);       // [nmax][GDN_RS] outputs
+    rec = up(O + (size_t)nmax * GDN_RS * 4);     // [nmax] GdnRec (deep trees only)
     total = up(rec + (size_t)nmax * sizeof(GdnRec));
   }
 };
@@ -129,7 +135,7 @@ __device__ __forceinline__ void put_v(GdnView &V, int idx, gu32x4 x) {
   constexpr int UE = 16 / (int)sizeof(T), VP = GDN_R / UE;
   float f[UE];
   piece_f32<T>(x, f);
-  float *dst = V.v + (idx / VP) * GDN_R + (idx % VP) * UE;
+  float *dst = V.v + (idx / VP) * GDN_RS + (idx % VP) * UE;
   *reinterpret_cast<gf32x4 *>(dst) = gf32x4{f[0], f[1], f[2], f[3]};
   if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(dst + 4) = gf32x4{f[4], f[5], f[6], f[7]};
 }
@@ -204,7 +210,7 @@ __device__ void gdn_front_rb(GdnView &V, int n, Gid gid, Anc anc_of, const T *__
   auto store_D = [&](int c, const gf32x4 &acc) {
     if (c < 2 * n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
+      for (int e = 0; e < 4; ++e) ((c & 1) ? V.F : V.D)[(c >> 1) * GDN_RS + 4 * kk + e] = acc[e];
     }
   };
   auto store_G = [&](int c, int m, const gf32x4 &g4) {
@@ -495,7 +501,7 @@ __device__ void gdn_front_lds_rb(GdnView &V, int n, const QkPlanes &Q, const Sro
     }
     if (c < 2 * n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) (isq ? V.F : V.D)[(c >> 1) * GDN_R + 4 * kk + e] = acc[e];
+      for (int e = 0; e < 4; ++e) (isq ? V.F : V.D)[(c >> 1) * GDN_RS + 4 * kk + e] = acc[e];
 #pragma unroll
       for (int m = 0; m < NRB; ++m)
 #pragma unroll
@@ -576,8 +582,8 @@ __device__ void gdn_path_solve(GdnView &V, int n, float scale) {
   for (int k = 0; k < PMAX; ++k) {
     al[k] = V.al[p[k]];
     be[k] = V.be[p[k]];
-    Dk[k] = *reinterpret_cast<const vec *>(V.D + p[k] * GDN_R + r0);
-    vk[k] = *reinterpret_cast<const vec *>(V.v + p[k] * GDN_R + r0);
+    Dk[k] = *reinterpret_cast<const vec *>(V.D + p[k] * GDN_RS + r0);
+    vk[k] = *reinterpret_cast<const vec *>(V.v + p[k] * GDN_RS + r0);
 #pragma unroll
     for (int j = 0; j < k; ++j) g[j][k] = V.Gm[p[j] * V.gs + 2 * p[k]];  // k_j . k_k
   }
@@ -599,12 +605,12 @@ __device__ void gdn_path_solve(GdnView &V, int n, float scale) {
     for (int e = 0; e < RW; ++e) u[k][e] = fmaf(be[k], fmaf(c1, Dk[k][e], vk[k][e]), acc[e]);
     if (k == d) ul = u[k];
   }
-  *reinterpret_cast<vec *>(V.U + i * GDN_R + r0) = ul;
+  *reinterpret_cast<vec *>(V.U + i * GDN_RS + r0) = ul;
   if (WANT_O) {
     float hq[PMAX];
 #pragma unroll
     for (int j = 0; j < PMAX; ++j) hq[j] = V.Gm[p[j] * V.gs + 2 * i + 1];  // k_j . q_i
-    const vec Fi = *reinterpret_cast<const vec *>(V.F + i * GDN_R + r0);
+    const vec Fi = *reinterpret_cast<const vec *>(V.F + i * GDN_RS + r0);
     const float kqd = V.Gm[i * V.gs + 2 * i + 1];
     float w = 1.f, ai = 0.f;
     vec y = (vec)(0.f);
@@ -620,7 +626,7 @@ __device__ void gdn_path_solve(GdnView &V, int n, float scale) {
     vec o;
 #pragma unroll
     for (int e = 0; e < RW; ++e) o[e] = scale * fmaf(ai, fmaf(w, Fi[e], y[e]), ul[e] * kqd);
-    *reinterpret_cast<vec *>(V.O + i * GDN_R + r0) = o;
+    *reinterpret_cast<vec *>(V.O + i * GDN_RS + r0) = o;
   }
 }
 
@@ -730,9 +736,9 @@ __device__ __forceinline__ void gdn_node(GdnView &V, const GdnRec &R, int n, int
   const int i = min((unsigned)R.i, (unsigned)(n - 1));
   float Ua[GDN_MAXA];
 #pragma unroll
-  for (int t = 0; t < GDN_MAXA; ++t) Ua[t] = V.U[min((unsigned)R.a[t], (unsigned)(n - 1)) * GDN_R + r];
-  const float Di = V.D[i * GDN_R + r], vi = V.v[i * GDN_R + r];
-  const float Fi = WANT_O ? V.F[i * GDN_R + r] : 0.f;
+  for (int t = 0; t < GDN_MAXA; ++t) Ua[t] = V.U[min((unsigned)R.a[t], (unsigned)(n - 1)) * GDN_RS + r];
+  const float Di = V.D[i * GDN_RS + r], vi = V.v[i * GDN_RS + r];
+  const float Fi = WANT_O ? V.F[i * GDN_RS + r] : 0.f;
   between();
   __builtin_amdgcn_sched_barrier(0);
   float acc = 0.f, y = 0.f;
@@ -749,15 +755,15 @@ __device__ __forceinline__ void gdn_node(GdnView &V, const GdnRec &R, int n, int
     while (bits) {
       const int a = top_bit(bits);
       bits &= ~(1ull << a);
-      const float ua = V.U[a * GDN_R + r];
+      const float ua = V.U[a * GDN_RS + r];
       acc = fmaf(-(ba * (w * V.Gm[a * V.gs + 2 * i])), ua, acc);
       if (WANT_O) y = fmaf(w * V.Gm[a * V.gs + 2 * i + 1], ua, y);
       w *= V.al[a];
     }
   }
   const float u = fmaf(R.bi, fmaf(R.c1, Di, vi), acc);
-  V.U[i * GDN_R + r] = u;
-  if (WANT_O) V.O[i * GDN_R + r] = scale * fmaf(R.ai, fmaf(R.P, Fi, y), u * R.kqd);
+  V.U[i * GDN_RS + r] = u;
+  if (WANT_O) V.O[i * GDN_RS + r] = scale * fmaf(R.ai, fmaf(R.P, Fi, y), u * R.kqd);
 }
 
 __device__ __forceinline__ GdnRec load_rec(const GdnView &V, int p) {
@@ -833,7 +839,7 @@ __device__ __forceinline__ void gdn_state(const GdnView &V, int i, int r, int c0
   while (bits) {
     const int a = top_bit(bits);
     bits &= ~(1ull << a);
-    const float c = (ai * w) * V.U[a * GDN_R + r];
+    const float c = (ai * w) * V.U[a * GDN_RS + r];
     float ka[8];
     load8(krow(a) + c0, ka);
 #pragma unroll
@@ -843,7 +849,7 @@ __device__ __forceinline__ void gdn_state(const GdnView &V, int i, int r, int c0
   float sc[8], ki[8];
   ld8f(Srow + c0, sc);
   load8(krow(i) + c0, ki);
-  const float cs = ai * w, ui = V.U[i * GDN_R + r];
+  const float cs = ai * w, ui = V.U[i * GDN_RS + r];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = fmaf(ui, ki[e], fmaf(cs, sc[e], s[e]));
 }
