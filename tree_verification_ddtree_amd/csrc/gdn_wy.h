@@ -460,21 +460,82 @@ __device__ void gdn_front_lds_rb(GdnView &V, int n, const QkPlanes &Q, const Sro
       o[0] = o[1] = z;
     }
   };
-  if (wave >= ncb) return;
+  // Key row block m is needed by column block cb only if the block holds a
+  // node at or before cb's last node (the solve reads k_a . x_b for a <= b
+  // only): m < nm(cb).  When there are fewer column blocks than waves, an
+  // idle wave takes the key row blocks m >= 1 of a column block (the last
+  // ones need the most), so that no wave forms all of them.
+  auto nm_of = [&](int cb) { return min(n - 1, 8 * cb + 7) / 16 + 1; };
+  const int spare = ncb < nw ? nw - ncb : 0;
+  auto helped = [&](int cb) { return ncb - 1 - cb < spare && nm_of(cb) >= 2; };
+  // column block cb: operands of column c = 16 cb + i16 (k of node c/2 for
+  // even c, q for odd c; past the tree the last node's)
+  auto column = [&](int cb, gu32x4 (&bv)[NS][2]) {
+    const int c = 16 * cb + i16;
+    const bool isq = c & 1;
+    const int cn = min(c, 2 * n - 1) >> 1;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) slice(isq ? Q.qh : Q.kh, isq ? Q.ql : Q.kl, cn, 32 * s + 8 * kk, bv[s]);
+  };
+  // key row blocks m_lo .. m_hi - 1 against column block cb (operands read
+  // by the caller for those blocks): k_a . k_b, k_a . q_b into Gm
+  auto key_cells = [&](int cb, int m_lo, int m_hi, const gu32x4 (&bv)[NS][2], const gu32x4 (&ka)[NRB][NS][2]) {
+    gf32x4 g4[NRB];
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) {
+      g4[m] = gf32x4{0.f, 0.f, 0.f, 0.f};
+      if (m < m_lo || m >= m_hi) continue;  // the same in every lane
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][1]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
+        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][0]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s][1]), g4[m], 0, 0, 0);
+        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][0]),
+                                                        __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
+      }
+    }
+    const int c = 16 * cb + i16;
+    if (c < 2 * n) {
+#pragma unroll
+      for (int m = 0; m < NRB; ++m) {
+        if (m < m_lo || m >= m_hi) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * m + 4 * kk + e;
+          if (r < n) V.Gm[r * V.gs + c] = g4[m][e];
+        }
+      }
+    }
+  };
+  auto key_rows = [&](int m_lo, int m_hi, gu32x4 (&ka)[NRB][NS][2]) {
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) {
+      if (m < m_lo || m >= m_hi) continue;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) slice(Q.kh, Q.kl, min(16 * m + i16, n - 1), 32 * s + 8 * kk, ka[m][s]);
+    }
+  };
+  if (wave >= ncb) {  // a spare wave: the upper key row blocks of one column block
+    const int cb = ncb - 1 - (wave - ncb);
+    if (cb < 0 || !helped(cb)) return;
+    const int nm = nm_of(cb);
+    gu32x4 bv[NS][2], ka[NRB][NS][2];
+    column(cb, bv);
+    key_rows(1, nm, ka);
+    key_cells(cb, 1, nm, bv, ka);
+    return;
+  }
   const auto &sa = S.sa;
   for (int cb = wave; cb < ncb; cb += nw) {
     const int c = 16 * cb + i16;
-    const int cn = min(c, 2 * n - 1) >> 1;
     const bool isq = c & 1;
+    const int mhi = helped(cb) ? 1 : nm_of(cb);
     // every operand read of the column block before any product is stored
     gu32x4 bv[NS][2], ka[NRB][NS][2];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) slice(isq ? Q.qh : Q.kh, isq ? Q.ql : Q.kl, cn, 32 * s + 8 * kk, bv[s]);
-#pragma unroll
-    for (int m = 0; m < NRB; ++m)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) slice(Q.kh, Q.kl, min(16 * m + i16, n - 1), 32 * s + 8 * kk, ka[m][s]);
-    gf32x4 acc = {0.f, 0.f, 0.f, 0.f}, g4[NRB];
+    column(cb, bv);
+    key_rows(0, mhi, ka);
+    gf32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[2][s]),
@@ -486,30 +547,11 @@ __device__ void gdn_front_lds_rb(GdnView &V, int n, const QkPlanes &Q, const Sro
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, sa[0][s]),
                                                     __builtin_bit_cast(gbf16x8, bv[s][0]), acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int m = 0; m < NRB; ++m) {
-      g4[m] = gf32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][1]),
-                                                        __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
-        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][0]),
-                                                        __builtin_bit_cast(gbf16x8, bv[s][1]), g4[m], 0, 0, 0);
-        g4[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, ka[m][s][0]),
-                                                        __builtin_bit_cast(gbf16x8, bv[s][0]), g4[m], 0, 0, 0);
-      }
-    }
     if (c < 2 * n) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) (isq ? V.F : V.D)[(c >> 1) * GDN_RS + 4 * kk + e] = acc[e];
-#pragma unroll
-      for (int m = 0; m < NRB; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * m + 4 * kk + e;
-          if (r < n) V.Gm[r * V.gs + c] = g4[m][e];
-        }
     }
+    key_cells(cb, 0, mhi, bv, ka);
   }
 }
 
