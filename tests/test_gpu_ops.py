@@ -257,6 +257,13 @@ ATTN_SHAPES = {
     # more splits than one combine batch holds (64), some of them left empty
     "many_splits": ([22], [40000], 6, 1, 256, False, False, 100),
     "many_splits_batch": ([22, 7], [30000, 900], 12, 2, 256, True, True, 90),
+    # a batch shares the splits of a (KV head, row group): fewer splits asked
+    # for than sequences (raised to one each), an empty context, a row group
+    # that only some sequences reach, more sequences than a wavefront's lanes
+    "pool_below_batch": ([3, 5, 2, 7], [500, 0, 2000, 64], 24, 4, 256, True, True, 2),
+    "pool_uneven_rows": ([40, 2, 30], [3000, 5000, 100], 24, 4, 256, True, True, 0),
+    "pool_70_seqs": ([1 + b % 8 for b in range(70)], [(b * 397) % 3001 for b in range(70)],
+                     24, 4, 256, True, False, 0),
 }
 
 
@@ -268,6 +275,24 @@ def test_attn_mfma_shapes(gpu, case):
     err, _ = attn_case(gpu, trees, T, Hq, Hkv, D, "f16", 15, paged=paged, nan_fill=nan_fill,
                        n_splits=ns)
     assert err < TOL
+
+
+def test_attn_mfma_batch_above_split_limit(gpu):
+    # every sequence of a batch needs a split of its own, and a (KV head, row
+    # group) has at most 1024: a larger batch is refused before any launch
+    banner("attn mfma batch of 1025 one-node sequences: shape error")
+    tb, par, off = make_batch([synth.chain(1)] * 1025, 4, gpu)
+    n = len(par)
+    q = torch.zeros(n, 24, 256, dtype=torch.float16, device=gpu)
+    kv = torch.zeros(n, 4, 256, dtype=torch.float16, device=gpu)
+    cache = torch.zeros(1, 4, 16, 256, dtype=torch.float16, device=gpu)
+    pt = torch.zeros(1025, 1, dtype=torch.int32, device=gpu)
+    T = torch.zeros(1025, dtype=torch.int32, device=gpu)
+    out = torch.zeros(n, 24, 256, dtype=torch.float32, device=gpu)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=gpu)
+    with pytest.raises(ddt.DDTError) as e:
+        ddt.ddt_tree_attn(tb, q, cache, cache, pt, T, 0, kv, kv, out, ws)
+    assert e.value.code == -3  # DDT_E_SHAPE
 
 
 # ---- 8-bit cache: the same attention over fp16(code * token scale)
@@ -315,6 +340,7 @@ ATTN_Q8 = {
     "ragged_tiny_splits": ([5], [75], 24, 4, 256, False, 4),
     "wide_scales": ([22], [4133], 24, 4, 256, False, 0, "wide"),
     "wide_scales_d128_paged": ([16, 9], [3000, 517], 16, 2, 128, True, 5, "wide"),
+    "pool_uneven_rows": ([40, 2, 30], [3000, 5000, 100], 24, 4, 256, True, 0),
 }
 
 

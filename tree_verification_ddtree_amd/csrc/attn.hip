@@ -102,11 +102,11 @@ __device__ __forceinline__ int ctx_len(const AttnArgs &A, int b, bool *cut) {
   return t;
 }
 
-// Keys per split of a sequence with Tb committed tokens: the sequence's own
-// length spread over the splits, in whole tiles, so every active split gets
-// the same number of tiles (give or take one).
-__device__ __forceinline__ int split_chunk(const AttnArgs &A, int Tb) {
-  int c = (Tb + A.n_splits - 1) / A.n_splits;
+// Keys per split of a sequence with Tb committed tokens and nb splits: the
+// sequence's own length spread over its splits, in whole tiles, so every
+// active split gets the same number of tiles (give or take one).
+__device__ __forceinline__ int split_chunk(int Tb, int nb) {
+  int c = (Tb + nb - 1) / nb;
   c = (c + TILE - 1) / TILE * TILE;
   return c < TILE ? TILE : c;
 }
@@ -123,11 +123,90 @@ __device__ __forceinline__ int page_uniform(const AttnArgs &A, int b, int t) {
   return *(const cint32 *)(A.pt + (size_t)b * A.max_pages + pg);
 }
 
-__device__ __forceinline__ int n_active_splits(const AttnArgs &A, int Tb) {
-  const int chunk = split_chunk(A, Tb);
+__device__ __forceinline__ int n_active_splits(int Tb, int nb) {
+  const int chunk = split_chunk(Tb, nb);
   int n = (Tb + chunk - 1) / chunk;
   n = n < 1 ? 1 : n;
-  return n > A.n_splits ? A.n_splits : n;
+  return n > nb ? nb : n;
+}
+
+// The batch's sequences share the A.n_splits context splits of a (KV head,
+// row group): every sequence with rows in the row group takes one, and the
+// rest are dealt in proportion to each sequence's work, its tiles (cache and
+// tree) times its row blocks per wavefront, with at least 256 keys per split.
+// A short context then no longer waits on a long one that has the same
+// number of splits.  Every workgroup of the attention kernel and of the
+// combine computes the same deal from the committed lengths (one lane per
+// sequence).  A batch of one sequence launches the direct mapping instead.
+struct PoolSlot {
+  int b, j, nb, first;  // sequence, its split, its split count, its first pool split
+};
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// want_b >= 0: the deal of sequence want_b; otherwise the sequence that pool
+// split s belongs to (b = -1 past the last dealt split).
+__device__ PoolSlot pool_slot(const AttnArgs &A, int rg, int s, int want_b) {
+  const int B = A.P.B;
+  const int lane = threadIdx.x & 63;
+  // per-lane sequence data: rows in this row group, weight, split cap
+  auto seq_data = [&](int b, long long &w, int &cap) {
+    w = 0;
+    cap = 0;
+    if (b >= B) return;
+    const Seq q = seq_of(A.P, b);
+    const int rows = min(max(A.G * q.n - rg * A.rows_wg, 0), A.rows_wg);
+    if (rows == 0) return;
+    const int Tb = ctx_len(A, b, nullptr);
+    const long long tiles = (Tb + TILE - 1) / TILE + (q.n + TILE - 1) / TILE;
+    w = tiles * ((rows + 63) / 64);
+    cap = max(1, (Tb + 255) / 256);
+  };
+  long long W = 0;
+  int m = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    long long w;
+    int cap;
+    seq_data(b0 + lane, w, cap);
+    m += __popcll(__ballot(cap > 0));
+    W += wave_sum_ll(w);
+  }
+  const long long E = A.n_splits > m ? A.n_splits - m : 0;
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    long long w;
+    int cap;
+    seq_data(b0 + lane, w, cap);
+    const int nb = cap > 0 ? min(cap, 1 + (int)(W > 0 ? E * w / W : 0)) : 0;
+    const int incl = wave_incl_scan(nb);
+    const int first = base + incl - nb;
+    if (want_b >= 0) {
+      if (want_b < b0 + 64) {
+        const int l = want_b - b0;
+        return {want_b, 0, __shfl(nb, l), __shfl(first, l)};
+      }
+    } else {
+      const unsigned long long hit = __ballot(nb > 0 && first <= s && s < first + nb);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        const int f = __shfl(first, l);
+        return {b0 + l, s - f, __shfl(nb, l), f};
+      }
+    }
+    base += __shfl(incl, 63);
+  }
+  return {-1, 0, 0, 0};
 }
 
 // Registers of N 16-byte K chunks and N V chunks of a tile being filled.
@@ -216,7 +295,10 @@ __device__ __forceinline__ void wait_vm_tiles(int later) {
   }
 }
 
-template <int D, int NB, bool Q8>
+// POOL: the batch's sequences share the splits of a (KV head, row group)
+// (pool_slot); otherwise the grid's z runs over sequences and row groups and
+// every sequence has A.n_splits splits.
+template <int D, int NB, bool Q8, bool POOL>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
   constexpr int WAVE_CH = (TILE * CPR) / 256;  // direct loads per wave, per tensor and tile
@@ -228,8 +310,16 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   extern __shared__ half8 lds_raw[];
   _Float16 *lds = reinterpret_cast<_Float16 *>(lds_raw);
 
-  const int split = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
+  const int g = blockIdx.y;
+  int b, rg, split, nbs;
+  if constexpr (POOL) {
+    rg = blockIdx.z;
+    const PoolSlot ps = pool_slot(A, rg, blockIdx.x, -1);
+    if (ps.b < 0) return;
+    b = ps.b, split = ps.j, nbs = ps.nb;
+  } else {
+    b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg, split = blockIdx.x, nbs = A.n_splits;
+  }
   const Seq s = seq_of(A.P, b);
   const int rows_b = A.G * s.n;
   const int row0 = rg * A.rows_wg;
@@ -263,10 +353,10 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   // Q fragments are on their way
   bool cut;
   const int Tb = ctx_len(A, b, &cut);
-  const int nsp = n_active_splits(A, Tb);
+  const int nsp = n_active_splits(Tb, nbs);
   if (split >= nsp) return;
   if (cut && split == 0 && g == 0 && rg == 0 && threadIdx.x == 0) A.P.status[b] |= DDT_ST_CTX;
-  const int chunk = split_chunk(A, Tb);
+  const int chunk = split_chunk(Tb, nbs);
   const int t_beg = split * chunk;
   const int t_end = min(Tb, t_beg + chunk);
   const int n_keys = t_end > t_beg ? t_end - t_beg : 0;
@@ -910,7 +1000,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
   }
 
   // ---- partial results of this split
-  const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits + split) * A.rows_wg;
+  const size_t base =
+      POOL ? (((size_t)g * A.n_rg + rg) * A.n_splits + blockIdx.x) * A.rows_wg
+           : (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits + split) * A.rows_wg;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     if (!blk_on[j]) continue;
@@ -937,7 +1029,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 // are then added in a fixed order, so the result does not depend on timing.
 constexpr int MAX_SPLITS = 1024;
 
-template <int D>
+template <int D, bool POOL>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
   constexpr int TPR = D / 4;     // threads per channel sweep
   constexpr int SG = 256 / TPR;  // split groups
@@ -950,16 +1042,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
   const int rho = rg * A.rows_wg + rl;
   if (rho >= A.G * s.n) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  const size_t base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
+  size_t base;
+  int nw;  // the sequence's split count
+  if constexpr (POOL) {
+    const PoolSlot ps = pool_slot(A, rg, 0, b);  // the sequence's pool splits
+    base = (((size_t)g * A.n_rg + rg) * A.n_splits + ps.first) * A.rows_wg + rl;
+    nw = ps.nb;
+  } else {
+    base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
+    nw = A.n_splits;
+  }
   const int dc = tid % TPR, sg = tid / TPR;
   const _Float16 *src = A.Opart + base * D + 4 * dc;
   const size_t sstride = (size_t)A.rows_wg * D;
   // Every load that depends on no other goes out first: the context length,
   // wave 0's split statistics and each thread's first BATCH partials.  Split
-  // indices are clamped to the workspace's n_splits, which bounds the active
-  // count; a split that turns out inactive is skipped after its load and never
-  // multiplied, since its slot may hold anything.
-  const int nw = A.n_splits;
+  // indices are clamped to the sequence's split count, which bounds the
+  // active count; a split that turns out inactive is skipped after its load
+  // and never multiplied, since its slot may hold anything.
   float2 ml0 = make_float2(-INFINITY, 0.f);
   if (tid < 64) ml0 = A.ML[base + (size_t)min(lane, nw - 1) * A.rows_wg];
   half4 v[BATCH];
@@ -968,7 +1068,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
   // the context length is read after the partials are requested (left to
   // itself the scheduler clamps it first and so waits for it before them)
   __builtin_amdgcn_sched_barrier(0);
-  const int nsp = n_active_splits(A, ctx_len(A, b, nullptr));
+  const int nsp = n_active_splits(ctx_len(A, b, nullptr), nw);
   if (tid < 64) {
     float m = lane < nsp ? fmaxf(-INFINITY, ml0.x) : -INFINITY;
     for (int sp = lane + 64; sp < nsp; sp += 64) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
@@ -1115,9 +1215,24 @@ static Cfg attn_cfg(const ddt_plan *P, int Hq, int Hkv, int D, int T_max, int n_
   c.rows_wg = 64 * c.nb;
   c.n_rg = (rows + c.rows_wg - 1) / c.rows_wg;
   int tmax = T_max > 0 ? T_max : 1;
+  if (P->B > 1) {
+    // a pool of splits per (KV head, row group) that the sequences share
+    // (pool_slot): about one workgroup per compute unit, at least one split
+    // per sequence, at most one per 256 keys of the longest context each
+    if (n_splits <= 0) {
+      const long long units = (long long)Hkv * c.n_rg;
+      const long long want = (256 + units - 1) / units;
+      const long long by_len = (long long)P->B * ((tmax + 255) / 256);
+      n_splits = (int)(want < by_len ? want : by_len);
+    }
+    if (n_splits < P->B) n_splits = P->B;
+    c.n_splits = n_splits < MAX_SPLITS ? n_splits : MAX_SPLITS;
+    c.chunk = 0;
+    return c;
+  }
   if (n_splits <= 0) {
-    // about one workgroup per compute unit over the whole batch
-    const long long units = (long long)P->B * Hkv * c.n_rg;
+    // about one workgroup per compute unit
+    const long long units = (long long)Hkv * c.n_rg;
     long long want = (256 + units - 1) / units;
     long long by_len = (tmax + 255) / 256;  // keep splits >= 256 keys
     n_splits = (int)(want < by_len ? want : by_len);
@@ -1155,7 +1270,7 @@ static AttnArgs attn_args(const ddt_plan *P, const void *q, const int32_t *page_
   A.n_splits = c.n_splits;
   A.n_rg = c.n_rg;
   A.rows_wg = c.rows_wg;
-  const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
+  const size_t rows = (size_t)Hkv * c.n_rg * c.n_splits * c.rows_wg;
   A.Opart = (_Float16 *)ws;
   A.ML = (float2 *)((char *)ws + rows * D * sizeof(_Float16));
   A.out = out;
@@ -1165,19 +1280,25 @@ static AttnArgs attn_args(const ddt_plan *P, const void *q, const int32_t *page_
 // The matrix-core path: the split kernel, then the combine.
 template <bool Q8>
 static int launch_attn_mfma(const ddt_plan &P, const AttnArgs &A, const Cfg &c, int D, hipStream_t st) {
-  dim3 grid(c.n_splits, A.Hkv, P.B * c.n_rg);
+  // one sequence: its splits directly; several: the shared pool
+  const bool pool = P.B > 1;
+  dim3 grid(c.n_splits, A.Hkv, c.n_rg);
   // fp16: the ring and one spare stage for the tree tile (160 KiB at D = 256)
   const size_t lds = Q8 ? (size_t)(D == 256 ? LdsQ8<256>::TOTAL : LdsQ8<128>::TOTAL)
                         : (size_t)(NSTAGE + 1) * (D == 256 ? Lds<256>::STAGE : Lds<128>::STAGE) * sizeof(_Float16);
 #define DDT_ATTN(DD, NBB)                                                                       \
   do {                                                                                          \
-    hipError_t e_ = hipFuncSetAttribute((const void *)attn_mfma_kernel<DD, NBB, Q8>,            \
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+    const void *k_ = pool ? (const void *)attn_mfma_kernel<DD, NBB, Q8, true>                   \
+                          : (const void *)attn_mfma_kernel<DD, NBB, Q8, false>;                 \
+    hipError_t e_ = hipFuncSetAttribute(k_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e_ != hipSuccess) {                                                                     \
       set_hip_error(e_);                                                                        \
       return DDT_E_HIP;                                                                         \
     }                                                                                           \
-    hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB, Q8>), grid, dim3(256), lds, st, A);           \
+    if (pool)                                                                                   \
+      hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB, Q8, true>), grid, dim3(256), lds, st, A);   \
+    else                                                                                        \
+      hipLaunchKernelGGL((attn_mfma_kernel<DD, NBB, Q8, false>), grid, dim3(256), lds, st, A);  \
   } while (0)
   if (D == 256) {
     if (c.nb == 1) DDT_ATTN(256, 1); else if (c.nb == 2) DDT_ATTN(256, 2); else DDT_ATTN(256, 3);
@@ -1188,10 +1309,14 @@ static int launch_attn_mfma(const ddt_plan &P, const AttnArgs &A, const Cfg &c, 
   const int r = launch_status();
   if (r) return r;
   dim3 cgrid(c.rows_wg, A.Hkv, P.B * c.n_rg);
-  if (D == 256)
-    hipLaunchKernelGGL(attn_combine_kernel<256>, cgrid, dim3(256), 0, st, A);
+  if (D == 256 && pool)
+    hipLaunchKernelGGL((attn_combine_kernel<256, true>), cgrid, dim3(256), 0, st, A);
+  else if (D == 256)
+    hipLaunchKernelGGL((attn_combine_kernel<256, false>), cgrid, dim3(256), 0, st, A);
+  else if (pool)
+    hipLaunchKernelGGL((attn_combine_kernel<128, true>), cgrid, dim3(256), 0, st, A);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_combine_kernel<128, false>), cgrid, dim3(256), 0, st, A);
   return launch_status();
 }
 
@@ -1204,7 +1329,7 @@ extern "C" size_t ddt_tree_attn_workspace(const ddt_plan *P, int32_t Hq, int32_t
   if (!P || Hkv < 1 || Hq < Hkv || Hq % Hkv || D < 1) return 0;
   Cfg c = attn_cfg(P, Hq, Hkv, D, T_max, n_splits, DDT_F16);
   if (!c.mfma) return 0;
-  const size_t rows = (size_t)P->B * Hkv * c.n_rg * c.n_splits * c.rows_wg;
+  const size_t rows = (size_t)Hkv * c.n_rg * c.n_splits * c.rows_wg;
   return rows * (size_t)D * sizeof(_Float16) + rows * sizeof(float2);
 }
 
@@ -1239,6 +1364,7 @@ extern "C" int ddt_tree_attn(const ddt_plan *P, const void *q, const void *Kc, c
 #undef DDT_SMALL
     return launch_status();
   }
+  if (P->B > MAX_SPLITS) return DDT_E_SHAPE;  // a split per sequence at least
   if (!ws || ws_bytes < ddt_tree_attn_workspace(P, Hq, Hkv, D, T_max, n_splits)) return DDT_E_WS;
   AttnArgs A = attn_args(P, q, page_table, max_pages, T, T_max, Kt, Vt, Hq, Hkv, D, scale, c, out, ws);
   A.Kc = (const _Float16 *)Kc;
@@ -1260,6 +1386,7 @@ extern "C" int ddt_tree_attn_q8(const ddt_plan *P, const void *q, const int8_t *
   if (D != 128 && D != 256) return DDT_E_SHAPE;
   if (T_max < 0 || n_splits < 0) return DDT_E_RANGE;
   const Cfg c = attn_cfg(P, Hq, Hkv, D, T_max, n_splits, DDT_F16);
+  if (P->B > MAX_SPLITS) return DDT_E_SHAPE;  // a split per sequence at least
   if (!ws || ws_bytes < ddt_tree_attn_workspace(P, Hq, Hkv, D, T_max, n_splits)) return DDT_E_WS;
   AttnArgs A = attn_args(P, q, page_table, max_pages, T, T_max, Kt, Vt, Hq, Hkv, D, scale, c, out, ws);
   A.Kq = Kq;
