@@ -273,6 +273,28 @@ int ddt_accept_walk(const ddt_plan *plan, const void *logits, int32_t dtype, int
                     int32_t *bonus, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The verify argmax and walk on the host: the fall-back of the validated
+ * device walk (codehub lucebox-hub@main, "GPU draft top-K & verify-argmax
+ * (DFlash)": the device result is checked, and the host computes it when the
+ * check fails).  The device walk reports a failed check as DDT_ST_ARGMAX in
+ * the plan's status word; the caller then copies that step's logits and draft
+ * tokens to the host and calls this.  Results are those of ddt_accept_walk,
+ * bit for bit (same ties, NaN and -0 rules).
+ *   plan      host struct with HOST pointers: tree_off, parent (read) and
+ *             status (DDT_ST_TOKEN OR-ed in for a draft token outside
+ *             [0, V), which can never match); depth, anc, win unused
+ *   logits    host [n_total][V]  DDT_F32 or DDT_BF16
+ *   draft_tok host [n_total] int32 (the root's entry is not compared)
+ *   argmax, path, L, bonus  host outputs, laid out as for ddt_accept_walk
+ * Errors: DDT_E_ARG (null pointer), DDT_E_SHAPE (B, n_total, n_max, V),
+ * DDT_E_DTYPE, DDT_E_TREE (the trees are checked as ddt_tree_plan_host checks
+ * them); nothing is written then.  Runs on the calling thread; no HIP call.
+ */
+int ddt_accept_walk_host(const ddt_plan *plan, const void *logits, int32_t dtype, int32_t V,
+                         const int32_t *draft_tok, int32_t *argmax, int32_t *path, int32_t *L,
+                         int32_t *bonus);
+
+/*
  * The same verify argmax and walk for callers that cannot allocate device
  * memory: code being captured into a HIP graph, tight serving loops, and
  * harnesses that forbid allocation.  Arguments and results are those of

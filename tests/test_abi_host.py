@@ -199,3 +199,54 @@ def test_q8_binding_rejects_wrong_dtypes():
         ddt.ddt_tree_attn_q8(P, q, Kq, Ks.float(), Vq, Vs, None, T, 16, Kt, Vt, out, None)
     with pytest.raises(TypeError):
         ddt.ddt_tree_attn_q8(P, q, Kq, Ks, Vq, Vs, None, T, 16, Kt, Vt, out.half(), None)
+
+
+# ---- the host acceptance walk (the fall-back of the validated device walk)
+def host_walk(trees, lg, tok):
+    par, off = synth.concat_trees(trees)
+    B, n = len(trees), len(par)
+    n_max = max(len(t) for t in trees)
+    status = np.zeros(B, np.int32)
+    st = ddt.plan_struct(B, n, n_max, 4, off, par, None, None, None, status)
+    am, path = np.empty(n, np.int32), np.empty((B, n_max), np.int32)
+    L, bonus = np.empty(B, np.int32), np.empty(B, np.int32)
+    ddt.ddt_accept_walk_host(st, lg, tok, am, path, L, bonus)
+    return par, off, am, path, L, bonus, status
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_host_walk_matches_oracle(dt):
+    trees = [synth.random_tree(synth.rng_for(3, 93, b), s, 10) for b, s in enumerate([22, 64, 1, 8])]
+    V = 2048
+    lgs, toks = [], []
+    for b, t in enumerate(trees):
+        lg, tk = synth.logits_and_draft(3, (94, b), t, V, dt, p_match=0.9, plant=(b != 1))
+        lgs.append(lg)
+        toks.append(tk)
+    lg, tok = np.concatenate(lgs), np.concatenate(toks).astype(np.int32)
+    tok[30] = V + 1   # never matches; flagged
+    par, off, am, path, L, bonus, status = host_walk(trees, lg, tok)
+    ref_am = oracle.argmax_rows(lg)
+    assert np.array_equal(am, ref_am)
+    paths, rL, rb = oracle.accept_walk(par, tok, ref_am, tree_off=off)
+    assert np.array_equal(L, rL) and np.array_equal(bonus, rb)
+    for b in range(len(trees)):
+        assert list(path[b, :rL[b]]) == paths[b] and (path[b, rL[b]:] == -1).all()
+    assert list(status) == [0, 4, 0, 0]   # node 30 is in the second tree
+
+
+def test_host_walk_refuses_bad_arguments():
+    trees = [synth.chain(4)]
+    lg = np.zeros((4, 8), np.float32)
+    tok = np.zeros(4, np.int32)
+    with pytest.raises(TypeError):
+        host_walk(trees, lg.astype(np.float64), tok)
+    with pytest.raises(TypeError):
+        host_walk(trees, lg, tok.astype(np.int64))
+    bad = [np.array([-1, 0, 2, 1], np.int32)]
+    with pytest.raises(ddt.DDTError) as e:
+        host_walk(bad, lg, tok)
+    assert e.value.code == -2   # DDT_E_TREE
+    with pytest.raises(ddt.DDTError) as e:
+        host_walk(trees, np.zeros((4, 0), np.float32), tok)
+    assert e.value.code == -3   # DDT_E_SHAPE

@@ -506,3 +506,51 @@ def test_accept_walk_nan_and_bad_tokens(gpu):
     assert host(tb.status)[0] == ddt.DDT_ST_TOKEN
     paths, rL, rb = oracle.accept_walk(par, tok, ref)
     assert host(L)[0] == rL[0] and host(bonus)[0] == rb[0]
+
+
+def walk_batch(gpu, dt, seed, V=4096):
+    trees = [synth.random_tree(synth.rng_for(seed, 95, b), s, 10) for b, s in enumerate([22, 64, 1, 8])]
+    lgs, toks = [], []
+    for b, t in enumerate(trees):
+        lg, tk = synth.logits_and_draft(seed, (96, b), t, V, dt, p_match=0.9, plant=(b % 2 == 0))
+        lgs.append(lg)
+        toks.append(tk)
+    lg, tok = np.concatenate(lgs), np.concatenate(toks).astype(np.int32)
+    lg[3, :] = lg[3, 0]                        # a whole row tied
+    tb, par, off = make_batch(trees, 4, gpu)
+    n, B = len(par), len(trees)
+    outs = dict(am=torch.empty(n, dtype=torch.int32, device=gpu),
+                path=torch.empty(B, tb.n_max, dtype=torch.int32, device=gpu),
+                L=torch.empty(B, dtype=torch.int32, device=gpu), bonus=torch.empty(B, dtype=torch.int32, device=gpu))
+    ws = torch.empty(ddt.ddt_accept_walk_workspace(tb, V), dtype=torch.uint8, device=gpu)
+    return tb, par, off, lg, tok, outs, ws
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_accept_walk_host_equals_device(gpu, dt):
+    # the host walk (the fall-back) gives the device walk's outputs bit for bit
+    banner(f"walk host == device {dt}")
+    tb, par, off, lg, tok, o, ws = walk_batch(gpu, dt, 4)
+    ddt.ddt_accept_walk(tb, dev(lg), dev(tok), o["am"], o["path"], o["L"], o["bonus"], ws)
+    torch.cuda.synchronize()
+    h = [np.empty(tuple(t.shape), np.int32) for t in (o["am"], o["path"], o["L"], o["bonus"])]
+    ddt.ddt_accept_walk_host(tb.struct_host, lg, tok, *h)
+    for t, a in zip((o["am"], o["path"], o["L"], o["bonus"]), h):
+        assert np.array_equal(host(t), a)
+    assert np.array_equal(h[0], oracle.argmax_rows(lg))
+
+
+def test_accept_walk_fallback_from_status(gpu):
+    banner("walk fall-back from the status word")
+    tb, par, off, lg, tok, o, ws = walk_batch(gpu, "bf16", 5)
+    args = (dev(lg), dev(tok), o["am"], o["path"], o["L"], o["bonus"], ws)
+    st, ran = ddt.accept_walk_with_fallback(tb, *args)
+    assert not ran and not st.any()
+    ref = [host(t) for t in (o["am"], o["path"], o["L"], o["bonus"])]
+    # a failed device check, set from the host: the host walk takes over and
+    # writes the same outputs
+    tb.status[2] = ddt.DDT_ST_ARGMAX
+    st, ran = ddt.accept_walk_with_fallback(tb, *args)
+    assert ran and st[2] & ddt.DDT_ST_ARGMAX
+    for t, r in zip((o["am"], o["path"], o["L"], o["bonus"]), ref):
+        assert np.array_equal(host(t), r)

@@ -67,6 +67,7 @@ _SIGS = {
     "ddt_accept_walk": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                          _vp], _i32),
     "ddt_accept_walk_noalloc": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "ddt_accept_walk_host": ([ctypes.POINTER(Plan), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
     "ddt_commit_state": ([ctypes.POINTER(Plan), _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp], _i32),
     "ddt_draft_topk_workspace": ([_i32, _i32, _i32, _i32], _sz),
@@ -155,6 +156,11 @@ class TreeBatch:
         self.status = torch.zeros(self.B, **i32)
         self.struct = plan_struct(self.B, self.n_total, self.n_max, self.W, self.tree_off,
                                   self.parent, self.depth, self.anc, self.win, self.status)
+        # host copies of the tree for the host walk (its status words are its own)
+        self.parent_host, self.tree_off_host = parent.copy(), tree_off.copy()
+        self.status_host = np.zeros(self.B, np.int32)
+        self.struct_host = plan_struct(self.B, self.n_total, self.n_max, self.W, self.tree_off_host,
+                                       self.parent_host, None, None, None, self.status_host)
 
 
 def _plan(p):
@@ -276,6 +282,44 @@ def ddt_accept_walk_noalloc(plan, logits, draft_tok, argmax, path, L, bonus, str
     _check(lib().ddt_accept_walk_noalloc(_plan(plan), _ptr(logits), dtype_code(logits), int(logits.shape[-1]),
                                          _ptr(draft_tok), _ptr(argmax), _ptr(path), _ptr(L), _ptr(bonus),
                                          _stream(stream)), "ddt_accept_walk_noalloc")
+
+
+def ddt_accept_walk_host(plan_struct_host, logits, draft_tok, argmax, path, L, bonus):
+    """The host walk on numpy arrays: logits float32, or uint16 holding bf16
+    bits, [n_total][V]; outputs int32 arrays sized as for ddt_accept_walk."""
+    arrs = [np.ascontiguousarray(a) for a in (logits, draft_tok)]
+    for a in (argmax, path, L, bonus):
+        if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+            raise TypeError("ddt_accept_walk_host: outputs must be C-contiguous int32 arrays")
+    code = {np.dtype(np.float32): DDT_F32, np.dtype(np.uint16): DDT_BF16}.get(arrs[0].dtype)
+    if code is None or arrs[1].dtype != np.int32:
+        raise TypeError("ddt_accept_walk_host: logits float32 or uint16 (bf16 bits), draft_tok int32")
+    _check(lib().ddt_accept_walk_host(ctypes.byref(plan_struct_host), _ptr(arrs[0]), code, int(arrs[0].shape[-1]),
+                                      _ptr(arrs[1]), _ptr(argmax), _ptr(path), _ptr(L), _ptr(bonus)),
+           "ddt_accept_walk_host")
+
+
+def accept_walk_with_fallback(tb, logits, draft_tok, argmax, path, L, bonus, ws, stream=None):
+    """The validate-then-fall-back walk: the device walk, then (after the
+    stream is synchronised) its status words; if the device check of the
+    argmax failed for any sequence (DDT_ST_ARGMAX), the step's logits and
+    draft tokens are copied to the host, the host walk recomputes every
+    output and the results are written back to the device arrays.  Returns
+    (status [B] as left by the device walk, whether the host walk ran)."""
+    import torch
+    ddt_accept_walk(tb, logits, draft_tok, argmax, path, L, bonus, ws, stream)
+    (stream or torch.cuda.current_stream()).synchronize()
+    st = tb.status.cpu().numpy()
+    if not (st & DDT_ST_ARGMAX).any():
+        return st, False
+    lg = logits.cpu()
+    lg = lg.view(torch.int16).numpy().view(np.uint16) if lg.dtype == torch.bfloat16 else lg.numpy()
+    out = [np.empty(tuple(t.shape), np.int32) for t in (argmax, path, L, bonus)]
+    tb.status_host[:] = 0
+    ddt_accept_walk_host(tb.struct_host, lg, draft_tok.cpu().numpy(), *out)
+    for t, a in zip((argmax, path, L, bonus), out):
+        t.copy_(torch.from_numpy(a))
+    return st, True
 
 
 def layer_table(structs, device):

@@ -14,8 +14,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libddtree.so")
-SOURCES = ["plan.hip", "conv.hip", "gdn.hip", "attn.hip", "walk.hip", "commit.hip", "draft.hip", "fused.hip", "sample.hip"]
+SOURCES = ["plan.hip", "conv.hip", "gdn.hip", "attn.hip", "walk.hip", "commit.hip", "draft.hip", "fused.hip", "sample.hip",
+           "host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+# the host-only part of the library (plain C++, no HIP)
+CXXFLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-I" + os.path.join(ROOT, "include")]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"),
@@ -47,8 +51,11 @@ def source_hash():
 
 
 def _compile(src, src_hash):
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, f'-DDDT_SOURCE_HASH="{src_hash}"', "-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, f'-DDDT_SOURCE_HASH="{src_hash}"', "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

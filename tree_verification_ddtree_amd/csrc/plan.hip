@@ -1,4 +1,4 @@
-// Tree plan (host and device) and library-wide bits.
+// Tree plan on the device and library-wide bits (the host plan is in host.cpp).
 //
 // The plan turns a parent-pointer draft tree (lucebox-hub README,
 // "02 · DFlash DDtree", "Algorithms used": DDTree verifies a tree of draft
@@ -8,8 +8,6 @@
 // topological and no visit order is needed.
 #include <stdio.h>
 #include <string.h>
-
-#include <vector>
 
 #include "common.h"
 
@@ -30,15 +28,8 @@ int launch_status() {
   return DDT_OK;
 }
 
-static int plan_fields_ok(const ddt_plan *P) {
-  if (!P) return DDT_E_ARG;
-  if (P->B < 1 || P->n_total < 1 || P->n_max < 1 || P->n_max > DDT_MAX_NODES) return DDT_E_SHAPE;
-  if (P->W < 1 || P->W > DDT_MAX_W) return DDT_E_SHAPE;
-  if (!P->tree_off || !P->parent || !P->depth || !P->anc || !P->win || !P->status) return DDT_E_ARG;
-  return DDT_OK;
-}
-
-int check_plan(const ddt_plan *P) { return plan_fields_ok(P); }
+// the plan fields check (host.cpp)
+int check_plan(const ddt_plan *P);
 
 // ------------------------------------------------------------------ device plan
 // One wavefront per sequence, lane c = node c, nothing through LDS.  The
@@ -129,59 +120,9 @@ extern "C" const char *ddt_status_str(int code) {
 }
 
 extern "C" int ddt_tree_plan(const ddt_plan *P, int32_t max_levels, void *stream) {
-  int r = plan_fields_ok(P);
+  int r = check_plan(P);
   if (r) return r;
   if (max_levels < 1) return DDT_E_RANGE;
   hipLaunchKernelGGL(plan_kernel, dim3(P->B), dim3(64), 0, (hipStream_t)stream, *P, max_levels);
   return launch_status();
-}
-
-// ------------------------------------------------------------------ host plan
-extern "C" int ddt_tree_plan_host(const ddt_plan *P, int32_t max_levels) {
-  int r = plan_fields_ok(P);
-  if (r) return r;
-  if (max_levels < 1) return DDT_E_RANGE;
-  const int B = P->B, W1 = P->W - 1;
-  if (P->tree_off[0] != 0 || P->tree_off[B] != P->n_total) return DDT_E_TREE;
-  // validate everything before writing anything
-  for (int b = 0; b < B; ++b) {
-    int o = P->tree_off[b], n = P->tree_off[b + 1] - o;
-    if (n < 1 || n > P->n_max) return DDT_E_TREE;
-    if (P->parent[o] != -1) return DDT_E_TREE;
-    for (int i = 1; i < n; ++i)
-      if (P->parent[o + i] < 0 || P->parent[o + i] >= i) return DDT_E_TREE;
-    std::vector<int> d(n, 0);
-    for (int i = 1; i < n; ++i) {
-      d[i] = d[P->parent[o + i]] + 1;
-      if (d[i] + 1 > max_levels) return DDT_E_RANGE;
-    }
-  }
-  for (int b = 0; b < B; ++b) {
-    const int o = P->tree_off[b], n = P->tree_off[b + 1] - o;
-    const int32_t *par = P->parent + o;
-    std::vector<int> d(n, 0);
-    std::vector<unsigned long long> a(n, 1ull);
-    for (int i = 1; i < n; ++i) {
-      d[i] = d[par[i]] + 1;
-      a[i] = a[par[i]] | (1ull << i);
-    }
-    for (int i = 0; i < n; ++i) {
-      P->depth[o + i] = d[i];
-      P->anc[o + i] = a[i];
-      int y = i;
-      for (int j = 1; j <= W1; ++j) {
-        int v;
-        if (j <= d[i]) {
-          y = par[y];
-          v = y;
-        } else {
-          v = -((W1 - (j - d[i])) + 1);
-        }
-        P->win[(size_t)(o + i) * W1 + (j - 1)] = v;
-      }
-      if (W1 == 0) P->win[o + i] = 0;
-    }
-    P->status[b] = 0;
-  }
-  return DDT_OK;
 }
