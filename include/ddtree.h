@@ -429,9 +429,9 @@ int ddt_commit_state(const ddt_plan *plan, const int32_t *path, const int32_t *L
  * the fp32 gates, and gdn_dtype DDT_F32; UPDATE and SELECT then give
  * bitwise the node state this call computes.  REPLAY (from q_out, k_out,
  * v_out) forms its products in fp32 and agrees within rounding only.
- * Same shape rules as ddt_tree_gdn; the workgroup's LDS,
- * ddt_tree_conv_gdn_lds(n_max, dk) bytes, must fit in 160 KiB (it does for
- * every n_max <= 64 at dk <= 128).
+ * Same shape rules as ddt_tree_gdn, with Hv and dv at most 65535; the
+ * workgroup's LDS, ddt_tree_conv_gdn_lds(n_max, dk) bytes, must fit in
+ * 160 KiB (it does for every n_max <= 64 at dk <= 128).
  * Errors: DDT_E_ARG, DDT_E_SHAPE, DDT_E_DTYPE, plan errors; nothing is
  * launched then.
  */

@@ -53,28 +53,27 @@ struct FusedLds {
   }
 };
 
-// The plan's sizes and the first pointers come first among the arguments:
-// the library is built to preload the first 16 argument dwords into scalar
-// registers at dispatch, so the first loads need no argument fetch.
+// Everything the first round of loads needs comes first among the
+// arguments, in 14 dwords: the library is built to preload the first
+// argument dwords into scalar registers at dispatch (14 of its 16 user
+// registers are free for them), so those loads wait for no argument fetch.
+// sizes = n_max | W << 8 | dv << 16, heads = Hk | Hv << 16.
 template <typename T, int DK, int MW>
-__global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_total, int plan_n_max, int plan_W,
+__global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_total, int sizes, int heads,
                                                        const float *__restrict__ S_c, const T *__restrict__ x,
                                                        const T *__restrict__ prefix, const T *__restrict__ w,
-                                                       const float *__restrict__ alpha,
-                                                       const float *__restrict__ beta, ddt_plan P, int Hk, int Hv,
-                                                       int dv, float scale, float *__restrict__ out,
-                                                       float *__restrict__ q_out, float *__restrict__ k_out,
-                                                       float *__restrict__ v_out, float *__restrict__ node_states,
-                                                       float *__restrict__ node_u) {
+                                                       int32_t *plan_win, const float *__restrict__ alpha,
+                                                       const float *__restrict__ beta, ddt_plan P, float scale,
+                                                       float *__restrict__ out, float *__restrict__ q_out,
+                                                       float *__restrict__ k_out, float *__restrict__ v_out,
+                                                       float *__restrict__ node_states, float *__restrict__ node_u) {
   // MW: conv width class (4 or 8); taps at or past W are zero
   P.B = plan_B;
   P.n_total = plan_n_total;
-  P.n_max = plan_n_max;
-  P.W = plan_W;
-  // every other argument fetched now, in one round (the compiler would
-  // otherwise fetch each group where it is first used, one wait each)
-  asm volatile("" ::"s"(P.anc), "s"(P.win), "s"(Hk), "s"(Hv), "s"(dv), "s"(scale), "s"(out), "s"(q_out),
-               "s"(k_out), "s"(v_out), "s"(node_states), "s"(node_u));
+  P.n_max = sizes & 0xff;
+  P.W = (sizes >> 8) & 0xff;
+  P.win = plan_win;
+  const int dv = (int)((unsigned)sizes >> 16), Hk = heads & 0xffff, Hv = (int)((unsigned)heads >> 16);
   constexpr int UE = 16 / (int)sizeof(T);     // elements per 16-byte piece
   constexpr int XW = 2 * DK + GDN_R;          // staged channels per node: q, k of the key head, v of the tile
   constexpr int PPN = XW / UE;                // pieces per node row
@@ -150,6 +149,11 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_to
     const int e = min(tid + 256 * k, ne - 1), i = e / MW, j = e % MW;
     wr[k] = P.win[(size_t)(s.o + i) * W1w + min(max(j - 1, 0), W1w - 1)];
   }
+  // every other argument, fetched in one round while those loads are in
+  // flight (the compiler would otherwise fetch each group where it is first
+  // used, one wait each)
+  asm volatile("" ::"s"(P.anc), "s"(alpha), "s"(beta), "s"(scale), "s"(out), "s"(q_out), "s"(k_out), "s"(v_out),
+               "s"(node_states), "s"(node_u));
   auto anc_of = [&](int j) { return (P.anc[s.o + j] & ((2ull << j) - 1)) | (1ull << j); };
   const int jt = min(tid, n - 1);
   const float a0 = alpha[(size_t)(s.o + jt) * Hv + h], b0 = beta[(size_t)(s.o + jt) * Hv + h];
@@ -333,9 +337,9 @@ static void launch_fused(int dk, dim3 grid, size_t lds, hipStream_t st, const dd
   do {                                                                                                    \
     (void)hipFuncSetAttribute((const void *)fused_kernel<T, D, M>,                                        \
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
-    hipLaunchKernelGGL((fused_kernel<T, D, M>), grid, dim3(256), lds, st, P.B, P.n_total, P.n_max, P.W, S,      \
-                       (const T *)x, (const T *)pre, (const T *)w, al, be, P, Hk, Hv, dv, scale, out, qo, ko, vo, \
-                       ns, nu);                                                                            \
+    hipLaunchKernelGGL((fused_kernel<T, D, M>), grid, dim3(256), lds, st, P.B, P.n_total,                 \
+                       P.n_max | (P.W << 8) | (dv << 16), Hk | (Hv << 16), S, (const T *)x, (const T *)pre,     \
+                       (const T *)w, P.win, al, be, P, scale, out, qo, ko, vo, ns, nu);                        \
   } while (0)
 #define DDT_FUSED_W(D)        \
   do {                        \
@@ -371,9 +375,9 @@ extern "C" int ddt_tree_conv_gdn(const ddt_plan *P, const void *x, const void *p
   int r = check_plan(P);
   if (r) return r;
   if (!x || !w || !alpha || !beta || !S_c || !out || (P->W > 1 && !prefix)) return DDT_E_ARG;
-  if (Hk < 1 || Hv < 1 || Hv % Hk) return DDT_E_SHAPE;
+  if (Hk < 1 || Hv < 1 || Hv % Hk || Hv > 65535) return DDT_E_SHAPE;  // (Hk, Hv and dv go in 16 bits each)
   if (dk != 16 && dk != 32 && dk != 64 && dk != 128) return DDT_E_SHAPE;
-  if (dv < GDN_R || dv % GDN_R) return DDT_E_SHAPE;
+  if (dv < GDN_R || dv % GDN_R || dv > 65535) return DDT_E_SHAPE;
   if (dtype != DDT_BF16 && dtype != DDT_F32) return DDT_E_DTYPE;
   const size_t lds = FusedLds(P->n_max, dk).total;
   if (lds > 160 * 1024) return DDT_E_SHAPE;
