@@ -51,6 +51,7 @@
 //  - Each split writes its output rows divided by their row sums (fp16),
 //    its reference max and the row sum; a combine kernel merges the splits
 //    in fixed order (deterministic, no atomics).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -1029,16 +1030,33 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 // are then added in a fixed order, so the result does not depend on timing.
 constexpr int MAX_SPLITS = 1024;
 
+// The fields of A that the first loads need lead the arguments, which the
+// library preloads into scalar registers at dispatch (14 dwords); n1 is the
+// node count of a batch of one sequence (without POOL).
 template <int D, bool POOL>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const _Float16 *__restrict__ a_Opart,
+                                                           const float2 *__restrict__ a_ML,
+                                                           const int32_t *__restrict__ a_T, const int32_t *a_pt,
+                                                           int n1, int a_G, int a_rows_wg, int a_n_rg,
+                                                           int a_n_splits, int a_T_max, AttnArgs A) {
   constexpr int TPR = D / 4;     // threads per channel sweep
   constexpr int SG = 256 / TPR;  // split groups
   constexpr int BATCH = 16;      // partial loads in flight per thread
   __shared__ float wts[MAX_SPLITS];
   __shared__ float Lsh;
   __shared__ float4 part[SG][TPR];
-  const int rl = blockIdx.x, g = blockIdx.y, b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
-  const Seq s = seq_of(A.P, b);
+  A.Opart = const_cast<_Float16 *>(a_Opart);
+  A.ML = const_cast<float2 *>(a_ML);
+  A.T = a_T;
+  A.pt = a_pt;
+  A.G = a_G;
+  A.rows_wg = a_rows_wg;
+  A.n_rg = a_n_rg;
+  A.n_splits = a_n_splits;
+  A.T_max = a_T_max;
+  const int rl = blockIdx.x, g = blockIdx.y;
+  const int b = POOL ? blockIdx.z / A.n_rg : 0, rg = POOL ? blockIdx.z % A.n_rg : blockIdx.z;
+  const Seq s = POOL ? seq_of(A.P, b) : Seq{0, n1};
   const int rho = rg * A.rows_wg + rl;
   if (rho >= A.G * s.n) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1066,9 +1084,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs A) {
 #pragma unroll
   for (int t = 0; t < BATCH; ++t) v[t] = *reinterpret_cast<const half4 *>(src + min(sg + t * SG, nw - 1) * sstride);
   // the context length is read after the partials are requested (left to
-  // itself the scheduler clamps it first and so waits for it before them)
+  // itself the scheduler clamps it first and so waits for it before them);
+  // the arguments not preloaded are fetched in the same round
   __builtin_amdgcn_sched_barrier(0);
   const int nsp = n_active_splits(ctx_len(A, b, nullptr), nw);
+  asm volatile("" ::"s"(A.c), "s"(A.out), "s"(A.Hq));
   if (tid < 64) {
     float m = lane < nsp ? fmaxf(-INFINITY, ml0.x) : -INFINITY;
     for (int sp = lane + 64; sp < nsp; sp += 64) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
@@ -1309,14 +1329,19 @@ static int launch_attn_mfma(const ddt_plan &P, const AttnArgs &A, const Cfg &c, 
   const int r = launch_status();
   if (r) return r;
   dim3 cgrid(c.rows_wg, A.Hkv, P.B * c.n_rg);
+  const int n1 = pool ? 0 : std::max(0, std::min(P.n_total, P.n_max));  // the one sequence's nodes (seq_of)
+#define DDT_COMBINE(DD, PL)                                                                                   \
+  hipLaunchKernelGGL((attn_combine_kernel<DD, PL>), cgrid, dim3(256), 0, st, A.Opart, A.ML, A.T, A.pt, n1, A.G, \
+                     A.rows_wg, A.n_rg, A.n_splits, A.T_max, A)
   if (D == 256 && pool)
-    hipLaunchKernelGGL((attn_combine_kernel<256, true>), cgrid, dim3(256), 0, st, A);
+    DDT_COMBINE(256, true);
   else if (D == 256)
-    hipLaunchKernelGGL((attn_combine_kernel<256, false>), cgrid, dim3(256), 0, st, A);
+    DDT_COMBINE(256, false);
   else if (pool)
-    hipLaunchKernelGGL((attn_combine_kernel<128, true>), cgrid, dim3(256), 0, st, A);
+    DDT_COMBINE(128, true);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<128, false>), cgrid, dim3(256), 0, st, A);
+    DDT_COMBINE(128, false);
+#undef DDT_COMBINE
   return launch_status();
 }
 
