@@ -116,12 +116,19 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_to
     const size_t o = pre ? ((size_t)b * W1 + row) * C : (size_t)(s.o + row - W1) * C;
     return (pre ? prefix : x) + o + gc;
   };
+  // A staged row is two planes of XW / 2 floats: channels 8 c .. 8 c + 3
+  // at 4 c of the first, 8 c + 4 .. 8 c + 7 at 4 c of the second.  The conv
+  // reads 8 channels as one 16-byte slot of each plane, so the 16 lanes of a
+  // read that take adjacent 8-channel groups cover 256 contiguous bytes, all
+  // the banks once (8 floats side by side would put lanes c and c + 8 on
+  // the same banks).
   auto put_piece = [&](int row, gu32x4 v) {
     float f[UE];
     piece_f32<T>(v, f);
-    float *d = xs + row * XW + pc * UE;
+    const int c4 = pc * UE / 4;  // first group of 4 channels of the piece
+    float *d = xs + row * XW + (c4 & 1) * (XW / 2) + (c4 >> 1) * 4;
     *reinterpret_cast<gf32x4 *>(d) = gf32x4{f[0], f[1], f[2], f[3]};
-    if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(d + 4) = gf32x4{f[4], f[5], f[6], f[7]};
+    if constexpr (UE == 8) *reinterpret_cast<gf32x4 *>(d + XW / 2) = gf32x4{f[4], f[5], f[6], f[7]};
   };
   // every first-round global load is issued before any store (a store
   // waits for its value, and for everything issued before it): the
@@ -226,7 +233,12 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(int plan_B, int plan_n_to
     }
     float xv[MW][8];
 #pragma unroll
-    for (int j = 0; j < MW; ++j) ld8f(xs + rows[j] * XW + lc0, xv[j]);
+    for (int j = 0; j < MW; ++j) {
+      const float4 a = *reinterpret_cast<const float4 *>(xs + rows[j] * XW + lc0 / 2);
+      const float4 c = *reinterpret_cast<const float4 *>(xs + rows[j] * XW + XW / 2 + lc0 / 2);
+      xv[j][0] = a.x, xv[j][1] = a.y, xv[j][2] = a.z, xv[j][3] = a.w;
+      xv[j][4] = c.x, xv[j][5] = c.y, xv[j][6] = c.z, xv[j][7] = c.w;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float a = tp[0][e] * xv[0][e];
