@@ -114,6 +114,10 @@ def test_device_entry_points_validate_before_launch():
     assert L.ddt_tree_attn(ctypes.byref(P2), one, one, one, None, 0, one, 100, one, one, 24, 4, 256,
                            0.1, 1, 0, one, one, 1 << 30, None) == -1
     assert ddt.ddt_tree_attn_workspace(P, 24, 4, 256, 131072) > 0
+    # a batch shares at most 1024 context splits and needs one per sequence
+    P3 = _dummy_plan(B=1025)
+    assert L.ddt_tree_attn(ctypes.byref(P3), one, one, one, one, 4, one, 100, one, one, 24, 4, 256,
+                           0.1, 1, 0, one, one, 1 << 30, None) == -3
     # 8-bit cache attention: head size outside {128, 256}, null scales, small workspace
     q8 = L.ddt_tree_attn_q8
     assert q8(bp, one, one, one, one, one, None, 0, one, 100, one, one, 24, 4, 64, 0.1, 0, one, one,
@@ -168,6 +172,11 @@ def test_device_entry_points_validate_before_launch():
              None) == -4
     assert f(bp, one, one, one, 2, None, one, one, 2, 4, 128, 128, 1.0, one, None, None, None, None, None,
              None) == -1
+    # ... head counts and d_v travel in 16 bits each
+    assert f(bp, one, one, one, 2, one, one, one, 1, 65536, 128, 128, 1.0, one, None, None, None, None, None,
+             None) == -3
+    assert f(bp, one, one, one, 2, one, one, one, 2, 4, 128, 65552, 1.0, one, None, None, None, None, None,
+             None) == -3
     assert 0 < ddt.ddt_tree_conv_gdn_lds(64, 128) <= 160 * 1024
     assert ddt.ddt_tree_conv_gdn_lds(65, 128) == 0 and ddt.ddt_tree_conv_gdn_lds(22, 96) == 0
     # sampled acceptance: temperature, top_k, top_p, dtype, workspace
