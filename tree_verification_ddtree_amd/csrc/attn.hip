@@ -1030,10 +1030,11 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs A) {
 // are then added in a fixed order, so the result does not depend on timing.
 constexpr int MAX_SPLITS = 1024;
 
-// The fields of A that the first loads need lead the arguments, which the
-// library preloads into scalar registers at dispatch (14 dwords); n1 is the
-// node count of a batch of one sequence (without POOL).
-template <int D, bool POOL>
+// The combine for a batch of one sequence (n1 nodes), whose splits are all
+// its own: one workgroup per row.  The fields of A that the first loads need
+// lead the arguments, which the library preloads into scalar registers at
+// dispatch (14 dwords).
+template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const _Float16 *__restrict__ a_Opart,
                                                            const float2 *__restrict__ a_ML,
                                                            const int32_t *__restrict__ a_T, const int32_t *a_pt,
@@ -1054,22 +1055,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const _Float16 *__res
   A.n_rg = a_n_rg;
   A.n_splits = a_n_splits;
   A.T_max = a_T_max;
-  const int rl = blockIdx.x, g = blockIdx.y;
-  const int b = POOL ? blockIdx.z / A.n_rg : 0, rg = POOL ? blockIdx.z % A.n_rg : blockIdx.z;
-  const Seq s = POOL ? seq_of(A.P, b) : Seq{0, n1};
+  const int rl = blockIdx.x, g = blockIdx.y, b = 0, rg = blockIdx.z;
+  const Seq s{0, n1};
   const int rho = rg * A.rows_wg + rl;
   if (rho >= A.G * s.n) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  size_t base;
-  int nw;  // the sequence's split count
-  if constexpr (POOL) {
-    const PoolSlot ps = pool_slot(A, rg, 0, b);  // the sequence's pool splits
-    base = (((size_t)g * A.n_rg + rg) * A.n_splits + ps.first) * A.rows_wg + rl;
-    nw = ps.nb;
-  } else {
-    base = (((size_t)(b * A.Hkv + g) * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
-    nw = A.n_splits;
-  }
+  const size_t base = (((size_t)g * A.n_rg + rg) * A.n_splits) * A.rows_wg + rl;
+  const int nw = A.n_splits;
   const int dc = tid % TPR, sg = tid / TPR;
   const _Float16 *src = A.Opart + base * D + 4 * dc;
   const size_t sstride = (size_t)A.rows_wg * D;
@@ -1142,6 +1134,76 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const _Float16 *__res
     *reinterpret_cast<float4 *>(A.out + ((size_t)(s.o + node) * A.Hq + hq) * D + 4 * dc) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
+}
+
+// The combine for a batch sharing pooled splits: one wavefront per row,
+// four rows of one sequence per workgroup.  A sequence has a few splits
+// each (its share of the pool), so a whole workgroup per row, as above,
+// would mostly wait; here each wave computes the sequence's deal, its
+// splits' weights (lane sp holds split sp, 64 at a time, then LDS makes
+// them visible to the whole wave) and its row's channels, CPL per lane,
+// with every partial load of a batch of 16 splits issued before any is
+// used.  Same fixed merge order as above, so results are deterministic.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_rows_kernel(AttnArgs A) {
+  constexpr int CPL = D / 64;  // channels per lane
+  constexpr int BATCH = 16;
+  typedef _Float16 hcpl __attribute__((ext_vector_type(CPL)));
+  __shared__ float wts[4][MAX_SPLITS];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = blockIdx.y, b = blockIdx.z / A.n_rg, rg = blockIdx.z % A.n_rg;
+  const int rl = 4 * blockIdx.x + wv;
+  const Seq s = seq_of(A.P, b);
+  const int rho = rg * A.rows_wg + rl;
+  if (rl >= A.rows_wg || rho >= A.G * s.n) return;  // the same in every lane of the wave
+  const PoolSlot ps = pool_slot(A, rg, 0, b);        // the sequence's pool splits
+  const size_t base = (((size_t)g * A.n_rg + rg) * A.n_splits + ps.first) * A.rows_wg + rl;
+  const int nsp = n_active_splits(ctx_len(A, b, nullptr), ps.nb);
+  const size_t sstride = (size_t)A.rows_wg * D;
+  const _Float16 *src = A.Opart + base * D + CPL * lane;
+  float *wt = wts[wv];
+  // reference maximum over the active splits, then the weights
+  float m = -INFINITY;
+  for (int sp = lane; sp < nsp; sp += 64) m = fmaxf(m, A.ML[base + (size_t)sp * A.rows_wg].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float l = 0.f;
+  for (int sp = lane; sp < nsp; sp += 64) {
+    const float2 ml = A.ML[base + (size_t)sp * A.rows_wg];
+    const float wgt = (ml.x == -INFINITY) ? 0.f : ml.y * exp2f((ml.x - m) * A.c);
+    wt[sp] = wgt;
+    l += wgt;
+  }
+  // fixed-order total: lane partials gathered in lane order
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_down(l, o);
+    if ((lane & (2 * o - 1)) == 0) l += t;
+  }
+  l = __shfl(l, 0);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done (lgkmcnt(0))
+  __builtin_amdgcn_wave_barrier();
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int sp0 = 0; sp0 < nsp; sp0 += BATCH) {
+    hcpl v[BATCH];
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) v[t] = *reinterpret_cast<const hcpl *>(src + min(sp0 + t, nsp - 1) * sstride);
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) {
+      if (sp0 + t < nsp) {
+        const float wgt = wt[sp0 + t];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf((float)v[t][c], wgt, acc[c]);
+      }
+    }
+  }
+  const float inv = 1.f / l;
+  const int node = rho / A.G, hq = g * A.G + rho % A.G;
+  float *o = A.out + ((size_t)(s.o + node) * A.Hq + hq) * D + CPL * lane;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[c] = acc[c] * inv;
 }
 
 // Small head dims (D <= 64) and fp32 caches: one workgroup per (node, q
@@ -1328,19 +1390,23 @@ static int launch_attn_mfma(const ddt_plan &P, const AttnArgs &A, const Cfg &c, 
 #undef DDT_ATTN
   const int r = launch_status();
   if (r) return r;
-  dim3 cgrid(c.rows_wg, A.Hkv, P.B * c.n_rg);
-  const int n1 = pool ? 0 : std::max(0, std::min(P.n_total, P.n_max));  // the one sequence's nodes (seq_of)
-#define DDT_COMBINE(DD, PL)                                                                                   \
-  hipLaunchKernelGGL((attn_combine_kernel<DD, PL>), cgrid, dim3(256), 0, st, A.Opart, A.ML, A.T, A.pt, n1, A.G, \
+  if (pool) {
+    dim3 rgrid((c.rows_wg + 3) / 4, A.Hkv, P.B * c.n_rg);
+    if (D == 256)
+      hipLaunchKernelGGL(attn_combine_rows_kernel<256>, rgrid, dim3(256), 0, st, A);
+    else
+      hipLaunchKernelGGL(attn_combine_rows_kernel<128>, rgrid, dim3(256), 0, st, A);
+    return launch_status();
+  }
+  dim3 cgrid(c.rows_wg, A.Hkv, c.n_rg);
+  const int n1 = std::max(0, std::min(P.n_total, P.n_max));  // the one sequence's nodes (seq_of)
+#define DDT_COMBINE(DD)                                                                                   \
+  hipLaunchKernelGGL(attn_combine_kernel<DD>, cgrid, dim3(256), 0, st, A.Opart, A.ML, A.T, A.pt, n1, A.G,   \
                      A.rows_wg, A.n_rg, A.n_splits, A.T_max, A)
-  if (D == 256 && pool)
-    DDT_COMBINE(256, true);
-  else if (D == 256)
-    DDT_COMBINE(256, false);
-  else if (pool)
-    DDT_COMBINE(128, true);
+  if (D == 256)
+    DDT_COMBINE(256);
   else
-    DDT_COMBINE(128, false);
+    DDT_COMBINE(128);
 #undef DDT_COMBINE
   return launch_status();
 }
