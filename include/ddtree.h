@@ -213,10 +213,10 @@ int ddt_tree_gdn(const ddt_plan *plan, const void *q, const void *k, const void 
  * context splits per KV head (and group of up to 192 query rows), 0 = automatic
  * (about one workgroup per compute unit, splits of at least 256 keys).  One
  * sequence has them all; the sequences of a larger batch share them: each
- * takes one, and the rest are dealt in proportion to each sequence's tiles
- * times its row blocks, at most one per 256 of its committed keys, so a batch
- * of B sequences uses at least B splits (matrix-core path: B <= 1024, else
- * DDT_E_SHAPE).  A sequence whose T[b] exceeds T_max or its page table is
+ * takes one, and the rest are dealt in proportion to each sequence's 32-key
+ * tiles (cache and tree), at most one per 256 of its committed keys, so a
+ * batch of B sequences uses at least B splits (matrix-core path: B <= 1024,
+ * else DDT_E_SHAPE).  A sequence whose T[b] exceeds T_max or its page table is
  * flagged DDT_ST_CTX and only its first T_max tokens are read.
  * Precision (matrix-core path): scores and value sums accumulate in fp32,
  * probabilities enter the value product as fp16 (as the fp16 values do);

@@ -133,12 +133,16 @@ __device__ __forceinline__ int n_active_splits(int Tb, int nb) {
 
 // The batch's sequences share the A.n_splits context splits of a (KV head,
 // row group): every sequence with rows in the row group takes one, and the
-// rest are dealt in proportion to each sequence's work, its tiles (cache and
-// tree) times its row blocks per wavefront, with at least 256 keys per split.
-// A short context then no longer waits on a long one that has the same
-// number of splits.  Every workgroup of the attention kernel and of the
-// combine computes the same deal from the committed lengths (one lane per
-// sequence).  A batch of one sequence launches the direct mapping instead.
+// rest are dealt in proportion to each sequence's tiles (cache and tree),
+// with at least 256 keys per split.  All splits stream at once, each at an
+// equal share of the memory bandwidth, so a split's time is its tile count
+// whatever its row blocks.  The shares are rounded cumulatively (sequence b
+// gets E S_(b+1) / W - E S_b / W, floors of its prefix sums of weights), so
+// the whole pool is dealt.  A short context then no longer waits on a long
+// one that has the same number of splits.  Every workgroup of the attention
+// kernel and of the combine computes the same deal from the committed
+// lengths (one lane per sequence).  A batch of one sequence launches the
+// direct mapping instead.
 struct PoolSlot {
   int b, j, nb, first;  // sequence, its split, its split count, its first pool split
 };
@@ -147,6 +151,15 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ long long wave_incl_scan_ll(long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(v, o);
     if (lane >= o) v += t;
   }
   return v;
@@ -170,8 +183,7 @@ __device__ PoolSlot pool_slot(const AttnArgs &A, int rg, int s, int want_b) {
     const int rows = min(max(A.G * q.n - rg * A.rows_wg, 0), A.rows_wg);
     if (rows == 0) return;
     const int Tb = ctx_len(A, b, nullptr);
-    const long long tiles = (Tb + TILE - 1) / TILE + (q.n + TILE - 1) / TILE;
-    w = tiles * ((rows + 63) / 64);
+    w = (Tb + TILE - 1) / TILE + (q.n + TILE - 1) / TILE;
     cap = max(1, (Tb + 255) / 256);
   };
   long long W = 0;
@@ -185,11 +197,13 @@ __device__ PoolSlot pool_slot(const AttnArgs &A, int rg, int s, int want_b) {
   }
   const long long E = A.n_splits > m ? A.n_splits - m : 0;
   int base = 0;
+  long long Sb = 0;  // weights of the sequences before this chunk
   for (int b0 = 0; b0 < B; b0 += 64) {
     long long w;
     int cap;
     seq_data(b0 + lane, w, cap);
-    const int nb = cap > 0 ? min(cap, 1 + (int)(W > 0 ? E * w / W : 0)) : 0;
+    const long long Si = Sb + wave_incl_scan_ll(w), Se = Si - w;
+    const int nb = cap > 0 ? min(cap, 1 + (int)(W > 0 ? E * Si / W - E * Se / W : 0)) : 0;
     const int incl = wave_incl_scan(nb);
     const int first = base + incl - nb;
     if (want_b >= 0) {
@@ -206,6 +220,7 @@ __device__ PoolSlot pool_slot(const AttnArgs &A, int rg, int s, int want_b) {
       }
     }
     base += __shfl(incl, 63);
+    Sb = __shfl(Si, 63);
   }
   return {-1, 0, 0, 0};
 }
