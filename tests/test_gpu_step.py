@@ -171,10 +171,13 @@ def test_step_is_deterministic_and_batch_independent(gpu):
     for k in ("conv", "gdn"):
         for a, b in zip(o1[k], o3[k]):
             assert torch.equal(a[o:e], b)
-    # attention splits the context by the batch's longest sequence, which
-    # is the same here, so the result is bitwise the same as well
+    # attention: in a batch the sequences share a pool of context splits,
+    # dealt in proportion to each one's tiles, so sequence 1's split bounds
+    # depend on its neighbour and its rows agree with the solo run to the
+    # rounding of the split merge (fp16 partials), not bit for bit
     for a, b in zip(o1["attn"], o3["attn"]):
-        assert torch.equal(a[o:e], b)
+        assert torch.isfinite(b).all()
+        assert rel_err(host(b), host(a[o:e]), (0, 1)) < TOL
     assert r3["L"][0] == r1["L"][1]
 
 
