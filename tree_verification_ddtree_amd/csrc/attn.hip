@@ -136,7 +136,10 @@ __device__ __forceinline__ int n_active_splits(int Tb, int nb) {
 // rest are dealt in proportion to each sequence's tiles (cache and tree),
 // with at least 256 keys per split.  All splits stream at once, each at an
 // equal share of the memory bandwidth, so a split's time is its tile count
-// whatever its row blocks.  The shares are rounded cumulatively (sequence b
+// as long as its matrix work per tile hides under that share; beyond nine
+// 16-row blocks in the row group (every wavefront then holds three) it does
+// not, and a tile of such a sequence weighs 1 + (blocks - 9) / 12 (32 nodes
+// at 6 query heads: 1.25).  The shares are rounded cumulatively (sequence b
 // gets E S_(b+1) / W - E S_b / W, floors of its prefix sums of weights), so
 // the whole pool is dealt.  A short context then no longer waits on a long
 // one that has the same number of splits.  Every workgroup of the attention
@@ -183,7 +186,8 @@ __device__ PoolSlot pool_slot(const AttnArgs &A, int rg, int s, int want_b) {
     const int rows = min(max(A.G * q.n - rg * A.rows_wg, 0), A.rows_wg);
     if (rows == 0) return;
     const int Tb = ctx_len(A, b, nullptr);
-    w = (Tb + TILE - 1) / TILE + (q.n + TILE - 1) / TILE;
+    // weights in twelfths of a tile
+    w = (long long)((Tb + TILE - 1) / TILE + (q.n + TILE - 1) / TILE) * (12 + max(0, (rows + 15) / 16 - 9));
     cap = max(1, (Tb + 255) / 256);
   };
   long long W = 0;
